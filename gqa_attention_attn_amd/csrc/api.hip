@@ -1,0 +1,234 @@
+// C ABI of the gfx950 GQA attention library: argument validation (all on the
+// host, before any HIP call), the split-KV plan, workspace sizing and the
+// kernel launches.  The contract of every entry point is in include/gqa_attn.h.
+#include <math.h>
+#include <stdint.h>
+
+#include "../../include/gqa_attn.h"
+#include "common.hpp"
+
+namespace {
+
+constexpr int kGridYZMax = 65535;
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+bool stride_ok(int64_t s, int elem) { return s >= 0 && ((s * elem) & 15) == 0; }
+int elem_size(int32_t dt) { return dt == GQA_BF16 ? 2 : 4; }
+bool dtype_ok(int32_t dt) { return dt == GQA_F32 || dt == GQA_BF16; }
+
+float resolve_scale_log2(float scale) {
+  const double s = scale > 0.f ? (double)scale : 1.0 / sqrt((double)GQA_ATTN_HEAD_DIM);
+  return (float)(s * 1.4426950408889634);   // scores are kept in log2 units
+}
+
+// Shape / dtype / stride checks that need no pointer.
+gqa_status check_decode_desc(const gqa_decode_desc* d) {
+  if (d == nullptr) return GQA_ERR_NULL;
+  if (d->batch < 1 || d->num_q_heads < 1 || d->num_kv_heads < 1 || d->max_seq < 1) return GQA_ERR_SHAPE;
+  if (d->batch > kGridYZMax || d->num_kv_heads > kGridYZMax) return GQA_ERR_SHAPE;
+  if (d->num_q_heads % d->num_kv_heads != 0) return GQA_ERR_SHAPE;
+  if (d->kv_split_tokens < 0) return GQA_ERR_SHAPE;
+  if (d->head_dim != GQA_ATTN_HEAD_DIM) return GQA_ERR_UNSUPPORTED;
+  if (d->num_q_heads / d->num_kv_heads > GQA_ATTN_MAX_GROUP) return GQA_ERR_UNSUPPORTED;
+  if (!dtype_ok(d->in_dtype) || !dtype_ok(d->out_dtype)) return GQA_ERR_UNSUPPORTED;
+  const int ei = elem_size(d->in_dtype), eo = elem_size(d->out_dtype);
+  if (d->q_stride_b < 0 || d->q_stride_h < 0 || d->k_stride_b < 0 || d->k_stride_h < 0 || d->k_stride_s < 0 ||
+      d->v_stride_b < 0 || d->v_stride_h < 0 || d->v_stride_s < 0 || d->out_stride_b < 0 || d->out_stride_h < 0)
+    return GQA_ERR_SHAPE;
+  if (!stride_ok(d->q_stride_b, ei) || !stride_ok(d->q_stride_h, ei) || !stride_ok(d->k_stride_b, ei) ||
+      !stride_ok(d->k_stride_h, ei) || !stride_ok(d->k_stride_s, ei) || !stride_ok(d->v_stride_b, ei) ||
+      !stride_ok(d->v_stride_h, ei) || !stride_ok(d->v_stride_s, ei) || !stride_ok(d->out_stride_b, eo) ||
+      !stride_ok(d->out_stride_h, eo))
+    return GQA_ERR_ALIGN;
+  return GQA_OK;
+}
+
+// Split plan.  Chunk length T; n = ceil(max_seq / T) chunks.  The heuristic
+// aims at ~768 workgroups (3 per compute unit) with at least one 32-key step
+// per wave (T >= 128, a multiple of 128).
+void decode_plan(const gqa_decode_desc* d, int32_t* T, int32_t* n) {
+  int64_t t;
+  if (d->kv_split_tokens >= d->max_seq) {
+    t = d->max_seq;
+  } else if (d->kv_split_tokens > 0) {
+    t = d->kv_split_tokens;
+  } else {
+    const int64_t base = (int64_t)d->batch * d->num_kv_heads;
+    const int64_t want = (768 + base - 1) / base;
+    t = ((int64_t)d->max_seq + want - 1) / want;
+    t = ((t + 127) / 128) * 128;
+    if (t < 128) t = 128;
+    if (t > d->max_seq) t = d->max_seq;
+  }
+  *T = (int32_t)t;
+  *n = (int32_t)(((int64_t)d->max_seq + t - 1) / t);
+}
+
+size_t decode_ws_bytes(const gqa_decode_desc* d, int32_t n) {
+  if (n <= 1) return 0;
+  const size_t slots = (size_t)d->batch * (size_t)d->num_q_heads * (size_t)n;
+  return slots * (GQA_ATTN_HEAD_DIM + 2) * sizeof(float);
+}
+
+gqa_status check_prefill_desc(const gqa_prefill_desc* d) {
+  if (d == nullptr) return GQA_ERR_NULL;
+  if (d->batch < 1 || d->num_q_heads < 1 || d->num_kv_heads < 1 || d->max_seq < 1) return GQA_ERR_SHAPE;
+  if (d->batch > kGridYZMax || d->num_q_heads > kGridYZMax) return GQA_ERR_SHAPE;
+  if (d->num_q_heads % d->num_kv_heads != 0) return GQA_ERR_SHAPE;
+  if (d->head_dim != GQA_ATTN_HEAD_DIM) return GQA_ERR_UNSUPPORTED;
+  if (d->in_dtype != GQA_BF16 || !dtype_ok(d->out_dtype)) return GQA_ERR_UNSUPPORTED;
+  if (d->causal != 0 && d->causal != 1) return GQA_ERR_SHAPE;
+  const int ei = 2, eo = elem_size(d->out_dtype);
+  const int64_t s[] = {d->q_stride_b, d->q_stride_h, d->q_stride_s, d->k_stride_b, d->k_stride_h, d->k_stride_s,
+                       d->v_stride_b, d->v_stride_h, d->v_stride_s};
+  for (int64_t x : s) {
+    if (x < 0) return GQA_ERR_SHAPE;
+  }
+  if (d->out_stride_b < 0 || d->out_stride_h < 0 || d->out_stride_s < 0) return GQA_ERR_SHAPE;
+  for (int64_t x : s) {
+    if (!stride_ok(x, ei)) return GQA_ERR_ALIGN;
+  }
+  if (!stride_ok(d->out_stride_b, eo) || !stride_ok(d->out_stride_h, eo) || !stride_ok(d->out_stride_s, eo))
+    return GQA_ERR_ALIGN;
+  return GQA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* gqa_attn_status_string(gqa_status status) {
+  switch (status) {
+    case GQA_OK: return "GQA_OK";
+    case GQA_ERR_NULL: return "GQA_ERR_NULL: a required pointer is NULL";
+    case GQA_ERR_SHAPE: return "GQA_ERR_SHAPE: invalid size, head ratio or stride";
+    case GQA_ERR_UNSUPPORTED: return "GQA_ERR_UNSUPPORTED: unsupported head_dim, dtype or group size";
+    case GQA_ERR_ALIGN: return "GQA_ERR_ALIGN: pointer or stride not 16-byte aligned";
+    case GQA_ERR_WORKSPACE: return "GQA_ERR_WORKSPACE: workspace missing or too small";
+    case GQA_ERR_HIP: return "GQA_ERR_HIP: kernel launch failed";
+  }
+  return "GQA_ERR_UNKNOWN: unknown status code";
+}
+
+int32_t gqa_attn_version(void) { return GQA_ATTN_VERSION; }
+
+gqa_status gqa_attn_decode_plan(const gqa_decode_desc* desc, int32_t* split_tokens, int32_t* num_splits) {
+  if (split_tokens == nullptr || num_splits == nullptr) return GQA_ERR_NULL;
+  const gqa_status st = check_decode_desc(desc);
+  if (st != GQA_OK) return st;
+  decode_plan(desc, split_tokens, num_splits);
+  return GQA_OK;
+}
+
+gqa_status gqa_attn_decode_workspace_size(const gqa_decode_desc* desc, size_t* bytes) {
+  if (bytes == nullptr) return GQA_ERR_NULL;
+  const gqa_status st = check_decode_desc(desc);
+  if (st != GQA_OK) return st;
+  int32_t T, n;
+  decode_plan(desc, &T, &n);
+  *bytes = decode_ws_bytes(desc, n);
+  return GQA_OK;
+}
+
+gqa_status gqa_attn_decode(const gqa_decode_desc* d, const void* q, const void* k_cache, const void* v_cache,
+                           const int32_t* seq_lens, const int32_t* positions, const void* q_norm_w,
+                           const void* k_norm_w, float rope_theta, void* out, void* workspace,
+                           size_t workspace_bytes, hipStream_t stream) {
+  gqa_status st = check_decode_desc(d);
+  if (st != GQA_OK) return st;
+  if (q == nullptr || k_cache == nullptr || v_cache == nullptr || seq_lens == nullptr || positions == nullptr ||
+      out == nullptr)
+    return GQA_ERR_NULL;
+  if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(out) || !aligned16(q_norm_w) ||
+      !aligned16(k_norm_w) || ((uintptr_t)seq_lens & 3u) || ((uintptr_t)positions & 3u))
+    return GQA_ERR_ALIGN;
+  int32_t T, n;
+  decode_plan(d, &T, &n);
+  const size_t need = decode_ws_bytes(d, n);
+  if (need > 0) {
+    if (workspace == nullptr || workspace_bytes < need) return GQA_ERR_WORKSPACE;
+    if (((uintptr_t)workspace & 255u) != 0) return GQA_ERR_ALIGN;
+  }
+
+  gqa::DecodeParams p{};
+  p.q = q;
+  p.k = k_cache;
+  p.v = v_cache;
+  p.seq_lens = seq_lens;
+  p.positions = positions;
+  p.q_norm_w = q_norm_w;
+  p.k_norm_w = k_norm_w;
+  p.out = out;
+  p.ws_o = need > 0 ? (float*)workspace : nullptr;
+  p.ws_ml = need > 0 ? (float*)((char*)workspace + (size_t)d->batch * d->num_q_heads * n * GQA_ATTN_HEAD_DIM * sizeof(float))
+                     : nullptr;
+  p.q_sb = d->q_stride_b;
+  p.q_sh = d->q_stride_h;
+  p.k_sb = d->k_stride_b;
+  p.k_sh = d->k_stride_h;
+  p.k_ss = d->k_stride_s;
+  p.v_sb = d->v_stride_b;
+  p.v_sh = d->v_stride_h;
+  p.v_ss = d->v_stride_s;
+  p.o_sb = d->out_stride_b;
+  p.o_sh = d->out_stride_h;
+  p.batch = d->batch;
+  p.num_q_heads = d->num_q_heads;
+  p.num_kv_heads = d->num_kv_heads;
+  p.group = d->num_q_heads / d->num_kv_heads;
+  p.max_seq = d->max_seq;
+  p.split = T;
+  p.n_split = n;
+  p.out_bf16 = d->out_dtype == GQA_BF16;
+  p.eps = d->eps;
+  p.scale_log2 = resolve_scale_log2(d->scale);
+  p.rope_theta = rope_theta > 0.f ? (double)rope_theta : 0.0;
+  return gqa::launch_decode(p, d->in_dtype == GQA_BF16, stream) == hipSuccess ? GQA_OK : GQA_ERR_HIP;
+}
+
+gqa_status gqa_attn_prefill(const gqa_prefill_desc* d, const void* q, const void* k, const void* v,
+                            const int32_t* seq_lens, const int32_t* positions, const void* q_norm_w,
+                            const void* k_norm_w, float rope_theta, void* out, hipStream_t stream) {
+  gqa_status st = check_prefill_desc(d);
+  if (st != GQA_OK) return st;
+  if (q == nullptr || k == nullptr || v == nullptr || seq_lens == nullptr || positions == nullptr || out == nullptr)
+    return GQA_ERR_NULL;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) || !aligned16(q_norm_w) ||
+      !aligned16(k_norm_w) || ((uintptr_t)seq_lens & 3u) || ((uintptr_t)positions & 3u))
+    return GQA_ERR_ALIGN;
+  gqa::PrefillParams p{};
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.seq_lens = seq_lens;
+  p.positions = positions;
+  p.q_norm_w = q_norm_w;
+  p.k_norm_w = k_norm_w;
+  p.out = out;
+  p.q_sb = d->q_stride_b;
+  p.q_sh = d->q_stride_h;
+  p.q_ss = d->q_stride_s;
+  p.k_sb = d->k_stride_b;
+  p.k_sh = d->k_stride_h;
+  p.k_ss = d->k_stride_s;
+  p.v_sb = d->v_stride_b;
+  p.v_sh = d->v_stride_h;
+  p.v_ss = d->v_stride_s;
+  p.o_sb = d->out_stride_b;
+  p.o_sh = d->out_stride_h;
+  p.o_ss = d->out_stride_s;
+  p.batch = d->batch;
+  p.num_q_heads = d->num_q_heads;
+  p.num_kv_heads = d->num_kv_heads;
+  p.group = d->num_q_heads / d->num_kv_heads;
+  p.max_seq = d->max_seq;
+  p.causal = d->causal;
+  p.out_bf16 = d->out_dtype == GQA_BF16;
+  p.n_qtiles = (d->max_seq + gqa::kPrefillBM - 1) / gqa::kPrefillBM;
+  p.eps = d->eps;
+  p.scale_log2 = resolve_scale_log2(d->scale);
+  p.rope_theta = rope_theta > 0.f ? (double)rope_theta : 0.0;
+  return gqa::launch_prefill(p, stream) == hipSuccess ? GQA_OK : GQA_ERR_HIP;
+}
+
+}  // extern "C"

@@ -1,0 +1,129 @@
+// Internal header of the gfx950 GQA attention library: launch parameter
+// structs, launcher declarations and small device helpers shared by the
+// decode and prefill kernels.  Not part of the public ABI (include/gqa_attn.h).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace gqa {
+
+constexpr int kHeadDim = 128;
+
+// ----------------------------------------------------------------- params
+
+struct DecodeParams {
+  const void* q;
+  const void* k;
+  const void* v;
+  const int32_t* seq_lens;
+  const int32_t* positions;
+  const void* q_norm_w;   // may be null: no RMSNorm on q
+  const void* k_norm_w;   // may be null: no RMSNorm on the new key row
+  void* out;
+  float* ws_o;            // [B][Hq][n_split][128] unnormalised partial O
+  float* ws_ml;           // [B][Hq][n_split][2]   (m in log2 units, l)
+  int64_t q_sb, q_sh;     // element strides
+  int64_t k_sb, k_sh, k_ss;
+  int64_t v_sb, v_sh, v_ss;
+  int64_t o_sb, o_sh;
+  int32_t batch, num_q_heads, num_kv_heads, group, max_seq;
+  int32_t split, n_split;
+  int32_t out_bf16;
+  float eps;
+  float scale_log2;       // softmax scale * log2(e): scores live in the log2 domain
+  double rope_theta;      // <= 0: RoPE off
+};
+
+struct PrefillParams {
+  const void* q;
+  const void* k;
+  const void* v;
+  const int32_t* seq_lens;
+  const int32_t* positions;
+  const void* q_norm_w;
+  const void* k_norm_w;
+  void* out;
+  int64_t q_sb, q_sh, q_ss;
+  int64_t k_sb, k_sh, k_ss;
+  int64_t v_sb, v_sh, v_ss;
+  int64_t o_sb, o_sh, o_ss;
+  int32_t batch, num_q_heads, num_kv_heads, group, max_seq;
+  int32_t causal;
+  int32_t out_bf16;
+  int32_t n_qtiles;
+  float eps;
+  float scale_log2;
+  double rope_theta;
+};
+
+// Launchers (return the hipGetLastError() of their launches).
+hipError_t launch_decode(const DecodeParams& p, bool in_bf16, hipStream_t stream);
+hipError_t launch_prefill(const PrefillParams& p, hipStream_t stream);
+
+// Prefill tiling, shared by the launcher and the host planning code.
+constexpr int kPrefillBM = 128;   // query rows per workgroup
+constexpr int kPrefillBN = 64;    // keys per K/V tile
+
+// ----------------------------------------------------------------- device helpers
+
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
+typedef __attribute__((ext_vector_type(4))) float f32x4;
+typedef __attribute__((ext_vector_type(16))) float f32x16;
+typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
+typedef __attribute__((ext_vector_type(2))) uint32_t u32x2;
+
+__device__ __forceinline__ float bf16lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// Two floats -> packed bf16 pair (round to nearest even; v_cvt_pk_bf16_f32).
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  bf16x2 v;
+  v[0] = (__bf16)lo;
+  v[1] = (__bf16)hi;
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+__device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
+
+// Element e (0..7) of 8 packed bf16 held in 4 dwords, as float.
+__device__ __forceinline__ float bf16_elem(const u32x4& v, int e) {
+  uint32_t w = v[e >> 1];
+  return (e & 1) ? bf16hi(w) : bf16lo(w);
+}
+
+// Low / high bf16 halves of two dwords combined into one dword:
+// (lo of a, lo of b) and (hi of a, hi of b).
+__device__ __forceinline__ uint32_t pair_lo(uint32_t a, uint32_t b) { return (a & 0xffffu) | (b << 16); }
+__device__ __forceinline__ uint32_t pair_hi(uint32_t a, uint32_t b) { return (a >> 16) | (b & 0xffff0000u); }
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+__device__ __forceinline__ float wave_max_xor(float v, int mask) {
+  return fmaxf(v, __shfl_xor(v, mask, 64));
+}
+__device__ __forceinline__ float wave_sum_xor(float v, int mask) { return v + __shfl_xor(v, mask, 64); }
+
+// cos / sin of the RoPE angle p * theta^(-2i/128), formed and evaluated in
+// double precision.  Used where only a few angles are needed.
+__device__ __forceinline__ void rope_cos_sin_f64(double pos, int i, double theta, float& c, float& s) {
+  const double inv = pow(theta, -2.0 * (double)i / (double)kHeadDim);
+  double sn, cn;
+  sincos(pos * inv, &sn, &cn);
+  c = (float)cn;
+  s = (float)sn;
+}
+
+// cos / sin of the angle pos * inv where inv_rev = inv / (2 pi): the product
+// and its reduction to [0, 1) revolutions are done in double, the final
+// sin / cos by the hardware instructions (which take revolutions).
+__device__ __forceinline__ void rope_cos_sin_rev(double pos, double inv_rev, float& c, float& s) {
+  double r = pos * inv_rev;
+  r -= floor(r);
+  const float rf = (float)r;
+  s = __builtin_amdgcn_sinf(rf);
+  c = __builtin_amdgcn_cosf(rf);
+}
+
+}  // namespace gqa

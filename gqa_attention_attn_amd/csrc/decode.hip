@@ -1,0 +1,548 @@
+// Grouped-query decode attention for gfx950 (MI355X): split-KV partition
+// kernel with the fused QK-norm + RoPE prologue, and the log-sum-exp merge.
+//
+// Algorithm (the pages):
+//  * "ADR-0060: AHBM GQA Fused Attention Kernel (Llama3-70B)", section 5.2:
+//    the G query heads of one KV head are folded into the matrix M dimension
+//    so that one K/V tile read from memory serves all G heads; section 3:
+//    per K/V tile, S = scale * Q K^T, running max m, P = exp(S - m_new),
+//    corr = exp(m - m_new), l = l*corr + sum P, O = O*corr + P V, seeded
+//    (-inf, 0, 0); section 4: split partials (m, l, O) are combined by the
+//    log-sum-exp merge and normalised once; section 2.2: chunk c of a
+//    sequence covers a contiguous block of keys.
+//  * "Qwen3-14B Optimization", section 2.1 "Shape 4" / #796: QK-norm and
+//    RoPE run inside the attention stage; #602: RoPE on lo/hi halves.
+//
+// gfx950 mapping (not the pages' design, which targets an NPU / simulator):
+//  * one workgroup = (chunk c, KV head h, sequence b), 4 waves of 64 lanes;
+//    wave w handles 32-key steps w, w+4, ... of the chunk and keeps its own
+//    online-softmax state; the 4 states are merged through LDS at the end.
+//  * S^T = K Q'^T and O^T = V^T P^T run on v_mfma_f32_16x16x32_bf16 (bf16
+//    inputs) or v_mfma_f32_16x16x4_f32 (f32 inputs) with the G <= 16 query
+//    rows as the 16-wide N dimension.  In this orientation a lane owns one
+//    query head (lane % 16), so the row max needs only two cross-lane steps,
+//    and V rows are read with 16 lanes covering one full 256-byte row; the
+//    8x8 bf16 transpose that V^T needs is done in registers.
+//  * K and V are streamed straight from HBM into registers, one step ahead.
+#include "common.hpp"
+
+namespace gqa {
+namespace {
+
+constexpr int kWaves = 4;
+constexpr int kThreads = kWaves * 64;
+constexpr int kStep = 32;        // keys per wave step
+constexpr int kORow = 132;       // padded LDS row (floats) of the in-workgroup merge
+
+struct DecodeSmem {
+  float cs[64][2];               // RoPE cos / sin at positions[b]
+  float qp[16][kHeadDim];        // q' rows after the prologue (rows >= G are zero)
+  float kn[kHeadDim];            // the new key row after the prologue
+  float mo[kWaves][16][kORow];   // per-wave unnormalised O (in-workgroup merge)
+  float mm[kWaves][16];
+  float ml[kWaves][16];
+};
+
+template <bool BF16>
+__device__ __forceinline__ void load_half_row(const void* row, int c16, float (&x)[8]) {
+  // x[0..3] = dims 4*c16 .. 4*c16+3; x[4..7] = dims 64+4*c16 .. 64+4*c16+3
+  if constexpr (BF16) {
+    const uint16_t* r = (const uint16_t*)row;
+    const u32x2 lo = *(const u32x2*)(r + 4 * c16);
+    const u32x2 hi = *(const u32x2*)(r + 64 + 4 * c16);
+    x[0] = bf16lo(lo[0]); x[1] = bf16hi(lo[0]); x[2] = bf16lo(lo[1]); x[3] = bf16hi(lo[1]);
+    x[4] = bf16lo(hi[0]); x[5] = bf16hi(hi[0]); x[6] = bf16lo(hi[1]); x[7] = bf16hi(hi[1]);
+  } else {
+    const float* r = (const float*)row;
+    const f32x4 lo = *(const f32x4*)(r + 4 * c16);
+    const f32x4 hi = *(const f32x4*)(r + 64 + 4 * c16);
+    #pragma unroll
+    for (int j = 0; j < 4; ++j) { x[j] = lo[j]; x[4 + j] = hi[j]; }
+  }
+}
+
+// The prologue on one row held by 16 consecutive lanes (8 elements each):
+// RMSNorm over the 128 elements (skipped if gamma is null), then RoPE with
+// the cos/sin table (skipped if !rope).  All 16 lanes must be active.
+template <bool BF16>
+__device__ __forceinline__ void prologue_row(float (&x)[8], int c16, const void* gamma, float eps, bool rope,
+                                             const float (*cs)[2]) {
+  if (gamma != nullptr) {
+    float ss = 0.f;
+    #pragma unroll
+    for (int j = 0; j < 8; ++j) ss += x[j] * x[j];
+    ss += __shfl_xor(ss, 1, 16);
+    ss += __shfl_xor(ss, 2, 16);
+    ss += __shfl_xor(ss, 4, 16);
+    ss += __shfl_xor(ss, 8, 16);
+    const float r = 1.0f / sqrtf(ss * (1.0f / kHeadDim) + eps);
+    float g[8];
+    load_half_row<BF16>(gamma, c16, g);
+    #pragma unroll
+    for (int j = 0; j < 8; ++j) x[j] = x[j] * r * g[j];
+  }
+  if (rope) {
+    #pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const float c = cs[4 * c16 + j][0], s = cs[4 * c16 + j][1];
+      const float lo = x[j], hi = x[4 + j];
+      x[j] = lo * c - hi * s;
+      x[4 + j] = hi * c + lo * s;
+    }
+  }
+}
+
+// ----------------------------------------------------------------- K/V step buffers
+
+struct StepBF16 {
+  u32x4 k[2][4];   // K rows key0 + 16*gi + (lane%16), dims 32*(lane/16) + 8*kb .. +8
+  u32x4 v[8];      // V rows key0 + vkey(t), dims 8*(lane%16) .. +8
+};
+
+struct StepF32 {
+  f32x4 k[2][8];   // K rows key0 + 16*gi + (lane%16), dims 32*(lane/16) .. +32
+  f32x4 v[8][2];   // V rows key0 + 16*gi + 4*(lane/16) + i (e = 4*gi + i), dims 8*(lane%16) .. +8
+};
+
+// key offset (within a 32-key step) of the t-th V row a bf16 lane loads; the
+// same permutation orders the P^T operand: t < 4 -> 4*q4 + t, else 16 + 4*q4 + t - 4
+__device__ __forceinline__ int vkey_bf16(int q4, int t) { return (t < 4) ? 4 * q4 + t : 12 + 4 * q4 + t; }
+
+__device__ __forceinline__ void load_step(StepBF16& st, const uint8_t* kb, const uint8_t* vb, int64_t kss,
+                                          int64_t vss, int key0, int kend, bool full, int n16, int q4) {
+  #pragma unroll
+  for (int gi = 0; gi < 2; ++gi) {
+    const int key = key0 + 16 * gi + n16;
+    const u32x4* src = (const u32x4*)(kb + (int64_t)key * kss + 64 * q4);
+    if (full || key < kend) {
+      #pragma unroll
+      for (int j = 0; j < 4; ++j) st.k[gi][j] = src[j];
+    } else {
+      #pragma unroll
+      for (int j = 0; j < 4; ++j) st.k[gi][j] = u32x4{0, 0, 0, 0};
+    }
+  }
+  #pragma unroll
+  for (int t = 0; t < 8; ++t) {
+    const int key = key0 + vkey_bf16(q4, t);
+    const u32x4* src = (const u32x4*)(vb + (int64_t)key * vss + 16 * n16);
+    st.v[t] = (full || key < kend) ? *src : u32x4{0, 0, 0, 0};
+  }
+}
+
+__device__ __forceinline__ void load_step(StepF32& st, const uint8_t* kb, const uint8_t* vb, int64_t kss,
+                                          int64_t vss, int key0, int kend, bool full, int n16, int q4) {
+  #pragma unroll
+  for (int gi = 0; gi < 2; ++gi) {
+    const int key = key0 + 16 * gi + n16;
+    const f32x4* src = (const f32x4*)(kb + (int64_t)key * kss + 128 * q4);
+    if (full || key < kend) {
+      #pragma unroll
+      for (int j = 0; j < 8; ++j) st.k[gi][j] = src[j];
+    } else {
+      #pragma unroll
+      for (int j = 0; j < 8; ++j) st.k[gi][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+  }
+  #pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const int key = key0 + 16 * (e >> 2) + 4 * q4 + (e & 3);
+    const f32x4* src = (const f32x4*)(vb + (int64_t)key * vss + 32 * n16);
+    if (full || key < kend) {
+      st.v[e][0] = src[0];
+      st.v[e][1] = src[1];
+    } else {
+      st.v[e][0] = f32x4{0.f, 0.f, 0.f, 0.f};
+      st.v[e][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+  }
+}
+
+// Replace the raw new-key row by its prologue output (lanes holding key kn).
+__device__ __forceinline__ void put_new_key(StepBF16& st, const float* knl, int key0, int kn, int n16, int q4) {
+  const int off = kn - key0;
+  if ((off & 15) != n16) return;
+  u32x4 f[4];
+  #pragma unroll
+  for (int kb = 0; kb < 4; ++kb) {
+    const float* s = knl + 32 * q4 + 8 * kb;
+    f[kb] = u32x4{pack_bf16x2(s[0], s[1]), pack_bf16x2(s[2], s[3]), pack_bf16x2(s[4], s[5]), pack_bf16x2(s[6], s[7])};
+  }
+  #pragma unroll
+  for (int gi = 0; gi < 2; ++gi)   // static register indices: no scratch
+    if ((off >> 4) == gi)
+      #pragma unroll
+      for (int kb = 0; kb < 4; ++kb) st.k[gi][kb] = f[kb];
+}
+
+__device__ __forceinline__ void put_new_key(StepF32& st, const float* knl, int key0, int kn, int n16, int q4) {
+  const int off = kn - key0;
+  if ((off & 15) != n16) return;
+  #pragma unroll
+  for (int gi = 0; gi < 2; ++gi)
+    if ((off >> 4) == gi)
+      #pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const float* s = knl + 32 * q4 + 4 * j;
+        st.k[gi][j] = f32x4{s[0], s[1], s[2], s[3]};
+      }
+}
+
+// ----------------------------------------------------------------- one step of the sweep
+
+struct QFragBF16 { bf16x8 q[4]; };
+struct QFragF32 { float q[32]; };
+
+struct RunState {
+  f32x4 o[8];      // O^T tiles: lane holds O[g = lane%16][dim (4*(lane/16)+i)*8 + T] in o[T][i]
+  float m;         // running max (log2 units), same in the 4 lanes of one query head
+  float l;         // this lane's share of the running normaliser
+};
+
+// scores: s[4*gi + i] = S[key key0 + 16*gi + 4*q4 + i][g = lane%16] (log2 units)
+__device__ __forceinline__ void scores(const StepBF16& st, const QFragBF16& qf, float scale_log2, float (&s)[8]) {
+  #pragma unroll
+  for (int gi = 0; gi < 2; ++gi) {
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    #pragma unroll
+    for (int kb = 0; kb < 4; ++kb)
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(st.k[gi][kb]), qf.q[kb], acc, 0, 0, 0);
+    #pragma unroll
+    for (int i = 0; i < 4; ++i) s[4 * gi + i] = acc[i] * scale_log2;
+  }
+}
+
+__device__ __forceinline__ void scores(const StepF32& st, const QFragF32& qf, float scale_log2, float (&s)[8]) {
+  #pragma unroll
+  for (int gi = 0; gi < 2; ++gi) {
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    #pragma unroll
+    for (int j = 0; j < 8; ++j)
+      #pragma unroll
+      for (int e = 0; e < 4; ++e)
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(st.k[gi][j][e], qf.q[4 * j + e], acc, 0, 0, 0);
+    #pragma unroll
+    for (int i = 0; i < 4; ++i) s[4 * gi + i] = acc[i] * scale_log2;
+  }
+}
+
+__device__ __forceinline__ void accumulate_pv(const StepBF16& st, const float (&p)[8], RunState& rs) {
+  // P^T operand: slot t of lane group q4 <-> key vkey_bf16(q4, t) = the score
+  // order s[0..7] of this lane.
+  const u32x4 pf = {pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]), pack_bf16x2(p[4], p[5]),
+                    pack_bf16x2(p[6], p[7])};
+  #pragma unroll
+  for (int T = 0; T < 8; ++T) {
+    const int w = T >> 1;
+    u32x4 a;
+    #pragma unroll
+    for (int u = 0; u < 4; ++u)
+      a[u] = (T & 1) ? pair_hi(st.v[2 * u][w], st.v[2 * u + 1][w]) : pair_lo(st.v[2 * u][w], st.v[2 * u + 1][w]);
+    rs.o[T] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a), as_bf16x8(pf), rs.o[T], 0, 0, 0);
+  }
+}
+
+__device__ __forceinline__ void accumulate_pv(const StepF32& st, const float (&p)[8], RunState& rs) {
+  #pragma unroll
+  for (int e = 0; e < 8; ++e)
+    #pragma unroll
+    for (int T = 0; T < 8; ++T)
+      rs.o[T] = __builtin_amdgcn_mfma_f32_16x16x4f32(st.v[e][T >> 2][T & 3], p[e], rs.o[T], 0, 0, 0);
+}
+
+template <class Step, class QFrag>
+__device__ __forceinline__ void sweep_step(const Step& st, const QFrag& qf, RunState& rs, float scale_log2,
+                                           int key0, int kend, bool full, int q4) {
+  float s[8];
+  scores(st, qf, scale_log2, s);
+  if (!full) {
+    #pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int key = key0 + 16 * (e >> 2) + 4 * q4 + (e & 3);
+      if (key >= kend) s[e] = -INFINITY;
+    }
+  }
+  float mx = s[0];
+  for (int e = 1; e < 8; ++e) mx = fmaxf(mx, s[e]);
+  mx = wave_max_xor(mx, 16);
+  mx = wave_max_xor(mx, 32);
+  const float m_new = fmaxf(rs.m, mx);
+  const float corr = fast_exp2(rs.m - m_new);   // 0 on the first step (m = -inf)
+  float p[8];
+  float ps = 0.f;
+  #pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    p[e] = fast_exp2(s[e] - m_new);
+    ps += p[e];
+  }
+  rs.l = rs.l * corr + ps;
+  rs.m = m_new;
+  #pragma unroll
+  for (int T = 0; T < 8; ++T) rs.o[T] *= corr;
+  accumulate_pv(st, p, rs);
+}
+
+template <bool BF16>
+__global__ __launch_bounds__(kThreads, 2) void decode_partition_kernel(const DecodeParams p) {
+  using Step = typename std::conditional<BF16, StepBF16, StepF32>::type;
+  using QFrag = typename std::conditional<BF16, QFragBF16, QFragF32>::type;
+  constexpr int kElem = BF16 ? 2 : 4;
+
+  __shared__ DecodeSmem sm;
+
+  const int c = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int n16 = lane & 15, q4 = lane >> 4;
+  const int G = p.group;
+  const bool direct = p.n_split == 1;
+
+  int L = p.seq_lens[b];
+  L = L < 0 ? 0 : (L > p.max_seq ? p.max_seq : L);
+  const int c0 = c * p.split;
+  if (c0 >= L) {
+    if (direct && c == 0) {   // L == 0: defined as an all-zero output row
+      const int g = tid >> 4, d8 = (tid & 15) * 8;
+      if (g < G) {
+        uint8_t* o = (uint8_t*)p.out + ((int64_t)b * p.o_sb + (int64_t)(h * G + g) * p.o_sh) * (p.out_bf16 ? 2 : 4);
+        if (p.out_bf16) {
+          *(u32x4*)(o + 2 * d8) = u32x4{0, 0, 0, 0};
+        } else {
+          *(f32x4*)(o + 4 * d8) = f32x4{0.f, 0.f, 0.f, 0.f};
+          *(f32x4*)(o + 4 * d8 + 16) = f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+      }
+    }
+    return;
+  }
+  const int c1 = min(c0 + p.split, L);
+  const bool rope = p.rope_theta > 0.0;
+  const bool k_pro = rope || p.k_norm_w != nullptr;
+  const bool has_new = k_pro && c1 == L;   // this chunk holds slot L-1
+  const double pos = (double)p.positions[b];
+
+  // ---- prologue: RoPE table, q' (and the new key row) into LDS
+  if (rope && tid < 64) rope_cos_sin_f64(pos, tid, p.rope_theta, sm.cs[tid][0], sm.cs[tid][1]);
+  __syncthreads();
+  {
+    const int r = tid >> 4, c16 = tid & 15;
+    float x[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    if (r < G) {
+      const uint8_t* row = (const uint8_t*)p.q + ((int64_t)b * p.q_sb + (int64_t)(h * G + r) * p.q_sh) * kElem;
+      load_half_row<BF16>(row, c16, x);
+    }
+    prologue_row<BF16>(x, c16, p.q_norm_w, p.eps, rope, sm.cs);
+    #pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      sm.qp[r][4 * c16 + j] = x[j];
+      sm.qp[r][64 + 4 * c16 + j] = x[4 + j];
+    }
+    if (has_new && tid < 16) {
+      const uint8_t* row = (const uint8_t*)p.k + ((int64_t)b * p.k_sb + (int64_t)h * p.k_sh + (int64_t)(L - 1) * p.k_ss) * kElem;
+      float y[8];
+      load_half_row<BF16>(row, c16, y);
+      prologue_row<BF16>(y, c16, p.k_norm_w, p.eps, rope, sm.cs);
+      #pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        sm.kn[4 * c16 + j] = y[j];
+        sm.kn[64 + 4 * c16 + j] = y[4 + j];
+      }
+    }
+  }
+  __syncthreads();
+
+  QFrag qf;
+  if constexpr (BF16) {
+    #pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+      const float* s = &sm.qp[n16][32 * q4 + 8 * kb];
+      qf.q[kb] = as_bf16x8(u32x4{pack_bf16x2(s[0], s[1]), pack_bf16x2(s[2], s[3]), pack_bf16x2(s[4], s[5]),
+                                 pack_bf16x2(s[6], s[7])});
+    }
+  } else {
+    #pragma unroll
+    for (int j = 0; j < 32; ++j) qf.q[j] = sm.qp[n16][32 * q4 + j];
+  }
+
+  // ---- the sweep over this chunk's keys
+  const uint8_t* kbase = (const uint8_t*)p.k + ((int64_t)b * p.k_sb + (int64_t)h * p.k_sh) * kElem;
+  const uint8_t* vbase = (const uint8_t*)p.v + ((int64_t)b * p.v_sb + (int64_t)h * p.v_sh) * kElem;
+  const int64_t kss = p.k_ss * kElem, vss = p.v_ss * kElem;
+  const int nsteps = (c1 - c0 + kStep - 1) / kStep;
+  const int kn = L - 1;
+
+  RunState rs;
+  #pragma unroll
+  for (int T = 0; T < 8; ++T) rs.o[T] = f32x4{0.f, 0.f, 0.f, 0.f};
+  rs.m = -INFINITY;
+  rs.l = 0.f;
+
+  int s = wave;
+  if constexpr (BF16) {
+    // two step buffers: the loads of step s + 4 are in flight while step s is computed
+    if (s < nsteps) {
+      Step A, B;
+      {
+        const int key0 = c0 + s * kStep;
+        load_step(A, kbase, vbase, kss, vss, key0, c1, key0 + kStep <= c1, n16, q4);
+      }
+      for (;;) {
+        const int keyA = c0 + s * kStep;
+        const bool fullA = keyA + kStep <= c1;
+        const int sB = s + kWaves;
+        const int keyB = c0 + sB * kStep;
+        if (sB < nsteps) load_step(B, kbase, vbase, kss, vss, keyB, c1, keyB + kStep <= c1, n16, q4);
+        if (has_new && kn >= keyA && kn < keyA + kStep) put_new_key(A, sm.kn, keyA, kn, n16, q4);
+        sweep_step(A, qf, rs, p.scale_log2, keyA, c1, fullA, q4);
+        if (sB >= nsteps) break;
+        const int sA2 = sB + kWaves;
+        const int keyA2 = c0 + sA2 * kStep;
+        if (sA2 < nsteps) load_step(A, kbase, vbase, kss, vss, keyA2, c1, keyA2 + kStep <= c1, n16, q4);
+        const bool fullB = keyB + kStep <= c1;
+        if (has_new && kn >= keyB && kn < keyB + kStep) put_new_key(B, sm.kn, keyB, kn, n16, q4);
+        sweep_step(B, qf, rs, p.scale_log2, keyB, c1, fullB, q4);
+        if (sA2 >= nsteps) break;
+        s = sA2;
+      }
+    }
+  } else {
+    // f32 steps are twice as large: one buffer (the f32 path serves small parity shapes)
+    for (; s < nsteps; s += kWaves) {
+      Step A;
+      const int key0 = c0 + s * kStep;
+      const bool full = key0 + kStep <= c1;
+      load_step(A, kbase, vbase, kss, vss, key0, c1, full, n16, q4);
+      if (has_new && kn >= key0 && kn < key0 + kStep) put_new_key(A, sm.kn, key0, kn, n16, q4);
+      sweep_step(A, qf, rs, p.scale_log2, key0, c1, full, q4);
+    }
+  }
+
+  // ---- merge the 4 wave states of this workgroup (ADR-0060 section 4 merge)
+  rs.l = wave_sum_xor(rs.l, 16);
+  rs.l = wave_sum_xor(rs.l, 32);
+  if (q4 == 0) {
+    sm.mm[wave][n16] = rs.m;
+    sm.ml[wave][n16] = rs.l;
+  }
+  #pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    float* dst = &sm.mo[wave][n16][(4 * q4 + i) * 8];
+    *(f32x4*)dst = f32x4{rs.o[0][i], rs.o[1][i], rs.o[2][i], rs.o[3][i]};
+    *(f32x4*)(dst + 4) = f32x4{rs.o[4][i], rs.o[5][i], rs.o[6][i], rs.o[7][i]};
+  }
+  __syncthreads();
+
+  const int g = tid >> 4, d8 = (tid & 15) * 8;
+  if (g >= G) return;
+  float M = sm.mm[0][g];
+  for (int w = 1; w < kWaves; ++w) M = fmaxf(M, sm.mm[w][g]);
+  float lt = 0.f;
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  #pragma unroll
+  for (int w = 0; w < kWaves; ++w) {
+    const float sc = fast_exp2(sm.mm[w][g] - M);   // 0 for a wave that saw no key
+    lt += sc * sm.ml[w][g];
+    const float* src = &sm.mo[w][g][d8];
+    #pragma unroll
+    for (int j = 0; j < 8; ++j) acc[j] += sc * src[j];
+  }
+  const int hq = h * G + g;
+  if (direct) {
+    const float inv = 1.0f / lt;
+    uint8_t* o = (uint8_t*)p.out + ((int64_t)b * p.o_sb + (int64_t)hq * p.o_sh) * (p.out_bf16 ? 2 : 4);
+    if (p.out_bf16) {
+      *(u32x4*)(o + 2 * d8) = u32x4{pack_bf16x2(acc[0] * inv, acc[1] * inv), pack_bf16x2(acc[2] * inv, acc[3] * inv),
+                                    pack_bf16x2(acc[4] * inv, acc[5] * inv), pack_bf16x2(acc[6] * inv, acc[7] * inv)};
+    } else {
+      *(f32x4*)(o + 4 * d8) = f32x4{acc[0] * inv, acc[1] * inv, acc[2] * inv, acc[3] * inv};
+      *(f32x4*)(o + 4 * d8 + 16) = f32x4{acc[4] * inv, acc[5] * inv, acc[6] * inv, acc[7] * inv};
+    }
+  } else {
+    const int64_t slot = ((int64_t)b * p.num_q_heads + hq) * p.n_split + c;
+    float* wo = p.ws_o + slot * kHeadDim + d8;
+    *(f32x4*)wo = f32x4{acc[0], acc[1], acc[2], acc[3]};
+    *(f32x4*)(wo + 4) = f32x4{acc[4], acc[5], acc[6], acc[7]};
+    if ((tid & 15) == 0) {
+      p.ws_ml[2 * slot] = M;
+      p.ws_ml[2 * slot + 1] = lt;
+    }
+  }
+}
+
+// ----------------------------------------------------------------- merge kernel
+// One workgroup per (q head, sequence): out = sum_c 2^(m_c - M) O_c / sum_c 2^(m_c - M) l_c
+// over the n = ceil(L / T) chunks that hold keys (ADR-0060 section 4).
+
+constexpr int kMergeThreads = 256;
+
+__global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(const DecodeParams p) {
+  __shared__ float red[kMergeThreads];
+  __shared__ float racc[8][kHeadDim + 4];
+  __shared__ float rl[8];
+
+  const int hq = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
+  int L = p.seq_lens[b];
+  L = L < 0 ? 0 : (L > p.max_seq ? p.max_seq : L);
+  const int n = (L + p.split - 1) / p.split;
+  uint8_t* o = (uint8_t*)p.out + ((int64_t)b * p.o_sb + (int64_t)hq * p.o_sh) * (p.out_bf16 ? 2 : 4);
+  if (n == 0) {
+    if (tid < 32) {
+      if (p.out_bf16) *(u32x2*)(o + 8 * tid) = u32x2{0, 0};
+      else *(f32x4*)(o + 16 * tid) = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+    return;
+  }
+  const int64_t slot0 = ((int64_t)b * p.num_q_heads + hq) * p.n_split;
+  float mx = -INFINITY;
+  for (int c = tid; c < n; c += kMergeThreads) mx = fmaxf(mx, p.ws_ml[2 * (slot0 + c)]);
+  red[tid] = mx;
+  __syncthreads();
+  for (int w = kMergeThreads / 2; w > 0; w >>= 1) {
+    if (tid < w) red[tid] = fmaxf(red[tid], red[tid + w]);
+    __syncthreads();
+  }
+  const float M = red[0];
+
+  const int dg = tid & 31, sg = tid >> 5;     // 4 dims x 8 split groups
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  float ls = 0.f;
+  for (int c = sg; c < n; c += 8) {
+    const float m_c = p.ws_ml[2 * (slot0 + c)];
+    const float l_c = p.ws_ml[2 * (slot0 + c) + 1];
+    const float w = fast_exp2(m_c - M);
+    const f32x4 oc = *(const f32x4*)(p.ws_o + (slot0 + c) * kHeadDim + 4 * dg);
+    acc += w * oc;
+    ls += w * l_c;
+  }
+  *(f32x4*)&racc[sg][4 * dg] = acc;
+  if (dg == 0) rl[sg] = ls;
+  __syncthreads();
+  if (tid < 32) {
+    f32x4 t = *(const f32x4*)&racc[0][4 * tid];
+    float lt = rl[0];
+    for (int j = 1; j < 8; ++j) {
+      t += *(const f32x4*)&racc[j][4 * tid];
+      lt += rl[j];
+    }
+    const float inv = 1.0f / lt;
+    t *= inv;
+    if (p.out_bf16) *(u32x2*)(o + 8 * tid) = u32x2{pack_bf16x2(t[0], t[1]), pack_bf16x2(t[2], t[3])};
+    else *(f32x4*)(o + 16 * tid) = t;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_decode(const DecodeParams& p, bool in_bf16, hipStream_t stream) {
+  const dim3 grid(p.n_split, p.num_kv_heads, p.batch);
+  if (in_bf16) {
+    hipLaunchKernelGGL(decode_partition_kernel<true>, grid, dim3(kThreads), 0, stream, p);
+  } else {
+    hipLaunchKernelGGL(decode_partition_kernel<false>, grid, dim3(kThreads), 0, stream, p);
+  }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || p.n_split == 1) return e;
+  hipLaunchKernelGGL(decode_merge_kernel, dim3(p.num_q_heads, p.batch), dim3(kMergeThreads), 0, stream, p);
+  return hipGetLastError();
+}
+
+}  // namespace gqa

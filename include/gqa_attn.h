@@ -1,0 +1,189 @@
+/*
+ * gqa_attn.h -- C ABI of the grouped-query fused attention library for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The operation is the fused attention stage of a grouped-query-attention
+ * decoder layer: a per-head RMSNorm ("QK-norm") and a rotary position
+ * embedding (RoPE) applied to the projected query and key rows, then
+ * softmax(scale * Q K^T) V where G = Hq / Hkv query heads share one KV head.
+ *
+ * Sources (the pages this library is built from):
+ *  - "Qwen3-14B Optimization" (pypto-lib case study), section 2.1 "Shape 4"
+ *    and change #796: QK-norm and RoPE are folded into the fused attention
+ *    stage; change #602: the G query heads of one (KV head, batch) are
+ *    batched into one tile, RoPE rotates the lo/hi halves of the head dim.
+ *  - "ADR-0060: AHBM GQA Fused Attention Kernel (Llama3-70B)": section 0.5.3
+ *    (inputs, softmax_scale = 1/sqrt(d)), section 0.5.4 (only O is an
+ *    output; S and P are never materialised), section 3 (online softmax),
+ *    section 4 (log-sum-exp merge of split partials), section 5.2 (decode,
+ *    G heads folded into the matrix M dimension, query head h reads KV head
+ *    floor(h / G)), section 5.4 (causal classification in prefill).
+ *
+ * Conventions shared by every entry point
+ *  - All tensor pointers are DEVICE pointers (HIP device memory of the
+ *    current device); seq_lens / positions are device int32 arrays.
+ *  - Strides are in ELEMENTS.  The head dimension is always contiguous
+ *    (stride 1) and must equal 128.
+ *  - Tensor base pointers must be 16-byte aligned and every stride must be a
+ *    multiple of 16 bytes (8 bf16 or 4 f32 elements): kernels use 128-bit
+ *    loads.
+ *  - The caller owns every buffer.  The library allocates nothing per call,
+ *    keeps no mutable global state (calls are reentrant and thread-safe),
+ *    never writes q / k / v / caches / norm weights, and writes only `out`
+ *    (and `workspace` for decode).  Calls are asynchronous on `stream`; the
+ *    library never synchronises the host.
+ *  - Every argument check except GQA_ERR_HIP happens on the host before any
+ *    HIP call, so a rejected call has no device side effects.  No exception
+ *    and no abort crosses this ABI.
+ *  - Device-resident seq_lens are not checked on the host: kernels clamp a
+ *    length L to [0, max_seq]; L = 0 yields an all-zero output row.
+ *  - The prologue, per row x of 128 elements at RoPE position p:
+ *        y = x * (mean(x^2) + eps)^(-1/2) * gamma      (skipped if gamma NULL)
+ *        (y_i, y_{i+64}) <- (y_i cos a - y_{i+64} sin a,
+ *                            y_{i+64} cos a + y_i sin a),
+ *        a = p * theta^(-2i/128), i in [0, 64)          (skipped if theta <= 0)
+ *    gamma is one [128] vector shared by all heads, in `in_dtype`.
+ *    Angles are formed and range-reduced in double precision.
+ */
+#ifndef GQA_ATTN_H
+#define GQA_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define GQA_ATTN_HEAD_DIM 128
+#define GQA_ATTN_MAX_GROUP 16      /* largest supported G = Hq / Hkv in decode */
+#define GQA_ATTN_VERSION 1
+
+typedef enum gqa_status {
+  GQA_OK = 0,
+  GQA_ERR_NULL = 1,        /* a required pointer is NULL                          */
+  GQA_ERR_SHAPE = 2,       /* non-positive size, Hq % Hkv != 0, bad stride        */
+  GQA_ERR_UNSUPPORTED = 3, /* head_dim != 128, dtype, G too large, prefill f32    */
+  GQA_ERR_ALIGN = 4,       /* base pointer or stride not 16-byte aligned          */
+  GQA_ERR_WORKSPACE = 5,   /* workspace NULL or smaller than required             */
+  GQA_ERR_HIP = 6          /* a kernel launch failed (hipGetLastError)            */
+} gqa_status;
+
+typedef enum gqa_dtype {
+  GQA_F32 = 0,
+  GQA_BF16 = 1
+} gqa_dtype;
+
+/* Decode: one new token per sequence (T_q = 1). */
+typedef struct gqa_decode_desc {
+  int32_t batch;           /* B >= 1                                               */
+  int32_t num_q_heads;     /* Hq >= 1                                              */
+  int32_t num_kv_heads;    /* Hkv >= 1, Hq % Hkv == 0, Hq / Hkv <= 16             */
+  int32_t head_dim;        /* must be 128                                          */
+  int32_t max_seq;         /* cache capacity: rows [0, max_seq) of each (b, head)  */
+  int32_t in_dtype;        /* gqa_dtype of q, k_cache, v_cache, q_norm_w, k_norm_w */
+  int32_t out_dtype;       /* gqa_dtype of out                                     */
+  int32_t kv_split_tokens; /* keys per split-KV chunk: 0 = library heuristic,
+                              >= max_seq = one chunk (no merge); any T >= 1 ok    */
+  int64_t q_stride_b, q_stride_h;               /* q[b, h, :]                      */
+  int64_t k_stride_b, k_stride_h, k_stride_s;   /* k_cache[b, h, s, :]             */
+  int64_t v_stride_b, v_stride_h, v_stride_s;   /* v_cache[b, h, s, :]             */
+  int64_t out_stride_b, out_stride_h;           /* out[b, h, :]                    */
+  float eps;               /* RMSNorm epsilon (e.g. 1e-6)                          */
+  float scale;             /* softmax scale; <= 0 selects 1/sqrt(head_dim)         */
+} gqa_decode_desc;
+
+/* Prefill: self-attention over seq_lens[b] tokens per sequence (T_q = S_kv). */
+typedef struct gqa_prefill_desc {
+  int32_t batch;           /* B >= 1                                               */
+  int32_t num_q_heads;     /* Hq                                                   */
+  int32_t num_kv_heads;    /* Hkv, Hq % Hkv == 0                                   */
+  int32_t head_dim;        /* must be 128                                          */
+  int32_t max_seq;         /* S: token rows per sequence in q / k / v / out        */
+  int32_t in_dtype;        /* must be GQA_BF16 (bf16 MFMA path)                    */
+  int32_t out_dtype;       /* GQA_F32 or GQA_BF16                                  */
+  int32_t causal;          /* 1: query i sees keys j <= i; 0: all keys < S_b       */
+  int64_t q_stride_b, q_stride_h, q_stride_s;
+  int64_t k_stride_b, k_stride_h, k_stride_s;
+  int64_t v_stride_b, v_stride_h, v_stride_s;
+  int64_t out_stride_b, out_stride_h, out_stride_s;
+  float eps;
+  float scale;             /* <= 0 selects 1/sqrt(head_dim)                        */
+} gqa_prefill_desc;
+
+/* Human-readable name of a status code (static storage; never NULL). */
+const char* gqa_attn_status_string(gqa_status status);
+
+/* Version of this ABI (GQA_ATTN_VERSION). */
+int32_t gqa_attn_version(void);
+
+/*
+ * Split plan for a decode call (host only, no HIP call): the chunk length T
+ * the call will use and the number of chunks n = ceil(max_seq / T).  Chunk c
+ * covers keys [c*T, min((c+1)*T, L)) of a sequence of length L
+ * (ADR-0060 section 2.2 contiguous blocks; section 4 merge).
+ */
+gqa_status gqa_attn_decode_plan(const gqa_decode_desc* desc, int32_t* split_tokens, int32_t* num_splits);
+
+/*
+ * Bytes of device workspace gqa_attn_decode needs for `desc` (host only, no
+ * HIP call).  0 when the plan has a single chunk.  The workspace holds one
+ * unnormalised partial (m, l, O[128]) in f32 per (b, q head, chunk).
+ */
+gqa_status gqa_attn_decode_workspace_size(const gqa_decode_desc* desc, size_t* bytes);
+
+/*
+ * Grouped-query decode attention with the fused QK-norm + RoPE prologue
+ * ("Qwen3-14B Optimization" 2.1 / #796; ADR-0060 sections 3, 4, 5.2).
+ *
+ * For each sequence b with L = clamp(seq_lens[b], 0, max_seq) and each
+ * query head h (KV head kv = floor(h / G)):
+ *   q'   = prologue(q[b, h, :], q_norm_w, positions[b])
+ *   K'_j = k_cache[b, kv, j, :]                         for j < L-1
+ *          (already post-prologue: cached keys are never re-rotated)
+ *   K'_{L-1} = prologue(k_cache[b, kv, L-1, :], k_norm_w, positions[b])
+ *          (the raw projected key of the token being decoded)
+ *   out[b, h, :] = sum_j softmax_j(scale * q' . K'_j) v_cache[b, kv, j, :]
+ * Rows j >= L of the caches are never read.  The cache is not written back.
+ *
+ * q: [B, Hq, 128] (strides q_stride_*); k_cache, v_cache: [B, Hkv, max_seq,
+ * 128]; seq_lens, positions: [B] int32 (device); q_norm_w, k_norm_w: [128]
+ * in in_dtype or NULL; rope_theta <= 0 disables RoPE; out: [B, Hq, 128] in
+ * out_dtype.  workspace: device buffer of at least
+ * gqa_attn_decode_workspace_size bytes, 256-byte aligned (may be NULL when
+ * that size is 0); its contents on entry are ignored.
+ * Errors: GQA_ERR_NULL, GQA_ERR_SHAPE, GQA_ERR_UNSUPPORTED, GQA_ERR_ALIGN,
+ * GQA_ERR_WORKSPACE (checked on the host), GQA_ERR_HIP (launch failure).
+ */
+gqa_status gqa_attn_decode(const gqa_decode_desc* desc, const void* q, const void* k_cache,
+                           const void* v_cache, const int32_t* seq_lens, const int32_t* positions,
+                           const void* q_norm_w, const void* k_norm_w, float rope_theta, void* out,
+                           void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * Grouped-query causal prefill attention with the fused QK-norm + RoPE
+ * prologue (ADR-0060 sections 3 and 5.4; "Qwen3-14B Optimization" 2.1).
+ *
+ * For each sequence b with n = clamp(seq_lens[b], 0, max_seq), every token
+ * s < n sits at RoPE position positions[b] + s; both its query row (every
+ * head) and its key row go through the prologue.  Query i of head h attends
+ * keys j <= i (causal) or j < n (non-causal) of KV head floor(h / G):
+ *   out[b, h, i, :] = sum_j softmax_j(scale * q'_i . k'_j) v[b, kv, j, :]
+ * Rows s >= n of out are not written; rows s >= n of q / k / v are not read.
+ *
+ * q: [B, Hq, max_seq, 128]; k, v: [B, Hkv, max_seq, 128]; out: [B, Hq,
+ * max_seq, 128].  in_dtype must be GQA_BF16 (QK^T and P V run on bf16 MFMA
+ * with f32 accumulation; q', k' and P are rounded to bf16 before the MFMA).
+ * Errors: as gqa_attn_decode, without GQA_ERR_WORKSPACE.
+ */
+gqa_status gqa_attn_prefill(const gqa_prefill_desc* desc, const void* q, const void* k, const void* v,
+                            const int32_t* seq_lens, const int32_t* positions, const void* q_norm_w,
+                            const void* k_norm_w, float rope_theta, void* out, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GQA_ATTN_H */

@@ -1,0 +1,208 @@
+"""GPU parity of gqa_attn_decode (through the C ABI) against the fp64 oracle.
+
+Tolerances: max |err| <= 1e-5 for f32 inputs and <= 1e-2 for bf16 inputs
+(f32 accumulation, f32 output); a bf16 output adds half a bf16 ulp of |ref|.
+"""
+
+import numpy as np
+import pytest
+
+import gqa_attention_attn_amd as G
+import oracle as O
+import synth
+from gpu_util import compare, dev, ints, log, require_gpu
+
+pytestmark = pytest.mark.gpu
+
+ATOL_F32 = 1e-5
+ATOL_BF16 = 1e-2
+
+
+def tdtype(name):
+    import torch
+    return torch.bfloat16 if name == "bf16" else torch.float32
+
+
+def gpu_inputs(inp, dtype):
+    torch = require_gpu()
+    dt = tdtype(dtype)
+    return dict(q=dev(inp["q"], dt), k=dev(inp["k"], dt), v=dev(inp["v"], dt), qw=dev(inp["q_norm_w"], dt),
+                kw=dev(inp["k_norm_w"], dt), sl=ints(inp["seq_lens"]), pos=ints(inp["positions"]))
+
+
+def run(inp, dtype, split=0, out_dtype=None, g=None, out=None, workspace=None):
+    torch = require_gpu()
+    g = g or gpu_inputs(inp, dtype)
+    o = G.decode(g["q"], g["k"], g["v"], g["sl"], g["pos"], g["qw"], g["kw"], inp["rope_theta"], out=out,
+                 workspace=workspace, kv_split_tokens=split, eps=inp["eps"], out_dtype=out_dtype or torch.float32)
+    torch.cuda.synchronize()
+    return o
+
+
+def ref(inp):
+    return O.decode_ref(inp["q"], inp["k"], inp["v"], inp["seq_lens"], inp["positions"], inp["q_norm_w"],
+                        inp["k_norm_w"], inp["rope_theta"], inp["eps"])
+
+
+def small(B=3, Hq=10, Hkv=2, S=300, dtype="bf16", lens=None, norm=True, theta=1e6, seed=11):
+    w = synth.DecodeWorkload(f"small_decode_b{B}_h{Hq}_{Hkv}_s{S}", B, Hq, Hkv, S, dtype, norm, theta, 0,
+                             seed=seed)
+    inp = synth.make_decode(w)
+    if lens is not None:
+        inp["seq_lens"] = np.asarray(lens, dtype=np.int32)
+        inp["positions"] = np.maximum(inp["seq_lens"], 1).astype(np.int32) - 1 + 7
+        k, v = synth.make_decode(w, poison=False)["k"], synth.make_decode(w, poison=False)["v"]
+        for b in range(B):
+            L = max(0, min(int(lens[b]), S))
+            k[b, :, L:] = np.nan
+            v[b, :, L:] = np.nan
+        inp["k"], inp["v"] = k, v
+    return inp
+
+
+# ------------------------------------------------------------------ the five workloads' decode shapes
+
+def test_tiny_decode_f32_full():
+    inp = synth.make_decode(synth.TINY_DECODE_F32)
+    log(f"case {synth.TINY_DECODE_F32.name}")
+    out = run(inp, "f32", split=synth.TINY_DECODE_F32.split_tokens)
+    compare(out.cpu().numpy(), ref(inp), ATOL_F32, "tiny f32 decode")
+
+
+def test_qwen3_decode_b1_s4096_full():
+    w = synth.QWEN3_DECODE
+    log(f"case {w.name}")
+    inp = synth.make_decode(w)
+    out = run(inp, w.dtype, split=w.split_tokens)
+    compare(out.cpu().numpy(), ref(inp), ATOL_BF16, w.name)
+
+
+def test_qwen3_ragged_b32_full():
+    w = synth.QWEN3_RAGGED
+    log(f"case {w.name}")
+    inp = synth.make_decode(w)
+    out = run(inp, w.dtype, split=w.split_tokens)
+    compare(out.cpu().numpy(), ref(inp), ATOL_BF16, w.name)
+
+
+def test_llama70b_long_decode_full():
+    w = synth.LLAMA70B_LONG
+    log(f"case {w.name}")
+    inp = synth.make_decode(w)
+    out = run(inp, w.dtype, split=w.split_tokens)
+    compare(out.cpu().numpy(), ref(inp), ATOL_BF16, w.name)
+
+
+# ------------------------------------------------------------------ shapes, splits, edge cases
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("G_", [1, 2, 5, 8, 16])
+def test_group_sizes(dtype, G_):
+    Hkv = 2
+    inp = small(B=2, Hq=G_ * Hkv, Hkv=Hkv, S=200, dtype=dtype, lens=[200, 77], seed=G_)
+    log(f"case group={G_} dtype={dtype}")
+    for split in (0, 64, 200):
+        out = run(inp, dtype, split=split)
+        compare(out.cpu().numpy(), ref(inp), ATOL_F32 if dtype == "f32" else ATOL_BF16, f"G={G_} split={split}")
+
+
+@pytest.mark.parametrize("split", [1, 7, 32, 100, 128, 300, 1000])
+def test_split_sweep_ragged(split):
+    inp = small(B=3, Hq=10, Hkv=2, S=300, dtype="bf16", lens=[300, 133, 1])
+    log(f"case split={split}")
+    out = run(inp, "bf16", split=split)
+    compare(out.cpu().numpy(), ref(inp), ATOL_BF16, f"split {split}")
+
+
+def test_split_sweep_f32():
+    inp = small(B=2, Hq=5, Hkv=1, S=513, dtype="f32", lens=[513, 65])
+    r = ref(inp)
+    for split in (0, 1, 31, 33, 64, 513):
+        out = run(inp, "f32", split=split)
+        compare(out.cpu().numpy(), r, ATOL_F32, f"f32 split {split}")
+
+
+def test_empty_and_clamped_lengths():
+    inp = small(B=4, Hq=10, Hkv=2, S=96, dtype="bf16", lens=[0, 96, 5, 96])
+    inp["seq_lens"] = np.array([0, 96, 5, 1000], dtype=np.int32)   # 1000 is clamped to 96
+    for split in (0, 32, 96):
+        out = run(inp, "bf16", split=split).cpu().numpy()
+        assert np.all(out[0] == 0.0)
+        compare(out, ref(inp), ATOL_BF16, f"empty/clamped split {split}")
+
+
+@pytest.mark.parametrize("norm,theta", [(False, 0.0), (True, 0.0), (False, 5e5)])
+def test_prologue_switches(norm, theta):
+    for dtype in ("f32", "bf16"):
+        inp = small(B=2, Hq=16, Hkv=2, S=160, dtype=dtype, lens=[160, 40], norm=norm, theta=theta)
+        out = run(inp, dtype, split=64)
+        compare(out.cpu().numpy(), ref(inp), ATOL_F32 if dtype == "f32" else ATOL_BF16, f"norm={norm} theta={theta} {dtype}")
+
+
+def test_large_positions_rope_precision():
+    # positions far beyond the cache length: angles up to ~131071 rad must be exact enough
+    inp = small(B=2, Hq=8, Hkv=1, S=64, dtype="f32", lens=[64, 64], theta=5e5)
+    inp["positions"] = np.array([131071, 100003], dtype=np.int32)
+    out = run(inp, "f32", split=0)
+    compare(out.cpu().numpy(), ref(inp), ATOL_F32, "large positions f32")
+
+
+def test_bf16_output():
+    torch = require_gpu()
+    inp = small(B=2, Hq=10, Hkv=2, S=256, dtype="bf16", lens=[256, 100])
+    r = ref(inp)
+    out = run(inp, "bf16", split=64, out_dtype=torch.bfloat16).float().cpu().numpy()
+    tol = ATOL_BF16 + np.abs(r) * 2.0 ** -8
+    assert np.all(np.abs(out - r) <= tol)
+
+
+def test_ones_value_column_pin():
+    # one V column of ones: that output column is sum_j p_j = 1
+    for dtype, tol in (("f32", 1e-6), ("bf16", 3e-3)):
+        inp = small(B=2, Hq=10, Hkv=2, S=300, dtype=dtype, lens=[300, 45])
+        inp["v"][:, :, :, 17] = np.where(np.isnan(inp["v"][:, :, :, 17]), np.nan, 1.0)
+        out = run(inp, dtype, split=64).cpu().numpy()
+        err = np.abs(out[:, :, 17] - 1.0).max()
+        log(f"  ones column {dtype}: {err:.2e}")
+        assert err <= tol
+
+
+def test_deterministic_bitwise():
+    inp = small(B=2, Hq=40, Hkv=8, S=1024, dtype="bf16", lens=[1024, 999])
+    g = gpu_inputs(inp, "bf16")
+    a = run(inp, "bf16", split=128, g=g).cpu().numpy()
+    b = run(inp, "bf16", split=128, g=g).cpu().numpy()
+    assert np.array_equal(a, b)
+
+
+def test_poisoned_workspace_and_output_canaries():
+    torch = require_gpu()
+    inp = small(B=2, Hq=10, Hkv=2, S=300, dtype="bf16", lens=[300, 123])
+    g = gpu_inputs(inp, "bf16")
+    desc = G.decode_desc(g["q"], g["k"], g["v"], torch.empty(2, 10, 128, device="cuda"), kv_split_tokens=64)
+    ws = G.decode_workspace(desc, "cuda")
+    ws.view(torch.float32).fill_(float("nan"))
+    # out lives inside a larger buffer whose other elements are canaries
+    big = torch.full((2, 12, 160), 12345.0, device="cuda")
+    out = big[:, 1:11, 16:144]
+    run(inp, "bf16", split=64, g=g, out=out, workspace=ws)
+    got = big.cpu().numpy()
+    compare(got[:, 1:11, 16:144], ref(inp), ATOL_BF16, "strided out, NaN workspace")
+    mask = np.ones_like(got, dtype=bool)
+    mask[:, 1:11, 16:144] = False
+    assert np.all(got[mask] == 12345.0)
+
+
+def test_token_major_cache_layout_and_strided_q():
+    # caches stored [B, S, Hkv, d] (strides b, h, s = S*Hkv*d, d, Hkv*d); q with a padded head stride
+    torch = require_gpu()
+    inp = small(B=2, Hq=10, Hkv=2, S=200, dtype="bf16", lens=[200, 61])
+    kt = dev(np.ascontiguousarray(inp["k"].transpose(0, 2, 1, 3)), torch.bfloat16).permute(0, 2, 1, 3)
+    vt = dev(np.ascontiguousarray(inp["v"].transpose(0, 2, 1, 3)), torch.bfloat16).permute(0, 2, 1, 3)
+    qpad = torch.zeros(2, 10, 136, dtype=torch.bfloat16, device="cuda")
+    qpad[:, :, :128] = dev(inp["q"], torch.bfloat16)
+    q = qpad[:, :, :128]
+    g = dict(q=q, k=kt, v=vt, qw=dev(inp["q_norm_w"], torch.bfloat16), kw=dev(inp["k_norm_w"], torch.bfloat16),
+             sl=ints(inp["seq_lens"]), pos=ints(inp["positions"]))
+    out = run(inp, "bf16", split=64, g=g)
+    compare(out.cpu().numpy(), ref(inp), ATOL_BF16, "token-major cache")
