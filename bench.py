@@ -1,0 +1,299 @@
+#!/usr/bin/env python3
+"""Benchmark of the grouped-query fused attention hot path on one MI355X.
+
+Headline (one JSON line on stdout): decode attention of the Qwen3-14B shape
+(B = 1, 40 query heads over 8 KV heads, d = 128, 4096 cached keys, bf16,
+fused QK-norm + RoPE, split-KV + log-sum-exp merge).  One step = one full
+decode call (partition + merge).  `value` is the achieved HBM bandwidth in
+algorithmic bytes (valid K/V rows + q + out) per second.  Inputs are resident
+in HBM; K/V rotate over enough distinct buffer sets (>= 1 GiB) that the
+256 MB Infinity Cache cannot serve them.  The K timed steps are replayed
+from a HIP graph.
+
+Also reported in the same line: per-kernel durations (HIP events on the
+launch stream) and the roofline of the dominant kernel, the oracle timed on
+the host cores, the causal prefill of the Qwen3-14B shape (S = 4096) in
+TFLOP/s against the bf16 MFMA peak, and the long-context / ragged decodes.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-extra] [--no-cpu-baseline]
+"""
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "GQA decode µs/step + achieved HBM GB/s; causal prefill TFLOP/s (1×MI355X)"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, published
+LLC_BYTES = 1 << 30            # rotate at least this many bytes of K/V
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def decode_bytes(lens, Hkv, Hq, B, in_elem=2, out_elem=4, d=128):
+    """Algorithmic bytes of one decode call: valid K and V rows, q and out."""
+    return int(sum(int(x) for x in lens)) * Hkv * 2 * d * in_elem + B * Hq * d * (in_elem + out_elem)
+
+
+def prefill_flops(lens, Hq, d=128, causal=True):
+    """QK^T and PV multiply-adds over the visible (query, key) pairs, 2 flops each."""
+    pairs = sum(n * (n + 1) // 2 if causal else n * n for n in (int(x) for x in lens))
+    return 4 * d * Hq * pairs
+
+
+class DecodeCase:
+    """Device buffers (R rotating K/V sets) and raw C-ABI arguments of one decode workload."""
+
+    def __init__(self, w, sets, torch, G, synth, exact_first=True):
+        self.w = w
+        dev = torch.device("cuda")
+        bf = torch.bfloat16
+        B, Hq, Hkv, S, d = w.batch, w.num_q_heads, w.num_kv_heads, w.max_seq, w.head_dim
+        lens = synth.lengths_of(w)
+        gen = torch.Generator(device=dev)
+        gen.manual_seed(1000 + w.seed)
+        self.q, self.k, self.v = [], [], []
+        if exact_first:
+            inp = synth.make_decode(w)
+            to = lambda x: torch.from_numpy(x).to(dev).to(bf)
+            self.q.append(to(inp["q"]))
+            self.k.append(to(inp["k"]))
+            self.v.append(to(inp["v"]))
+            self.qw, self.kw = (to(inp["q_norm_w"]), to(inp["k_norm_w"])) if w.qk_norm else (None, None)
+        else:
+            self.qw = (1 + 0.1 * torch.randn(d, generator=gen, device=dev)).to(bf) if w.qk_norm else None
+            self.kw = (1 + 0.1 * torch.randn(d, generator=gen, device=dev)).to(bf) if w.qk_norm else None
+        while len(self.k) < sets:
+            self.q.append(torch.randn(B, Hq, d, generator=gen, device=dev).to(bf))
+            self.k.append(torch.randn(B, Hkv, S, d, generator=gen, device=dev).to(bf))
+            self.v.append(torch.randn(B, Hkv, S, d, generator=gen, device=dev).to(bf))
+        self.lens = lens
+        self.sl = torch.from_numpy(lens).to(dev)
+        self.pos = torch.from_numpy((lens - 1).astype("int32")).to(dev)
+        self.out = torch.empty(B, Hq, d, dtype=torch.float32, device=dev)
+        self.desc = G.decode_desc(self.q[0], self.k[0], self.v[0], self.out, w.split_tokens, w.eps, 0.0)
+        st, self.T, self.n = G.gqa_attn_decode_plan(self.desc)
+        assert st == G.GQA_OK
+        self.ws = G.decode_workspace(self.desc, dev)
+        self.ws_bytes = 0 if self.ws is None else self.ws.numel()
+        self.bytes = decode_bytes(lens, Hkv, Hq, B)
+        self.G = G
+
+    def args(self, i):
+        j = i % len(self.k)
+        p = lambda t: None if t is None else t.data_ptr()
+        return (self.desc, p(self.q[j]), p(self.k[j]), p(self.v[j]), p(self.sl), p(self.pos), p(self.qw),
+                p(self.kw), self.w.rope_theta, p(self.out), p(self.ws), self.ws_bytes)
+
+    def call(self, i, stream):
+        st = self.G.gqa_attn_decode(*self.args(i), stream)
+        assert st == self.G.GQA_OK, self.G.gqa_attn_status_string(st)
+
+    def partition(self, i, stream):
+        st = self.G.gqa_attn_decode_partition(*self.args(i), stream)
+        assert st == self.G.GQA_OK
+
+    def merge(self, i, stream):
+        a = self.args(i)
+        st = self.G.gqa_attn_decode_merge(a[0], a[4], a[9], a[10], a[11], stream)
+        assert st == self.G.GQA_OK
+
+
+def graph_time_ms(torch, fn, steps, warmup):
+    """Capture `steps` calls of fn(i, stream) in a HIP graph, replay it after a
+    warmup graph, and return the elapsed GPU time of the timed replay (ms)."""
+    s = torch.cuda.Stream()
+    torch.cuda.synchronize()
+    with torch.cuda.stream(s):
+        for i in range(2):                         # eager warm-up before capture
+            fn(i, s.cuda_stream)
+    torch.cuda.synchronize()
+    gw, gt = torch.cuda.CUDAGraph(), torch.cuda.CUDAGraph()
+    with torch.cuda.graph(gw, stream=s):
+        for i in range(max(warmup, 1)):
+            fn(i, s.cuda_stream)
+    with torch.cuda.graph(gt, stream=s):
+        for i in range(steps):
+            fn(i, s.cuda_stream)
+    torch.cuda.synchronize()
+    gw.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    with torch.cuda.stream(s):
+        e0.record(s)
+        gt.replay()
+        e1.record(s)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1)
+
+
+def event_kernel_times(torch, parts, steps):
+    """Average GPU durations (us) of each callable in `parts` (each fn(i, stream)),
+    bracketed by HIP events on the launch stream.  A spin kernel queued first
+    keeps the GPU behind the host so the events bracket only kernel time."""
+    s = torch.cuda.Stream()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(parts) + 1)] for _ in range(steps)]
+    torch.cuda.synchronize()
+    with torch.cuda.stream(s):
+        torch.cuda._sleep(int(2.4e9 * 0.05))     # ~50 ms of spinning while the host enqueues
+        for i in range(steps):
+            evs[i][0].record(s)
+            for j, fn in enumerate(parts):
+                fn(i, s.cuda_stream)
+                evs[i][j + 1].record(s)
+    torch.cuda.synchronize()
+    return [1000.0 * sum(evs[i][j].elapsed_time(evs[i][j + 1]) for i in range(steps)) / steps
+            for j in range(len(parts))]
+
+
+def cpu_baseline(case_inputs, bytes_per_call, budget_s=12.0):
+    """The oracle as it stands, on the host cores, over the same decode workload."""
+    import numpy as np
+    from threadpoolctl import threadpool_info, threadpool_limits
+    import oracle as O
+    cores = len(os.sched_getaffinity(0))
+    inp = case_inputs
+    with threadpool_limits(cores):
+        info = threadpool_info()
+        threads = max([x.get("num_threads", 1) for x in info] or [1])
+        t0 = time.perf_counter()
+        reps = 0
+        while True:
+            O.decode_ref(inp["q"], inp["k"], inp["v"], inp["seq_lens"], inp["positions"], inp["q_norm_w"],
+                         inp["k_norm_w"], inp["rope_theta"], inp["eps"])
+            reps += 1
+            el = time.perf_counter() - t0
+            if el >= budget_s or reps >= 1000:
+                break
+    per = el / reps
+    return {"value": bytes_per_call / per / 1e9, "unit": "GB/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{reps} full oracle decode calls of the headline workload ({el:.1f} s, "
+                      f"{per * 1e3:.1f} ms each, host cores available {cores})"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--no-extra", action="store_true", help="skip the prefill and long-context decode fields")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE {world}): this build has "
+              "no multi-GPU path; the sharding design is described in DESIGN.md.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    import gqa_attention_attn_amd as G
+    import synth
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    G.lib()
+    K, W = args.steps, args.warmup
+
+    # ---------------- headline: Qwen3-14B decode, B = 1, S = 4096
+    w = synth.QWEN3_DECODE
+    per_set = decode_bytes(synth.lengths_of(w), w.num_kv_heads, w.num_q_heads, w.batch)
+    sets = max(1, math.ceil(LLC_BYTES / per_set))
+    log(f"[bench] {w.name}: {per_set} B per call, rotating {sets} K/V sets")
+    case = DecodeCase(w, sets, torch, G, synth)
+    t_ms = graph_time_ms(torch, case.call, K, W)
+    us_step = 1000.0 * t_ms / K
+    gbs = case.bytes / (us_step * 1e-6) / 1e9
+    log(f"[bench] decode step {us_step:.2f} us  -> {gbs:.1f} GB/s (split T={case.T}, n={case.n})")
+    t_part, t_merge = event_kernel_times(torch, [case.partition, case.merge], K)
+    log(f"[bench] event durations: partition {t_part:.2f} us, merge {t_merge:.2f} us")
+    ach = case.bytes / (t_part * 1e-6) / 1e9
+    result = {
+        "metric": METRIC, "value": round(gbs, 2), "unit": "GB/s", "n_gpus": 1, "steps": K, "warmup": W,
+        "ms_per_step": round(us_step / 1000.0, 6), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": w.name, "batch": w.batch, "num_q_heads": w.num_q_heads,
+                   "num_kv_heads": w.num_kv_heads, "head_dim": w.head_dim, "seq_len": w.max_seq,
+                   "kv_split_tokens": case.T, "num_splits": case.n, "qk_norm": w.qk_norm,
+                   "rope_theta": w.rope_theta, "kv_sets_rotated": sets, "hip_graph": True},
+        "us_per_step": round(us_step, 3),
+        "kernel_us": {"decode_partition": round(t_part, 3), "decode_merge": round(t_merge, 3)},
+        "roofline": {"bound": "hbm", "kernel": "decode_partition", "achieved": round(ach, 1),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBS, 4),
+                     "traffic": None, "algorithmic_bytes": case.bytes},
+    }
+    cb_inputs = synth.make_decode(w) if not args.no_cpu_baseline else None
+    del case
+    torch.cuda.empty_cache()
+
+    # ---------------- extras: causal prefill and the other decode shapes
+    if not args.no_extra:
+        extra = {}
+        pw = synth.QWEN3_PREFILL
+        pin = synth.make_prefill(pw)
+        bf = torch.bfloat16
+        to = lambda x: None if x is None else torch.from_numpy(np.ascontiguousarray(x)).cuda().to(bf)
+        pq, pk, pv = to(pin["q"]), to(pin["k"]), to(pin["v"])
+        pqw, pkw = to(pin["q_norm_w"]), to(pin["k_norm_w"])
+        psl = torch.from_numpy(pin["seq_lens"]).cuda()
+        ppos = torch.from_numpy(pin["positions"]).cuda()
+        pout = torch.empty(pq.shape, dtype=torch.float32, device="cuda")
+        pdesc = G.prefill_desc(pq, pk, pv, pout, True, pw.eps)
+
+        def pcall(i, stream):
+            st = G.gqa_attn_prefill(pdesc, pq.data_ptr(), pk.data_ptr(), pv.data_ptr(), psl.data_ptr(),
+                                    ppos.data_ptr(), pqw.data_ptr(), pkw.data_ptr(), pw.rope_theta,
+                                    pout.data_ptr(), stream)
+            assert st == G.GQA_OK
+        pk_steps = max(5, K // 10)
+        pt = graph_time_ms(torch, pcall, pk_steps, max(2, W // 10))
+        us_p = 1000.0 * pt / pk_steps
+        (ev_p,) = event_kernel_times(torch, [pcall], pk_steps)
+        flops = prefill_flops(pin["seq_lens"], pw.num_q_heads)
+        tf = flops / (us_p * 1e-6) / 1e12
+        tf_k = flops / (ev_p * 1e-6) / 1e12
+        extra["prefill"] = {"workload": pw.name, "us_per_call": round(us_p, 2), "tflops": round(tf, 2),
+                            "kernel_us": round(ev_p, 2),
+                            "roofline": {"bound": "mfma", "kernel": "prefill", "achieved": round(tf_k, 2),
+                                         "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                                         "frac": round(tf_k / BF16_PEAK_TFLOPS, 4), "traffic": None,
+                                         "algorithmic_flops": flops}}
+        log(f"[bench] prefill {us_p:.1f} us -> {tf:.1f} TFLOP/s (kernel {ev_p:.1f} us)")
+        del pq, pk, pv, pout
+        torch.cuda.empty_cache()
+
+        for dw in (synth.LLAMA70B_LONG, synth.QWEN3_RAGGED):
+            nb = decode_bytes(synth.lengths_of(dw), dw.num_kv_heads, dw.num_q_heads, dw.batch)
+            dsets = max(1, math.ceil(LLC_BYTES / nb))
+            c = DecodeCase(dw, dsets, torch, G, synth, exact_first=False)
+            steps = max(5, K // 10)
+            t = graph_time_ms(torch, c.call, steps, 2)
+            us = 1000.0 * t / steps
+            tp, tm = event_kernel_times(torch, [c.partition, c.merge], steps)
+            extra[dw.name] = {"us_per_step": round(us, 2), "gbs": round(c.bytes / (us * 1e-6) / 1e9, 1),
+                              "kernel_us": {"decode_partition": round(tp, 2), "decode_merge": round(tm, 2)},
+                              "partition_frac_of_hbm_peak": round(c.bytes / (tp * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                              "kv_split_tokens": c.T, "num_splits": c.n, "kv_sets_rotated": dsets,
+                              "algorithmic_bytes": c.bytes}
+            log(f"[bench] {dw.name}: {us:.1f} us/step, {c.bytes / (us * 1e-6) / 1e9:.0f} GB/s "
+                f"(partition {tp:.1f} us, merge {tm:.1f} us)")
+            del c
+            torch.cuda.empty_cache()
+        result["extra"] = extra
+
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(cb_inputs, result["roofline"]["algorithmic_bytes"])
+        log(f"[bench] cpu baseline {result['cpu_baseline']}")
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

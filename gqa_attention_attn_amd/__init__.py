@@ -36,6 +36,8 @@ EXPORTS = (
     "gqa_attn_decode_plan",
     "gqa_attn_decode_workspace_size",
     "gqa_attn_decode",
+    "gqa_attn_decode_partition",
+    "gqa_attn_decode_merge",
     "gqa_attn_prefill",
 )
 
@@ -95,6 +97,10 @@ def lib() -> ctypes.CDLL:
         L.gqa_attn_decode.argtypes = [ctypes.POINTER(GqaDecodeDesc), vp, vp, vp, vp, vp, vp, vp, ctypes.c_float, vp,
                                       vp, ctypes.c_size_t, vp]
         L.gqa_attn_decode.restype = ctypes.c_int
+        L.gqa_attn_decode_partition.argtypes = L.gqa_attn_decode.argtypes
+        L.gqa_attn_decode_partition.restype = ctypes.c_int
+        L.gqa_attn_decode_merge.argtypes = [ctypes.POINTER(GqaDecodeDesc), vp, vp, vp, ctypes.c_size_t, vp]
+        L.gqa_attn_decode_merge.restype = ctypes.c_int
         L.gqa_attn_prefill.argtypes = [ctypes.POINTER(GqaPrefillDesc), vp, vp, vp, vp, vp, vp, vp, ctypes.c_float,
                                        vp, vp]
         L.gqa_attn_prefill.restype = ctypes.c_int
@@ -132,6 +138,18 @@ def gqa_attn_decode(desc, q, k_cache, v_cache, seq_lens, positions, q_norm_w, k_
     return int(lib().gqa_attn_decode(ctypes.byref(desc) if desc is not None else None, q, k_cache, v_cache, seq_lens,
                                      positions, q_norm_w, k_norm_w, float(rope_theta), out, workspace,
                                      int(workspace_bytes), stream))
+
+
+def gqa_attn_decode_partition(desc, q, k_cache, v_cache, seq_lens, positions, q_norm_w, k_norm_w, rope_theta,
+                              out, workspace, workspace_bytes, stream) -> int:
+    return int(lib().gqa_attn_decode_partition(ctypes.byref(desc) if desc is not None else None, q, k_cache,
+                                               v_cache, seq_lens, positions, q_norm_w, k_norm_w, float(rope_theta),
+                                               out, workspace, int(workspace_bytes), stream))
+
+
+def gqa_attn_decode_merge(desc, seq_lens, out, workspace, workspace_bytes, stream) -> int:
+    return int(lib().gqa_attn_decode_merge(ctypes.byref(desc) if desc is not None else None, seq_lens, out,
+                                           workspace, int(workspace_bytes), stream))
 
 
 def gqa_attn_prefill(desc, q, k, v, seq_lens, positions, q_norm_w, k_norm_w, rope_theta, out, stream) -> int:

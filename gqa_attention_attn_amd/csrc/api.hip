@@ -130,14 +130,21 @@ gqa_status gqa_attn_decode_workspace_size(const gqa_decode_desc* desc, size_t* b
   return GQA_OK;
 }
 
-gqa_status gqa_attn_decode(const gqa_decode_desc* d, const void* q, const void* k_cache, const void* v_cache,
-                           const int32_t* seq_lens, const int32_t* positions, const void* q_norm_w,
-                           const void* k_norm_w, float rope_theta, void* out, void* workspace,
-                           size_t workspace_bytes, hipStream_t stream) {
-  gqa_status st = check_decode_desc(d);
+}  // extern "C"
+
+namespace {
+
+// Validation shared by the decode entry points; fills the kernel parameters.
+// need_inputs: q / caches / positions are used (partition); the merge needs
+// only seq_lens, out and the workspace.
+gqa_status prepare_decode(const gqa_decode_desc* d, const void* q, const void* k_cache, const void* v_cache,
+                          const int32_t* seq_lens, const int32_t* positions, const void* q_norm_w,
+                          const void* k_norm_w, float rope_theta, void* out, void* workspace,
+                          size_t workspace_bytes, bool need_inputs, gqa::DecodeParams* p) {
+  const gqa_status st = check_decode_desc(d);
   if (st != GQA_OK) return st;
-  if (q == nullptr || k_cache == nullptr || v_cache == nullptr || seq_lens == nullptr || positions == nullptr ||
-      out == nullptr)
+  if (seq_lens == nullptr || out == nullptr) return GQA_ERR_NULL;
+  if (need_inputs && (q == nullptr || k_cache == nullptr || v_cache == nullptr || positions == nullptr))
     return GQA_ERR_NULL;
   if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(out) || !aligned16(q_norm_w) ||
       !aligned16(k_norm_w) || ((uintptr_t)seq_lens & 3u) || ((uintptr_t)positions & 3u))
@@ -149,41 +156,77 @@ gqa_status gqa_attn_decode(const gqa_decode_desc* d, const void* q, const void* 
     if (workspace == nullptr || workspace_bytes < need) return GQA_ERR_WORKSPACE;
     if (((uintptr_t)workspace & 255u) != 0) return GQA_ERR_ALIGN;
   }
+  *p = gqa::DecodeParams{};
+  p->q = q;
+  p->k = k_cache;
+  p->v = v_cache;
+  p->seq_lens = seq_lens;
+  p->positions = positions;
+  p->q_norm_w = q_norm_w;
+  p->k_norm_w = k_norm_w;
+  p->out = out;
+  p->ws_o = need > 0 ? (float*)workspace : nullptr;
+  p->ws_ml = need > 0 ? (float*)((char*)workspace + (size_t)d->batch * d->num_q_heads * n * GQA_ATTN_HEAD_DIM *
+                                                        sizeof(float))
+                      : nullptr;
+  p->q_sb = d->q_stride_b;
+  p->q_sh = d->q_stride_h;
+  p->k_sb = d->k_stride_b;
+  p->k_sh = d->k_stride_h;
+  p->k_ss = d->k_stride_s;
+  p->v_sb = d->v_stride_b;
+  p->v_sh = d->v_stride_h;
+  p->v_ss = d->v_stride_s;
+  p->o_sb = d->out_stride_b;
+  p->o_sh = d->out_stride_h;
+  p->batch = d->batch;
+  p->num_q_heads = d->num_q_heads;
+  p->num_kv_heads = d->num_kv_heads;
+  p->group = d->num_q_heads / d->num_kv_heads;
+  p->max_seq = d->max_seq;
+  p->split = T;
+  p->n_split = n;
+  p->out_bf16 = d->out_dtype == GQA_BF16;
+  p->eps = d->eps;
+  p->scale_log2 = resolve_scale_log2(d->scale);
+  p->rope_theta = rope_theta > 0.f ? (double)rope_theta : 0.0;
+  return GQA_OK;
+}
 
-  gqa::DecodeParams p{};
-  p.q = q;
-  p.k = k_cache;
-  p.v = v_cache;
-  p.seq_lens = seq_lens;
-  p.positions = positions;
-  p.q_norm_w = q_norm_w;
-  p.k_norm_w = k_norm_w;
-  p.out = out;
-  p.ws_o = need > 0 ? (float*)workspace : nullptr;
-  p.ws_ml = need > 0 ? (float*)((char*)workspace + (size_t)d->batch * d->num_q_heads * n * GQA_ATTN_HEAD_DIM * sizeof(float))
-                     : nullptr;
-  p.q_sb = d->q_stride_b;
-  p.q_sh = d->q_stride_h;
-  p.k_sb = d->k_stride_b;
-  p.k_sh = d->k_stride_h;
-  p.k_ss = d->k_stride_s;
-  p.v_sb = d->v_stride_b;
-  p.v_sh = d->v_stride_h;
-  p.v_ss = d->v_stride_s;
-  p.o_sb = d->out_stride_b;
-  p.o_sh = d->out_stride_h;
-  p.batch = d->batch;
-  p.num_q_heads = d->num_q_heads;
-  p.num_kv_heads = d->num_kv_heads;
-  p.group = d->num_q_heads / d->num_kv_heads;
-  p.max_seq = d->max_seq;
-  p.split = T;
-  p.n_split = n;
-  p.out_bf16 = d->out_dtype == GQA_BF16;
-  p.eps = d->eps;
-  p.scale_log2 = resolve_scale_log2(d->scale);
-  p.rope_theta = rope_theta > 0.f ? (double)rope_theta : 0.0;
-  return gqa::launch_decode(p, d->in_dtype == GQA_BF16, stream) == hipSuccess ? GQA_OK : GQA_ERR_HIP;
+}  // namespace
+
+extern "C" {
+
+gqa_status gqa_attn_decode_partition(const gqa_decode_desc* d, const void* q, const void* k_cache,
+                                     const void* v_cache, const int32_t* seq_lens, const int32_t* positions,
+                                     const void* q_norm_w, const void* k_norm_w, float rope_theta, void* out,
+                                     void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  gqa::DecodeParams p;
+  const gqa_status st = prepare_decode(d, q, k_cache, v_cache, seq_lens, positions, q_norm_w, k_norm_w, rope_theta,
+                                       out, workspace, workspace_bytes, true, &p);
+  if (st != GQA_OK) return st;
+  return gqa::launch_decode_partition(p, d->in_dtype == GQA_BF16, stream) == hipSuccess ? GQA_OK : GQA_ERR_HIP;
+}
+
+gqa_status gqa_attn_decode_merge(const gqa_decode_desc* d, const int32_t* seq_lens, void* out, void* workspace,
+                                 size_t workspace_bytes, hipStream_t stream) {
+  gqa::DecodeParams p;
+  const gqa_status st = prepare_decode(d, nullptr, nullptr, nullptr, seq_lens, nullptr, nullptr, nullptr, 0.f, out,
+                                       workspace, workspace_bytes, false, &p);
+  if (st != GQA_OK) return st;
+  return gqa::launch_decode_merge(p, stream) == hipSuccess ? GQA_OK : GQA_ERR_HIP;
+}
+
+gqa_status gqa_attn_decode(const gqa_decode_desc* d, const void* q, const void* k_cache, const void* v_cache,
+                           const int32_t* seq_lens, const int32_t* positions, const void* q_norm_w,
+                           const void* k_norm_w, float rope_theta, void* out, void* workspace,
+                           size_t workspace_bytes, hipStream_t stream) {
+  gqa::DecodeParams p;
+  const gqa_status st = prepare_decode(d, q, k_cache, v_cache, seq_lens, positions, q_norm_w, k_norm_w, rope_theta,
+                                       out, workspace, workspace_bytes, true, &p);
+  if (st != GQA_OK) return st;
+  if (gqa::launch_decode_partition(p, d->in_dtype == GQA_BF16, stream) != hipSuccess) return GQA_ERR_HIP;
+  return gqa::launch_decode_merge(p, stream) == hipSuccess ? GQA_OK : GQA_ERR_HIP;
 }
 
 gqa_status gqa_attn_prefill(const gqa_prefill_desc* d, const void* q, const void* k, const void* v,

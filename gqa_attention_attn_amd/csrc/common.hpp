@@ -58,7 +58,8 @@ struct PrefillParams {
 };
 
 // Launchers (return the hipGetLastError() of their launches).
-hipError_t launch_decode(const DecodeParams& p, bool in_bf16, hipStream_t stream);
+hipError_t launch_decode_partition(const DecodeParams& p, bool in_bf16, hipStream_t stream);
+hipError_t launch_decode_merge(const DecodeParams& p, hipStream_t stream);
 hipError_t launch_prefill(const PrefillParams& p, hipStream_t stream);
 
 // Prefill tiling, shared by the launcher and the host planning code.

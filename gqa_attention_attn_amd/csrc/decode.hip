@@ -532,15 +532,18 @@ __global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(const Decod
 
 }  // namespace
 
-hipError_t launch_decode(const DecodeParams& p, bool in_bf16, hipStream_t stream) {
+hipError_t launch_decode_partition(const DecodeParams& p, bool in_bf16, hipStream_t stream) {
   const dim3 grid(p.n_split, p.num_kv_heads, p.batch);
   if (in_bf16) {
     hipLaunchKernelGGL(decode_partition_kernel<true>, grid, dim3(kThreads), 0, stream, p);
   } else {
     hipLaunchKernelGGL(decode_partition_kernel<false>, grid, dim3(kThreads), 0, stream, p);
   }
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess || p.n_split == 1) return e;
+  return hipGetLastError();
+}
+
+hipError_t launch_decode_merge(const DecodeParams& p, hipStream_t stream) {
+  if (p.n_split == 1) return hipSuccess;
   hipLaunchKernelGGL(decode_merge_kernel, dim3(p.num_q_heads, p.batch), dim3(kMergeThreads), 0, stream, p);
   return hipGetLastError();
 }

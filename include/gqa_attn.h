@@ -163,6 +163,34 @@ gqa_status gqa_attn_decode(const gqa_decode_desc* desc, const void* q, const voi
                            void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * The two steps of gqa_attn_decode as separate calls (same descriptor, same
+ * plan, same workspace).  gqa_attn_decode(...) is exactly
+ * gqa_attn_decode_partition(...) followed by gqa_attn_decode_merge(...) on
+ * the same stream.
+ *
+ * gqa_attn_decode_partition: the split-KV partition step (ADR-0060 sections
+ * 3 and 5.2 with the fused prologue).  Each (b, KV head, chunk) writes one
+ * unnormalised partial (m, l, O) per query head of its group to `workspace`
+ * (m in log2 units: scores are scaled by log2(e)).  When the plan has a
+ * single chunk it writes the normalised result to `out` instead and needs no
+ * workspace.
+ *
+ * gqa_attn_decode_merge: the log-sum-exp merge step (ADR-0060 section 4):
+ * out[b, h, :] = sum_c 2^(m_c - M) O_c / sum_c 2^(m_c - M) l_c over the
+ * ceil(L / T) chunks that hold keys; L = 0 writes zeros.  Reads only
+ * `workspace` and seq_lens; a no-op returning GQA_OK when the plan has a
+ * single chunk.
+ * Errors: as gqa_attn_decode.
+ */
+gqa_status gqa_attn_decode_partition(const gqa_decode_desc* desc, const void* q, const void* k_cache,
+                                     const void* v_cache, const int32_t* seq_lens, const int32_t* positions,
+                                     const void* q_norm_w, const void* k_norm_w, float rope_theta, void* out,
+                                     void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+gqa_status gqa_attn_decode_merge(const gqa_decode_desc* desc, const int32_t* seq_lens, void* out, void* workspace,
+                                 size_t workspace_bytes, hipStream_t stream);
+
+/*
  * Grouped-query causal prefill attention with the fused QK-norm + RoPE
  * prologue (ADR-0060 sections 3 and 5.4; "Qwen3-14B Optimization" 2.1).
  *

@@ -5,7 +5,7 @@ none of the attention method's arithmetic: it only draws random tensors, rounds
 them to the storage dtype and poisons unused cache rows.
 
 Recipe (one numpy ``Generator(PCG64(seed))`` per workload):
-  draw order q, k, v, gamma_q, gamma_k, lengths;
+  draw order lengths (ragged workloads only), q, k, v, gamma_q, gamma_k;
   q, k, v ~ N(0, 1) drawn in float32; gamma ~ N(1, 0.1);
   bf16 workloads round every float tensor to bf16 (round to nearest even);
   ragged lengths are integers uniform on [lo, hi] inclusive;
@@ -88,21 +88,31 @@ def _store(x: np.ndarray, dtype: str) -> np.ndarray:
     return bf16_round(x) if dtype == "bf16" else np.ascontiguousarray(x, dtype=np.float32)
 
 
+def _lengths(rng, B: int, S: int, lengths) -> np.ndarray:
+    if lengths is None:
+        return np.full(B, S, dtype=np.int32)
+    lo, hi = lengths
+    return rng.integers(lo, hi, size=B, endpoint=True).astype(np.int32)
+
+
+def lengths_of(w) -> np.ndarray:
+    """The per-sequence lengths of a workload without drawing its tensors."""
+    rng = np.random.Generator(np.random.PCG64(w.seed))
+    S = w.max_seq if isinstance(w, DecodeWorkload) else w.seq
+    return _lengths(rng, w.batch, S, w.lengths)
+
+
 def make_decode(w: DecodeWorkload, poison: bool = True) -> dict:
     """Inputs of one decode workload as float32 numpy arrays (bf16-exact when
     w.dtype == 'bf16').  Caches are head-major [B, Hkv, max_seq, d]."""
     rng = np.random.Generator(np.random.PCG64(w.seed))
     B, Hq, Hkv, S, d = w.batch, w.num_q_heads, w.num_kv_heads, w.max_seq, w.head_dim
+    lens = _lengths(rng, B, S, w.lengths)
     q = _store(rng.standard_normal((B, Hq, d), dtype=np.float32), w.dtype)
     k = _store(rng.standard_normal((B, Hkv, S, d), dtype=np.float32), w.dtype)
     v = _store(rng.standard_normal((B, Hkv, S, d), dtype=np.float32), w.dtype)
     gq = _store(1.0 + 0.1 * rng.standard_normal(d, dtype=np.float32), w.dtype)
     gk = _store(1.0 + 0.1 * rng.standard_normal(d, dtype=np.float32), w.dtype)
-    if w.lengths is None:
-        lens = np.full(B, S, dtype=np.int32)
-    else:
-        lo, hi = w.lengths
-        lens = rng.integers(lo, hi, size=B, endpoint=True).astype(np.int32)
     pos = (lens - 1).astype(np.int32)
     if poison:
         for b in range(B):
@@ -116,16 +126,12 @@ def make_prefill(w: PrefillWorkload, poison: bool = True) -> dict:
     """Inputs of one prefill workload: q [B, Hq, S, d], k/v [B, Hkv, S, d]."""
     rng = np.random.Generator(np.random.PCG64(w.seed))
     B, Hq, Hkv, S, d = w.batch, w.num_q_heads, w.num_kv_heads, w.seq, w.head_dim
+    lens = _lengths(rng, B, S, w.lengths)
     q = _store(rng.standard_normal((B, Hq, S, d), dtype=np.float32), w.dtype)
     k = _store(rng.standard_normal((B, Hkv, S, d), dtype=np.float32), w.dtype)
     v = _store(rng.standard_normal((B, Hkv, S, d), dtype=np.float32), w.dtype)
     gq = _store(1.0 + 0.1 * rng.standard_normal(d, dtype=np.float32), w.dtype)
     gk = _store(1.0 + 0.1 * rng.standard_normal(d, dtype=np.float32), w.dtype)
-    if w.lengths is None:
-        lens = np.full(B, S, dtype=np.int32)
-    else:
-        lo, hi = w.lengths
-        lens = rng.integers(lo, hi, size=B, endpoint=True).astype(np.int32)
     pos = np.full(B, w.position0, dtype=np.int32)
     if poison:
         for b in range(B):
