@@ -35,6 +35,10 @@ gqa_status check_decode_desc(const gqa_decode_desc* d) {
   if (d->q_stride_b < 0 || d->q_stride_h < 0 || d->k_stride_b < 0 || d->k_stride_h < 0 || d->k_stride_s < 0 ||
       d->v_stride_b < 0 || d->v_stride_h < 0 || d->v_stride_s < 0 || d->out_stride_b < 0 || d->out_stride_h < 0)
     return GQA_ERR_SHAPE;
+  // decode addresses one (b, KV head) cache slab with 32-bit byte offsets
+  if ((int64_t)d->max_seq * d->k_stride_s * ei + 512 > ((int64_t)1 << 32) ||
+      (int64_t)d->max_seq * d->v_stride_s * ei + 512 > ((int64_t)1 << 32))
+    return GQA_ERR_UNSUPPORTED;
   if (!stride_ok(d->q_stride_b, ei) || !stride_ok(d->q_stride_h, ei) || !stride_ok(d->k_stride_b, ei) ||
       !stride_ok(d->k_stride_h, ei) || !stride_ok(d->k_stride_s, ei) || !stride_ok(d->v_stride_b, ei) ||
       !stride_ok(d->v_stride_h, ei) || !stride_ok(d->v_stride_s, ei) || !stride_ok(d->out_stride_b, eo) ||
@@ -73,7 +77,8 @@ size_t decode_ws_bytes(const gqa_decode_desc* d, int32_t n) {
 gqa_status check_prefill_desc(const gqa_prefill_desc* d) {
   if (d == nullptr) return GQA_ERR_NULL;
   if (d->batch < 1 || d->num_q_heads < 1 || d->num_kv_heads < 1 || d->max_seq < 1) return GQA_ERR_SHAPE;
-  if (d->batch > kGridYZMax || d->num_q_heads > kGridYZMax) return GQA_ERR_SHAPE;
+  if ((int64_t)d->batch * d->num_q_heads * ((d->max_seq + gqa::kPrefillBM - 1) / gqa::kPrefillBM) > INT32_MAX)
+    return GQA_ERR_SHAPE;
   if (d->num_q_heads % d->num_kv_heads != 0) return GQA_ERR_SHAPE;
   if (d->head_dim != GQA_ATTN_HEAD_DIM) return GQA_ERR_UNSUPPORTED;
   if (d->in_dtype != GQA_BF16 || !dtype_ok(d->out_dtype)) return GQA_ERR_UNSUPPORTED;

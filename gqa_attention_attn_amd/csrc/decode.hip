@@ -23,7 +23,10 @@
 //    query head (lane % 16), so the row max needs only two cross-lane steps,
 //    and V rows are read with 16 lanes covering one full 256-byte row; the
 //    8x8 bf16 transpose that V^T needs is done in registers.
-//  * K and V are streamed straight from HBM into registers, one step ahead.
+//  * K and V are streamed straight from HBM into registers: the first step is
+//    requested before the query prologue runs, and each step buffer is
+//    refilled with the wave's next step as soon as its K (then V) half has
+//    been consumed.
 #include "common.hpp"
 
 namespace gqa {
@@ -106,91 +109,108 @@ struct StepF32 {
 
 // key offset (within a 32-key step) of the t-th V row a bf16 lane loads; the
 // same permutation orders the P^T operand: t < 4 -> 4*q4 + t, else 16 + 4*q4 + t - 4
-__device__ __forceinline__ int vkey_bf16(int q4, int t) { return (t < 4) ? 4 * q4 + t : 12 + 4 * q4 + t; }
+__device__ __forceinline__ constexpr int vkey_t(int t) { return t < 4 ? t : 12 + t; }
 
-__device__ __forceinline__ void load_step(StepBF16& st, const uint8_t* kb, const uint8_t* vb, int64_t kss,
-                                          int64_t vss, int key0, int kend, bool full, int n16, int q4) {
-  #pragma unroll
+// Addressing of one (b, KV head) slab: a uniform 64-bit base plus 32-bit byte
+// offsets (the host guarantees the slab spans less than 4 GiB).  The per-lane
+// parts of the offsets are fixed for the whole sweep.
+struct Slab {
+  const uint8_t* kb;
+  const uint8_t* vb;
+  uint32_t kss, vss;     // row strides in bytes
+  uint32_t klane, vlane; // per-lane byte offsets
+};
+
+// Loads of one step.  FULL: every row of the step is below kend, no
+// predication.  !FULL (the last step of a chunk): rows at or past kend are
+// replaced by row kend-1 (always valid) and the loaded values are zeroed, so
+// rows past the sequence are never read and the code stays branch-free.
+template <bool FULL>
+__device__ __forceinline__ void load_k(StepBF16& st, const Slab& sl, int key0, int kend, int n16, int q4) {
+#pragma unroll
   for (int gi = 0; gi < 2; ++gi) {
     const int key = key0 + 16 * gi + n16;
-    const u32x4* src = (const u32x4*)(kb + (int64_t)key * kss + 64 * q4);
-    if (full || key < kend) {
-      #pragma unroll
-      for (int j = 0; j < 4; ++j) st.k[gi][j] = src[j];
-    } else {
-      #pragma unroll
-      for (int j = 0; j < 4; ++j) st.k[gi][j] = u32x4{0, 0, 0, 0};
+    const bool ok = FULL || key < kend;
+    const uint32_t off = FULL ? (uint32_t)(key0 + 16 * gi) * sl.kss + sl.klane
+                              : (uint32_t)(ok ? key : kend - 1) * sl.kss + 64u * q4;
+    const u32x4* src = (const u32x4*)(sl.kb + off);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const u32x4 x = src[j];
+      st.k[gi][j] = ok ? x : u32x4{0, 0, 0, 0};
     }
-  }
-  #pragma unroll
-  for (int t = 0; t < 8; ++t) {
-    const int key = key0 + vkey_bf16(q4, t);
-    const u32x4* src = (const u32x4*)(vb + (int64_t)key * vss + 16 * n16);
-    st.v[t] = (full || key < kend) ? *src : u32x4{0, 0, 0, 0};
   }
 }
 
-__device__ __forceinline__ void load_step(StepF32& st, const uint8_t* kb, const uint8_t* vb, int64_t kss,
-                                          int64_t vss, int key0, int kend, bool full, int n16, int q4) {
-  #pragma unroll
+template <bool FULL>
+__device__ __forceinline__ void load_v(StepBF16& st, const Slab& sl, int key0, int kend, int n16, int q4) {
+#pragma unroll
+  for (int t = 0; t < 8; ++t) {
+    const int key = key0 + 4 * q4 + vkey_t(t);
+    const bool ok = FULL || key < kend;
+    const uint32_t off = FULL ? (uint32_t)(key0 + vkey_t(t)) * sl.vss + sl.vlane
+                              : (uint32_t)(ok ? key : kend - 1) * sl.vss + 16u * n16;
+    const u32x4 x = *(const u32x4*)(sl.vb + off);
+    st.v[t] = ok ? x : u32x4{0, 0, 0, 0};
+  }
+}
+
+template <bool FULL>
+__device__ __forceinline__ void load_k(StepF32& st, const Slab& sl, int key0, int kend, int n16, int q4) {
+#pragma unroll
   for (int gi = 0; gi < 2; ++gi) {
     const int key = key0 + 16 * gi + n16;
-    const f32x4* src = (const f32x4*)(kb + (int64_t)key * kss + 128 * q4);
-    if (full || key < kend) {
-      #pragma unroll
-      for (int j = 0; j < 8; ++j) st.k[gi][j] = src[j];
-    } else {
-      #pragma unroll
-      for (int j = 0; j < 8; ++j) st.k[gi][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    const bool ok = FULL || key < kend;
+    const uint32_t off = FULL ? (uint32_t)(key0 + 16 * gi) * sl.kss + sl.klane
+                              : (uint32_t)(ok ? key : kend - 1) * sl.kss + 128u * q4;
+    const f32x4* src = (const f32x4*)(sl.kb + off);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const f32x4 x = src[j];
+      st.k[gi][j] = ok ? x : f32x4{0.f, 0.f, 0.f, 0.f};
     }
   }
-  #pragma unroll
+}
+
+template <bool FULL>
+__device__ __forceinline__ void load_v(StepF32& st, const Slab& sl, int key0, int kend, int n16, int q4) {
+#pragma unroll
   for (int e = 0; e < 8; ++e) {
     const int key = key0 + 16 * (e >> 2) + 4 * q4 + (e & 3);
-    const f32x4* src = (const f32x4*)(vb + (int64_t)key * vss + 32 * n16);
-    if (full || key < kend) {
-      st.v[e][0] = src[0];
-      st.v[e][1] = src[1];
-    } else {
-      st.v[e][0] = f32x4{0.f, 0.f, 0.f, 0.f};
-      st.v[e][1] = f32x4{0.f, 0.f, 0.f, 0.f};
-    }
+    const bool ok = FULL || key < kend;
+    const uint32_t off = FULL ? (uint32_t)(key0 + 16 * (e >> 2) + (e & 3)) * sl.vss + sl.vlane
+                              : (uint32_t)(ok ? key : kend - 1) * sl.vss + 32u * n16;
+    const f32x4* src = (const f32x4*)(sl.vb + off);
+    const f32x4 x0 = src[0], x1 = src[1];
+    st.v[e][0] = ok ? x0 : f32x4{0.f, 0.f, 0.f, 0.f};
+    st.v[e][1] = ok ? x1 : f32x4{0.f, 0.f, 0.f, 0.f};
   }
 }
 
-// Replace the raw new-key row by its prologue output (lanes holding key kn).
-__device__ __forceinline__ void put_new_key(StepBF16& st, const float* knl, int key0, int kn, int n16, int q4) {
-  const int off = kn - key0;
-  if ((off & 15) != n16) return;
-  u32x4 f[4];
-  #pragma unroll
-  for (int kb = 0; kb < 4; ++kb) {
-    const float* s = knl + 32 * q4 + 8 * kb;
-    f[kb] = u32x4{pack_bf16x2(s[0], s[1]), pack_bf16x2(s[2], s[3]), pack_bf16x2(s[4], s[5]), pack_bf16x2(s[6], s[7])};
-  }
-  #pragma unroll
-  for (int gi = 0; gi < 2; ++gi)   // static register indices: no scratch
-    if ((off >> 4) == gi)
-      #pragma unroll
-      for (int kb = 0; kb < 4; ++kb) st.k[gi][kb] = f[kb];
+template <class Step>
+__device__ __forceinline__ void load_k_any(Step& st, const Slab& sl, int key0, int kend, int n16, int q4) {
+  if (key0 + kStep <= kend) load_k<true>(st, sl, key0, kend, n16, q4);
+  else load_k<false>(st, sl, key0, kend, n16, q4);
 }
 
-__device__ __forceinline__ void put_new_key(StepF32& st, const float* knl, int key0, int kn, int n16, int q4) {
-  const int off = kn - key0;
-  if ((off & 15) != n16) return;
-  #pragma unroll
-  for (int gi = 0; gi < 2; ++gi)
-    if ((off >> 4) == gi)
-      #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const float* s = knl + 32 * q4 + 4 * j;
-        st.k[gi][j] = f32x4{s[0], s[1], s[2], s[3]};
-      }
+template <class Step>
+__device__ __forceinline__ void load_v_any(Step& st, const Slab& sl, int key0, int kend, int n16, int q4) {
+  if (key0 + kStep <= kend) load_v<true>(st, sl, key0, kend, n16, q4);
+  else load_v<false>(st, sl, key0, kend, n16, q4);
 }
 
-// ----------------------------------------------------------------- one step of the sweep
+template <class Step>
+__device__ __forceinline__ void load_step(Step& st, const Slab& sl, int key0, int kend, int n16, int q4) {
+  load_k_any(st, sl, key0, kend, n16, q4);
+  load_v_any(st, sl, key0, kend, n16, q4);
+}
 
-struct QFragBF16 { bf16x8 q[4]; };
+// ----------------------------------------------------------------- query operand and running state
+
+// bf16 path: q' = hi + lo with hi = bf16(q'), lo = bf16(q' - hi), so the score
+// keeps ~16 significant bits of q' (two MFMAs per product; decode has the
+// matrix-core headroom).
+struct QFragBF16 { bf16x8 hi[4], lo[4]; };
 struct QFragF32 { float q[32]; };
 
 struct RunState {
@@ -199,70 +219,127 @@ struct RunState {
   float l;         // this lane's share of the running normaliser
 };
 
-// scores: s[4*gi + i] = S[key key0 + 16*gi + 4*q4 + i][g = lane%16] (log2 units)
-__device__ __forceinline__ void scores(const StepBF16& st, const QFragBF16& qf, float scale_log2, float (&s)[8]) {
-  #pragma unroll
+// scores: s[4*gi + i] = S[key key0 + 16*gi + 4*q4 + i][g = lane%16] (log2 units).
+// nk_gi >= 0 (wave-uniform): the step holds the new key (slot L-1) in group
+// nk_gi; the lane whose row it is (nk_lane) uses its prologue output, read
+// from LDS, instead of the raw cached row.
+__device__ __forceinline__ void scores(const StepBF16& st, const QFragBF16& qf, const float* knl, int nk_gi,
+                                       bool nk_lane, int q4, float scale_log2, float (&s)[8]) {
+#pragma unroll
   for (int gi = 0; gi < 2; ++gi) {
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    #pragma unroll
-    for (int kb = 0; kb < 4; ++kb)
-      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(st.k[gi][kb]), qf.q[kb], acc, 0, 0, 0);
-    #pragma unroll
+    if (nk_gi == gi) {
+      // K'_new = hi + lo: hi replaces the raw row, lo adds one more product
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) {
+        const float* x = knl + 32 * q4 + 8 * kb;
+        float hv[8], lv[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          hv[j] = (float)(__bf16)x[j];
+          lv[j] = nk_lane ? x[j] - hv[j] : 0.f;
+        }
+        const u32x4 hi = {pack_bf16x2(hv[0], hv[1]), pack_bf16x2(hv[2], hv[3]), pack_bf16x2(hv[4], hv[5]),
+                          pack_bf16x2(hv[6], hv[7])};
+        const u32x4 lo = {pack_bf16x2(lv[0], lv[1]), pack_bf16x2(lv[2], lv[3]), pack_bf16x2(lv[4], lv[5]),
+                          pack_bf16x2(lv[6], lv[7])};
+        const u32x4 a = nk_lane ? hi : st.k[gi][kb];
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a), qf.hi[kb], acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a), qf.lo[kb], acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(lo), qf.hi[kb], acc, 0, 0, 0);
+      }
+    } else {
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) {
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(st.k[gi][kb]), qf.hi[kb], acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(st.k[gi][kb]), qf.lo[kb], acc, 0, 0, 0);
+      }
+    }
+#pragma unroll
     for (int i = 0; i < 4; ++i) s[4 * gi + i] = acc[i] * scale_log2;
   }
 }
 
-__device__ __forceinline__ void scores(const StepF32& st, const QFragF32& qf, float scale_log2, float (&s)[8]) {
-  #pragma unroll
+__device__ __forceinline__ void scores(const StepF32& st, const QFragF32& qf, const float* knl, int nk_gi,
+                                       bool nk_lane, int q4, float scale_log2, float (&s)[8]) {
+#pragma unroll
   for (int gi = 0; gi < 2; ++gi) {
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    #pragma unroll
-    for (int j = 0; j < 8; ++j)
-      #pragma unroll
-      for (int e = 0; e < 4; ++e)
-        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(st.k[gi][j][e], qf.q[4 * j + e], acc, 0, 0, 0);
-    #pragma unroll
+    const bool sub = nk_gi == gi && nk_lane;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      f32x4 a = st.k[gi][j];
+      if (sub) {
+        const float* x = knl + 32 * q4 + 4 * j;
+        a = f32x4{x[0], x[1], x[2], x[3]};
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[e], qf.q[4 * j + e], acc, 0, 0, 0);
+    }
+#pragma unroll
     for (int i = 0; i < 4; ++i) s[4 * gi + i] = acc[i] * scale_log2;
   }
 }
 
+// O^T += V^T P^T.  bf16 path: P = hi + lo (two MFMAs per tile).
 __device__ __forceinline__ void accumulate_pv(const StepBF16& st, const float (&p)[8], RunState& rs) {
   // P^T operand: slot t of lane group q4 <-> key vkey_bf16(q4, t) = the score
-  // order s[0..7] of this lane.
-  const u32x4 pf = {pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]), pack_bf16x2(p[4], p[5]),
-                    pack_bf16x2(p[6], p[7])};
-  #pragma unroll
+  // order p[0..7] of this lane.
+  float h[8], r[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    h[e] = (float)(__bf16)p[e];
+    r[e] = p[e] - h[e];
+  }
+  const u32x4 phi = {pack_bf16x2(h[0], h[1]), pack_bf16x2(h[2], h[3]), pack_bf16x2(h[4], h[5]), pack_bf16x2(h[6], h[7])};
+  const u32x4 plo = {pack_bf16x2(r[0], r[1]), pack_bf16x2(r[2], r[3]), pack_bf16x2(r[4], r[5]), pack_bf16x2(r[6], r[7])};
+#pragma unroll
   for (int T = 0; T < 8; ++T) {
     const int w = T >> 1;
     u32x4 a;
-    #pragma unroll
+#pragma unroll
     for (int u = 0; u < 4; ++u)
       a[u] = (T & 1) ? pair_hi(st.v[2 * u][w], st.v[2 * u + 1][w]) : pair_lo(st.v[2 * u][w], st.v[2 * u + 1][w]);
-    rs.o[T] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a), as_bf16x8(pf), rs.o[T], 0, 0, 0);
+    rs.o[T] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a), as_bf16x8(phi), rs.o[T], 0, 0, 0);
+    rs.o[T] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a), as_bf16x8(plo), rs.o[T], 0, 0, 0);
   }
 }
 
 __device__ __forceinline__ void accumulate_pv(const StepF32& st, const float (&p)[8], RunState& rs) {
-  #pragma unroll
+#pragma unroll
   for (int e = 0; e < 8; ++e)
-    #pragma unroll
+#pragma unroll
     for (int T = 0; T < 8; ++T)
       rs.o[T] = __builtin_amdgcn_mfma_f32_16x16x4f32(st.v[e][T >> 2][T & 3], p[e], rs.o[T], 0, 0, 0);
 }
 
+// One 32-key step from buffer st; afterwards st is refilled with the step at
+// next_key0 (if next_key0 < kend): its K half right after the QK^T MFMAs
+// have consumed st.k, its V half right after P V has consumed st.v.
 template <class Step, class QFrag>
-__device__ __forceinline__ void sweep_step(const Step& st, const QFrag& qf, RunState& rs, float scale_log2,
-                                           int key0, int kend, bool full, int q4) {
+__device__ __forceinline__ void sweep_step(Step& st, const QFrag& qf, const float* knl, bool has_new, int kn,
+                                           RunState& rs, float scale_log2, int key0, int kend, int next_key0,
+                                           const Slab& sl, int n16, int q4) {
+  const bool full = key0 + kStep <= kend;
+  int nk_gi = -1;
+  bool nk_lane = false;
+  if (has_new && kn >= key0 && kn < key0 + kStep) {   // wave-uniform
+    nk_gi = (kn - key0) >> 4;
+    nk_lane = ((kn - key0) & 15) == n16;
+  }
   float s[8];
-  scores(st, qf, scale_log2, s);
+  scores(st, qf, knl, nk_gi, nk_lane, q4, scale_log2, s);
+  const bool more = next_key0 < kend;
+  if (more) load_k_any(st, sl, next_key0, kend, n16, q4);
   if (!full) {
-    #pragma unroll
+#pragma unroll
     for (int e = 0; e < 8; ++e) {
       const int key = key0 + 16 * (e >> 2) + 4 * q4 + (e & 3);
       if (key >= kend) s[e] = -INFINITY;
     }
   }
   float mx = s[0];
+#pragma unroll
   for (int e = 1; e < 8; ++e) mx = fmaxf(mx, s[e]);
   mx = wave_max_xor(mx, 16);
   mx = wave_max_xor(mx, 32);
@@ -270,16 +347,17 @@ __device__ __forceinline__ void sweep_step(const Step& st, const QFrag& qf, RunS
   const float corr = fast_exp2(rs.m - m_new);   // 0 on the first step (m = -inf)
   float p[8];
   float ps = 0.f;
-  #pragma unroll
+#pragma unroll
   for (int e = 0; e < 8; ++e) {
     p[e] = fast_exp2(s[e] - m_new);
     ps += p[e];
   }
   rs.l = rs.l * corr + ps;
   rs.m = m_new;
-  #pragma unroll
+#pragma unroll
   for (int T = 0; T < 8; ++T) rs.o[T] *= corr;
   accumulate_pv(st, p, rs);
+  if (more) load_v_any(st, sl, next_key0, kend, n16, q4);
 }
 
 template <bool BF16>
@@ -315,6 +393,26 @@ __global__ __launch_bounds__(kThreads, 2) void decode_partition_kernel(const Dec
     return;
   }
   const int c1 = min(c0 + p.split, L);
+  const int nsteps = (c1 - c0 + kStep - 1) / kStep;
+  Slab sl;
+  sl.kb = (const uint8_t*)p.k + ((int64_t)b * p.k_sb + (int64_t)h * p.k_sh) * kElem;
+  sl.vb = (const uint8_t*)p.v + ((int64_t)b * p.v_sb + (int64_t)h * p.v_sh) * kElem;
+  sl.kss = (uint32_t)(p.k_ss * kElem);
+  sl.vss = (uint32_t)(p.v_ss * kElem);
+  if constexpr (BF16) {
+    sl.klane = (uint32_t)n16 * sl.kss + 64u * q4;          // K row n16, dims 32*q4 ..
+    sl.vlane = (uint32_t)(4 * q4) * sl.vss + 16u * n16;    // V rows 4*q4 + .., dims 8*n16 ..
+  } else {
+    sl.klane = (uint32_t)n16 * sl.kss + 128u * q4;
+    sl.vlane = (uint32_t)(4 * q4) * sl.vss + 32u * n16;
+  }
+
+  // ---- the first K/V steps go to memory before anything else, so that their
+  //      latency overlaps the query prologue
+  int s = wave;
+  Step A;
+  if (s < nsteps) load_step(A, sl, c0 + s * kStep, c1, n16, q4);
+
   const bool rope = p.rope_theta > 0.0;
   const bool k_pro = rope || p.k_norm_w != nullptr;
   const bool has_new = k_pro && c1 == L;   // this chunk holds slot L-1
@@ -331,7 +429,7 @@ __global__ __launch_bounds__(kThreads, 2) void decode_partition_kernel(const Dec
       load_half_row<BF16>(row, c16, x);
     }
     prologue_row<BF16>(x, c16, p.q_norm_w, p.eps, rope, sm.cs);
-    #pragma unroll
+#pragma unroll
     for (int j = 0; j < 4; ++j) {
       sm.qp[r][4 * c16 + j] = x[j];
       sm.qp[r][64 + 4 * c16 + j] = x[4 + j];
@@ -341,7 +439,7 @@ __global__ __launch_bounds__(kThreads, 2) void decode_partition_kernel(const Dec
       float y[8];
       load_half_row<BF16>(row, c16, y);
       prologue_row<BF16>(y, c16, p.k_norm_w, p.eps, rope, sm.cs);
-      #pragma unroll
+#pragma unroll
       for (int j = 0; j < 4; ++j) {
         sm.kn[4 * c16 + j] = y[j];
         sm.kn[64 + 4 * c16 + j] = y[4 + j];
@@ -352,68 +450,39 @@ __global__ __launch_bounds__(kThreads, 2) void decode_partition_kernel(const Dec
 
   QFrag qf;
   if constexpr (BF16) {
-    #pragma unroll
+#pragma unroll
     for (int kb = 0; kb < 4; ++kb) {
-      const float* s = &sm.qp[n16][32 * q4 + 8 * kb];
-      qf.q[kb] = as_bf16x8(u32x4{pack_bf16x2(s[0], s[1]), pack_bf16x2(s[2], s[3]), pack_bf16x2(s[4], s[5]),
-                                 pack_bf16x2(s[6], s[7])});
+      const float* x = &sm.qp[n16][32 * q4 + 8 * kb];
+      float hi[8], lo[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        hi[j] = (float)(__bf16)x[j];
+        lo[j] = x[j] - hi[j];
+      }
+      qf.hi[kb] = as_bf16x8(u32x4{pack_bf16x2(hi[0], hi[1]), pack_bf16x2(hi[2], hi[3]), pack_bf16x2(hi[4], hi[5]),
+                                  pack_bf16x2(hi[6], hi[7])});
+      qf.lo[kb] = as_bf16x8(u32x4{pack_bf16x2(lo[0], lo[1]), pack_bf16x2(lo[2], lo[3]), pack_bf16x2(lo[4], lo[5]),
+                                  pack_bf16x2(lo[6], lo[7])});
     }
   } else {
-    #pragma unroll
+#pragma unroll
     for (int j = 0; j < 32; ++j) qf.q[j] = sm.qp[n16][32 * q4 + j];
   }
-
-  // ---- the sweep over this chunk's keys
-  const uint8_t* kbase = (const uint8_t*)p.k + ((int64_t)b * p.k_sb + (int64_t)h * p.k_sh) * kElem;
-  const uint8_t* vbase = (const uint8_t*)p.v + ((int64_t)b * p.v_sb + (int64_t)h * p.v_sh) * kElem;
-  const int64_t kss = p.k_ss * kElem, vss = p.v_ss * kElem;
-  const int nsteps = (c1 - c0 + kStep - 1) / kStep;
   const int kn = L - 1;
 
+  // ---- the sweep over this chunk's keys
   RunState rs;
-  #pragma unroll
+#pragma unroll
   for (int T = 0; T < 8; ++T) rs.o[T] = f32x4{0.f, 0.f, 0.f, 0.f};
   rs.m = -INFINITY;
   rs.l = 0.f;
 
-  int s = wave;
-  if constexpr (BF16) {
-    // two step buffers: the loads of step s + 4 are in flight while step s is computed
-    if (s < nsteps) {
-      Step A, B;
-      {
-        const int key0 = c0 + s * kStep;
-        load_step(A, kbase, vbase, kss, vss, key0, c1, key0 + kStep <= c1, n16, q4);
-      }
-      for (;;) {
-        const int keyA = c0 + s * kStep;
-        const bool fullA = keyA + kStep <= c1;
-        const int sB = s + kWaves;
-        const int keyB = c0 + sB * kStep;
-        if (sB < nsteps) load_step(B, kbase, vbase, kss, vss, keyB, c1, keyB + kStep <= c1, n16, q4);
-        if (has_new && kn >= keyA && kn < keyA + kStep) put_new_key(A, sm.kn, keyA, kn, n16, q4);
-        sweep_step(A, qf, rs, p.scale_log2, keyA, c1, fullA, q4);
-        if (sB >= nsteps) break;
-        const int sA2 = sB + kWaves;
-        const int keyA2 = c0 + sA2 * kStep;
-        if (sA2 < nsteps) load_step(A, kbase, vbase, kss, vss, keyA2, c1, keyA2 + kStep <= c1, n16, q4);
-        const bool fullB = keyB + kStep <= c1;
-        if (has_new && kn >= keyB && kn < keyB + kStep) put_new_key(B, sm.kn, keyB, kn, n16, q4);
-        sweep_step(B, qf, rs, p.scale_log2, keyB, c1, fullB, q4);
-        if (sA2 >= nsteps) break;
-        s = sA2;
-      }
-    }
-  } else {
-    // f32 steps are twice as large: one buffer (the f32 path serves small parity shapes)
-    for (; s < nsteps; s += kWaves) {
-      Step A;
-      const int key0 = c0 + s * kStep;
-      const bool full = key0 + kStep <= c1;
-      load_step(A, kbase, vbase, kss, vss, key0, c1, full, n16, q4);
-      if (has_new && kn >= key0 && kn < key0 + kStep) put_new_key(A, sm.kn, key0, kn, n16, q4);
-      sweep_step(A, qf, rs, p.scale_log2, key0, c1, full, q4);
-    }
+  // one step buffer per wave, refilled in place: the next step's K is in
+  // flight during this step's softmax and P V, its V during the next QK^T
+  while (s < nsteps) {
+    sweep_step(A, qf, sm.kn, has_new, kn, rs, p.scale_log2, c0 + s * kStep, c1, c0 + (s + kWaves) * kStep, sl, n16,
+               q4);
+    s += kWaves;
   }
 
   // ---- merge the 4 wave states of this workgroup (ADR-0060 section 4 merge)
@@ -423,7 +492,7 @@ __global__ __launch_bounds__(kThreads, 2) void decode_partition_kernel(const Dec
     sm.mm[wave][n16] = rs.m;
     sm.ml[wave][n16] = rs.l;
   }
-  #pragma unroll
+#pragma unroll
   for (int i = 0; i < 4; ++i) {
     float* dst = &sm.mo[wave][n16][(4 * q4 + i) * 8];
     *(f32x4*)dst = f32x4{rs.o[0][i], rs.o[1][i], rs.o[2][i], rs.o[3][i]};
@@ -434,15 +503,16 @@ __global__ __launch_bounds__(kThreads, 2) void decode_partition_kernel(const Dec
   const int g = tid >> 4, d8 = (tid & 15) * 8;
   if (g >= G) return;
   float M = sm.mm[0][g];
+#pragma unroll
   for (int w = 1; w < kWaves; ++w) M = fmaxf(M, sm.mm[w][g]);
   float lt = 0.f;
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  #pragma unroll
+#pragma unroll
   for (int w = 0; w < kWaves; ++w) {
     const float sc = fast_exp2(sm.mm[w][g] - M);   // 0 for a wave that saw no key
     lt += sc * sm.ml[w][g];
     const float* src = &sm.mo[w][g][d8];
-    #pragma unroll
+#pragma unroll
     for (int j = 0; j < 8; ++j) acc[j] += sc * src[j];
   }
   const int hq = h * G + g;
@@ -470,14 +540,18 @@ __global__ __launch_bounds__(kThreads, 2) void decode_partition_kernel(const Dec
 
 // ----------------------------------------------------------------- merge kernel
 // One workgroup per (q head, sequence): out = sum_c 2^(m_c - M) O_c / sum_c 2^(m_c - M) l_c
-// over the n = ceil(L / T) chunks that hold keys (ADR-0060 section 4).
+// over the n = ceil(L / T) chunks that hold keys (ADR-0060 section 4).  Thread
+// (group sg, dims 4*d4 .. 4*d4+3) folds chunks sg, sg + 16, ... with a running
+// maximum, kMergeUnroll chunks per batch of loads; the 16 group states are then
+// merged through LDS.
 
-constexpr int kMergeThreads = 256;
+constexpr int kMergeThreads = 512;
+constexpr int kMergeGroups = kMergeThreads / 32;
+constexpr int kMergeUnroll = 8;
 
 __global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(const DecodeParams p) {
-  __shared__ float red[kMergeThreads];
-  __shared__ float racc[8][kHeadDim + 4];
-  __shared__ float rl[8];
+  __shared__ __attribute__((aligned(16))) float racc[kMergeGroups][kHeadDim];
+  __shared__ float rm[kMergeGroups], rl[kMergeGroups];
 
   const int hq = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
   int L = p.seq_lens[b];
@@ -492,39 +566,59 @@ __global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(const Decod
     return;
   }
   const int64_t slot0 = ((int64_t)b * p.num_q_heads + hq) * p.n_split;
-  float mx = -INFINITY;
-  for (int c = tid; c < n; c += kMergeThreads) mx = fmaxf(mx, p.ws_ml[2 * (slot0 + c)]);
-  red[tid] = mx;
-  __syncthreads();
-  for (int w = kMergeThreads / 2; w > 0; w >>= 1) {
-    if (tid < w) red[tid] = fmaxf(red[tid], red[tid + w]);
-    __syncthreads();
-  }
-  const float M = red[0];
-
-  const int dg = tid & 31, sg = tid >> 5;     // 4 dims x 8 split groups
+  const int d4 = tid & 31, sg = tid >> 5;
+  float M = -INFINITY, ls = 0.f;
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  float ls = 0.f;
-  for (int c = sg; c < n; c += 8) {
-    const float m_c = p.ws_ml[2 * (slot0 + c)];
-    const float l_c = p.ws_ml[2 * (slot0 + c) + 1];
-    const float w = fast_exp2(m_c - M);
-    const f32x4 oc = *(const f32x4*)(p.ws_o + (slot0 + c) * kHeadDim + 4 * dg);
-    acc += w * oc;
-    ls += w * l_c;
+  for (int c = sg; c < n; c += kMergeGroups * kMergeUnroll) {
+    float mc[kMergeUnroll], lc[kMergeUnroll];
+    f32x4 oc[kMergeUnroll];
+#pragma unroll
+    for (int u = 0; u < kMergeUnroll; ++u) {
+      const int cc = c + u * kMergeGroups;
+      if (cc < n) {
+        const u32x2 ml = *(const u32x2*)(p.ws_ml + 2 * (slot0 + cc));
+        mc[u] = __uint_as_float(ml[0]);
+        lc[u] = __uint_as_float(ml[1]);
+        oc[u] = *(const f32x4*)(p.ws_o + (slot0 + cc) * kHeadDim + 4 * d4);
+      } else {
+        mc[u] = -INFINITY;
+        lc[u] = 0.f;
+        oc[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+      }
+    }
+    float mb = M;
+#pragma unroll
+    for (int u = 0; u < kMergeUnroll; ++u) mb = fmaxf(mb, mc[u]);
+    const float corr = fast_exp2(M - mb);   // 0 while M = -inf
+    ls *= corr;
+    acc *= corr;
+#pragma unroll
+    for (int u = 0; u < kMergeUnroll; ++u) {
+      const float w = fast_exp2(mc[u] - mb);
+      ls += w * lc[u];
+      acc += w * oc[u];
+    }
+    M = mb;
   }
-  *(f32x4*)&racc[sg][4 * dg] = acc;
-  if (dg == 0) rl[sg] = ls;
+  *(f32x4*)&racc[sg][4 * d4] = acc;
+  if (d4 == 0) {
+    rm[sg] = M;
+    rl[sg] = ls;
+  }
   __syncthreads();
   if (tid < 32) {
-    f32x4 t = *(const f32x4*)&racc[0][4 * tid];
-    float lt = rl[0];
-    for (int j = 1; j < 8; ++j) {
-      t += *(const f32x4*)&racc[j][4 * tid];
-      lt += rl[j];
+    float Mt = rm[0];
+#pragma unroll
+    for (int j = 1; j < kMergeGroups; ++j) Mt = fmaxf(Mt, rm[j]);
+    f32x4 t = {0.f, 0.f, 0.f, 0.f};
+    float lt = 0.f;
+#pragma unroll
+    for (int j = 0; j < kMergeGroups; ++j) {
+      const float w = fast_exp2(rm[j] - Mt);   // 0 for a group that held no chunk
+      t += w * *(const f32x4*)&racc[j][4 * tid];
+      lt += w * rl[j];
     }
-    const float inv = 1.0f / lt;
-    t *= inv;
+    t *= 1.0f / lt;
     if (p.out_bf16) *(u32x2*)(o + 8 * tid) = u32x2{pack_bf16x2(t[0], t[1]), pack_bf16x2(t[2], t[3])};
     else *(f32x4*)(o + 16 * tid) = t;
   }

@@ -12,7 +12,8 @@
 //
 // gfx950 mapping:
 //  * one workgroup = (128-query tile, query head, sequence), 4 waves of 32
-//    query rows; workgroups are issued heaviest (last) query tile first.
+//    query rows, on a 1-D grid ordered so that all workgroups of one KV head
+//    land on one XCD (shared L2), heaviest (last) query tile first.
 //  * per 64-key tile: raw K/V rows are fetched into registers one tile ahead,
 //    the key prologue runs on them (f32), K' (bf16) and V go to LDS;
 //    S^T = K' Q'^T and O^T = V^T P^T run on v_mfma_f32_32x32x16_bf16 with
@@ -30,6 +31,7 @@ constexpr int kWaves = 4;
 constexpr int kThreads = 256;
 constexpr int BM = kPrefillBM;   // 128
 constexpr int BN = kPrefillBN;   // 64
+constexpr int kXcds = 8;         // MI355X: 8 accelerator complex dies, each with its own L2
 
 struct __attribute__((aligned(16))) PrefillSmem {
   uint32_t kt[BN][kHeadDim / 2];   // K' tile, bf16 pairs, 16-byte chunks swizzled by key & 15
@@ -46,9 +48,27 @@ __device__ __forceinline__ int qk_chunk(int kk, int hf) { return kk < 4 ? 4 * hf
 __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(const PrefillParams p) {
   __shared__ PrefillSmem sm;
 
-  const int qt = p.n_qtiles - 1 - (int)blockIdx.x;   // heaviest tiles first
-  const int hq = blockIdx.y, b = blockIdx.z;
-  const int h = hq / p.group;
+  // XCD-aware workgroup order: consecutive workgroup ids are dealt round-robin
+  // to the 8 XCDs, so when the (sequence, KV head) groups divide evenly every
+  // group's workgroups share one XCD and its K/V tiles stay in that XCD's L2.
+  // Within a group: heaviest (last) query tile first, the G query heads of a
+  // tile adjacent.
+  const int G = p.group;
+  const int per_group = p.n_qtiles * G;
+  const int groups = p.batch * p.num_kv_heads;
+  const int bid = blockIdx.x;
+  int grp, w;
+  if (groups % kXcds == 0) {
+    const int slot = bid / kXcds;
+    grp = bid % kXcds + kXcds * (slot / per_group);
+    w = slot % per_group;
+  } else {
+    grp = bid / per_group;
+    w = bid % per_group;
+  }
+  const int b = grp / p.num_kv_heads, h = grp % p.num_kv_heads;
+  const int qt = p.n_qtiles - 1 - w / G;
+  const int hq = h * G + w % G;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int n32 = lane & 31, hf = lane >> 5;
 
@@ -325,7 +345,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(const PrefillParam
 }  // namespace
 
 hipError_t launch_prefill(const PrefillParams& p, hipStream_t stream) {
-  const dim3 grid(p.n_qtiles, p.num_q_heads, p.batch);
+  const dim3 grid(p.n_qtiles * p.num_q_heads * p.batch);
   hipLaunchKernelGGL(prefill_kernel, grid, dim3(kThreads), 0, stream, p);
   return hipGetLastError();
 }

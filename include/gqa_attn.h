@@ -65,7 +65,8 @@ typedef enum gqa_status {
   GQA_OK = 0,
   GQA_ERR_NULL = 1,        /* a required pointer is NULL                          */
   GQA_ERR_SHAPE = 2,       /* non-positive size, Hq % Hkv != 0, bad stride        */
-  GQA_ERR_UNSUPPORTED = 3, /* head_dim != 128, dtype, G too large, prefill f32    */
+  GQA_ERR_UNSUPPORTED = 3, /* head_dim != 128, dtype, G too large, prefill f32,
+                              decode cache slab of one (b, head) >= 4 GiB        */
   GQA_ERR_ALIGN = 4,       /* base pointer or stride not 16-byte aligned          */
   GQA_ERR_WORKSPACE = 5,   /* workspace NULL or smaller than required             */
   GQA_ERR_HIP = 6          /* a kernel launch failed (hipGetLastError)            */

@@ -226,3 +226,26 @@ def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(G, "_lib", None)
     with pytest.raises(RuntimeError, match="not built"):
         G.gqa_attn_version()
+
+
+def test_decode_merge_entry_errors_and_single_chunk_noop():
+    d = ddesc(kv_split_tokens=512)
+    st, need = G.gqa_attn_decode_workspace_size(d)
+    assert G.gqa_attn_decode_merge(None, FAKE, FAKE, FAKE, need, None) == G.GQA_ERR_NULL
+    assert G.gqa_attn_decode_merge(d, NULL, FAKE, FAKE, need, None) == G.GQA_ERR_NULL
+    assert G.gqa_attn_decode_merge(d, FAKE, NULL, FAKE, need, None) == G.GQA_ERR_NULL
+    assert G.gqa_attn_decode_merge(d, FAKE, FAKE, NULL, need, None) == G.GQA_ERR_WORKSPACE
+    assert G.gqa_attn_decode_merge(d, FAKE, FAKE, FAKE, need - 4, None) == G.GQA_ERR_WORKSPACE
+    assert G.gqa_attn_decode_merge(d, FAKE, FAKE + 4, FAKE, need, None) == G.GQA_ERR_ALIGN
+    # one chunk: the merge step has nothing to do and launches nothing
+    assert G.gqa_attn_decode_merge(ddesc(kv_split_tokens=4096), FAKE, FAKE, NULL, 0, None) == G.GQA_OK
+    assert G.gqa_attn_decode_partition(None, FAKE, FAKE, FAKE, FAKE, FAKE, NULL, NULL, 1e6, FAKE, NULL, 0,
+                                       None) == G.GQA_ERR_NULL
+
+
+def test_decode_cache_slab_limit():
+    # one (b, head) slab of 2^20 rows with a 4096-element row stride spans 8 GiB
+    d = ddesc(max_seq=1 << 20, k_stride_s=4096, v_stride_s=128, k_stride_h=(1 << 20) * 4096,
+              v_stride_h=(1 << 20) * 128, k_stride_b=8 * (1 << 20) * 4096, v_stride_b=8 * (1 << 20) * 128,
+              kv_split_tokens=4096)
+    assert call_decode(d) == G.GQA_ERR_UNSUPPORTED
