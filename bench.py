@@ -180,6 +180,45 @@ def cpu_baseline(case_inputs, bytes_per_call, budget_s=12.0):
                       f"{per * 1e3:.1f} ms each, host cores available {cores})"}
 
 
+def prefill_case(torch, G, synth, np):
+    """Device inputs and a call closure of the causal prefill workload."""
+    pw = synth.QWEN3_PREFILL
+    pin = synth.make_prefill(pw)
+    bf = torch.bfloat16
+    to = lambda x: None if x is None else torch.from_numpy(np.ascontiguousarray(x)).cuda().to(bf)
+    t = dict(q=to(pin["q"]), k=to(pin["k"]), v=to(pin["v"]), qw=to(pin["q_norm_w"]), kw=to(pin["k_norm_w"]),
+             sl=torch.from_numpy(pin["seq_lens"]).cuda(), pos=torch.from_numpy(pin["positions"]).cuda())
+    t["out"] = torch.empty(t["q"].shape, dtype=torch.float32, device="cuda")
+    desc = G.prefill_desc(t["q"], t["k"], t["v"], t["out"], True, pw.eps)
+
+    def call(i, stream):
+        st = G.gqa_attn_prefill(desc, t["q"].data_ptr(), t["k"].data_ptr(), t["v"].data_ptr(), t["sl"].data_ptr(),
+                                t["pos"].data_ptr(), t["qw"].data_ptr(), t["kw"].data_ptr(), pw.rope_theta,
+                                t["out"].data_ptr(), stream)
+        assert st == G.GQA_OK
+    return pw, pin, t, call
+
+
+def profile_calls(args, torch, G, synth, np):
+    """Plain back-to-back calls of one workload, for profiler runs."""
+    if args.only == "prefill":
+        _, _, _, call = prefill_case(torch, G, synth, np)
+    else:
+        w = {"decode": synth.QWEN3_DECODE, "long": synth.LLAMA70B_LONG, "ragged": synth.QWEN3_RAGGED}[args.only or "decode"]
+        call = DecodeCase(w, 1, torch, G, synth, exact_first=(w is synth.QWEN3_DECODE)).call
+    if args.copy_probe_mib:
+        src = torch.ones(args.copy_probe_mib << 18, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"[bench] copy probe: {args.copy_probe_mib} MiB read, {args.copy_probe_mib} MiB written")
+    s = torch.cuda.current_stream().cuda_stream
+    for i in range(args.eager_calls):
+        call(i, s)
+    torch.cuda.synchronize()
+    log(f"[bench] {args.eager_calls} calls of {args.only} done")
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
@@ -187,6 +226,12 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-extra", action="store_true", help="skip the prefill and long-context decode fields")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--only", choices=["decode", "prefill", "long", "ragged"],
+                    help="with --eager-calls: the workload to run")
+    ap.add_argument("--eager-calls", type=int, default=0,
+                    help="profiling mode: run this many plain calls of --only's workload (no timing, no JSON)")
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="profiling mode: first copy a device buffer of this many MiB (counter calibration)")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -202,6 +247,8 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     G.lib()
     K, W = args.steps, args.warmup
+    if args.eager_calls:
+        return profile_calls(args, torch, G, synth, np)
 
     # ---------------- headline: Qwen3-14B decode, B = 1, S = 4096
     w = synth.QWEN3_DECODE
@@ -237,22 +284,7 @@ def main():
     # ---------------- extras: causal prefill and the other decode shapes
     if not args.no_extra:
         extra = {}
-        pw = synth.QWEN3_PREFILL
-        pin = synth.make_prefill(pw)
-        bf = torch.bfloat16
-        to = lambda x: None if x is None else torch.from_numpy(np.ascontiguousarray(x)).cuda().to(bf)
-        pq, pk, pv = to(pin["q"]), to(pin["k"]), to(pin["v"])
-        pqw, pkw = to(pin["q_norm_w"]), to(pin["k_norm_w"])
-        psl = torch.from_numpy(pin["seq_lens"]).cuda()
-        ppos = torch.from_numpy(pin["positions"]).cuda()
-        pout = torch.empty(pq.shape, dtype=torch.float32, device="cuda")
-        pdesc = G.prefill_desc(pq, pk, pv, pout, True, pw.eps)
-
-        def pcall(i, stream):
-            st = G.gqa_attn_prefill(pdesc, pq.data_ptr(), pk.data_ptr(), pv.data_ptr(), psl.data_ptr(),
-                                    ppos.data_ptr(), pqw.data_ptr(), pkw.data_ptr(), pw.rope_theta,
-                                    pout.data_ptr(), stream)
-            assert st == G.GQA_OK
+        pw, pin, pt_inputs, pcall = prefill_case(torch, G, synth, np)
         pk_steps = max(5, K // 10)
         pt = graph_time_ms(torch, pcall, pk_steps, max(2, W // 10))
         us_p = 1000.0 * pt / pk_steps
@@ -267,7 +299,7 @@ def main():
                                          "frac": round(tf_k / BF16_PEAK_TFLOPS, 4), "traffic": None,
                                          "algorithmic_flops": flops}}
         log(f"[bench] prefill {us_p:.1f} us -> {tf:.1f} TFLOP/s (kernel {ev_p:.1f} us)")
-        del pq, pk, pv, pout
+        del pt_inputs, pcall
         torch.cuda.empty_cache()
 
         for dw in (synth.LLAMA70B_LONG, synth.QWEN3_RAGGED):

@@ -74,15 +74,31 @@ size_t decode_ws_bytes(const gqa_decode_desc* d, int32_t n) {
   return slots * (GQA_ATTN_HEAD_DIM + 2) * sizeof(float);
 }
 
+// Prefill workgroup blocking: HC query heads (the largest divisor of G that is
+// at most 8) times BQ query tokens, with HC * BQ / 32 <= 10 waves of 32 rows.
+void prefill_blocking(int G, int32_t* HC, int32_t* BQ) {
+  int hc = 1;
+  for (int c = 1; c <= 8 && c <= G; ++c)
+    if (G % c == 0) hc = c;
+  int tb = gqa::kPrefillMaxWaves / hc;   // 32-token blocks per head
+  if (tb > 4) tb = 4;
+  if (tb < 1) tb = 1;
+  *HC = hc;
+  *BQ = 32 * tb;
+}
+
 gqa_status check_prefill_desc(const gqa_prefill_desc* d) {
   if (d == nullptr) return GQA_ERR_NULL;
   if (d->batch < 1 || d->num_q_heads < 1 || d->num_kv_heads < 1 || d->max_seq < 1) return GQA_ERR_SHAPE;
-  if ((int64_t)d->batch * d->num_q_heads * ((d->max_seq + gqa::kPrefillBM - 1) / gqa::kPrefillBM) > INT32_MAX)
-    return GQA_ERR_SHAPE;
+  if ((int64_t)d->batch * d->num_q_heads * ((d->max_seq + 31) / 32) > INT32_MAX) return GQA_ERR_SHAPE;
   if (d->num_q_heads % d->num_kv_heads != 0) return GQA_ERR_SHAPE;
   if (d->head_dim != GQA_ATTN_HEAD_DIM) return GQA_ERR_UNSUPPORTED;
   if (d->in_dtype != GQA_BF16 || !dtype_ok(d->out_dtype)) return GQA_ERR_UNSUPPORTED;
   if (d->causal != 0 && d->causal != 1) return GQA_ERR_SHAPE;
+  // prefill addresses one (b, KV head) K / V slab with 32-bit byte offsets
+  if ((int64_t)d->max_seq * d->k_stride_s * 2 + 512 > ((int64_t)1 << 32) ||
+      (int64_t)d->max_seq * d->v_stride_s * 2 + 512 > ((int64_t)1 << 32))
+    return GQA_ERR_UNSUPPORTED;
   const int ei = 2, eo = elem_size(d->out_dtype);
   const int64_t s[] = {d->q_stride_b, d->q_stride_h, d->q_stride_s, d->k_stride_b, d->k_stride_h, d->k_stride_s,
                        d->v_stride_b, d->v_stride_h, d->v_stride_s};
@@ -272,7 +288,8 @@ gqa_status gqa_attn_prefill(const gqa_prefill_desc* d, const void* q, const void
   p.max_seq = d->max_seq;
   p.causal = d->causal;
   p.out_bf16 = d->out_dtype == GQA_BF16;
-  p.n_qtiles = (d->max_seq + gqa::kPrefillBM - 1) / gqa::kPrefillBM;
+  prefill_blocking(p.group, &p.heads_per_wg, &p.block_q);
+  p.n_qblocks = (d->max_seq + p.block_q - 1) / p.block_q;
   p.eps = d->eps;
   p.scale_log2 = resolve_scale_log2(d->scale);
   p.rope_theta = rope_theta > 0.f ? (double)rope_theta : 0.0;

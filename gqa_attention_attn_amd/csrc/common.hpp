@@ -51,7 +51,9 @@ struct PrefillParams {
   int32_t batch, num_q_heads, num_kv_heads, group, max_seq;
   int32_t causal;
   int32_t out_bf16;
-  int32_t n_qtiles;
+  int32_t heads_per_wg;   // HC: query heads of one KV head batched in a workgroup
+  int32_t block_q;        // BQ: query tokens per workgroup (multiple of 32)
+  int32_t n_qblocks;      // ceil(max_seq / BQ)
   float eps;
   float scale_log2;
   double rope_theta;
@@ -62,9 +64,8 @@ hipError_t launch_decode_partition(const DecodeParams& p, bool in_bf16, hipStrea
 hipError_t launch_decode_merge(const DecodeParams& p, hipStream_t stream);
 hipError_t launch_prefill(const PrefillParams& p, hipStream_t stream);
 
-// Prefill tiling, shared by the launcher and the host planning code.
-constexpr int kPrefillBM = 128;   // query rows per workgroup
-constexpr int kPrefillBN = 64;    // keys per K/V tile
+// Prefill workgroups hold HC * BQ / 32 waves of 32 query rows, at most this many.
+constexpr int kPrefillMaxWaves = 10;
 
 // ----------------------------------------------------------------- device helpers
 

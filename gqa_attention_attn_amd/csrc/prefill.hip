@@ -3,41 +3,51 @@
 //
 // Algorithm (the pages):
 //  * "ADR-0060: AHBM GQA Fused Attention Kernel (Llama3-70B)", section 3:
-//    tiled online softmax (FlashAttention) over K/V tiles; section 5.4: a
-//    key tile entirely in the future of a query block is skipped, one
-//    entirely in its past needs no mask, an overlapping one gets the
-//    triangular mask; section 5.2: query head h reads KV head floor(h / G).
-//  * "Qwen3-14B Optimization", section 2.1 "Shape 4" / #796: QK-norm and
-//    RoPE are applied inside the attention stage; #602: RoPE on lo/hi halves.
+//    tiled online softmax (FlashAttention) over K/V tiles; section 5.4: a key
+//    tile entirely in the future of a query block is skipped, one entirely in
+//    its past needs no mask, an overlapping one gets the triangular mask, and
+//    the query heads of one KV head are batched along the matrix M axis as in
+//    decode (section 5.2: query head h reads KV head floor(h / G)).
+//  * "Qwen3-14B Optimization", section 2.1 "Shape 4" / #796: QK-norm and RoPE
+//    are applied inside the attention stage; #602: RoPE on lo/hi halves.
 //
 // gfx950 mapping:
-//  * one workgroup = (128-query tile, query head, sequence), 4 waves of 32
-//    query rows, on a 1-D grid ordered so that all workgroups of one KV head
-//    land on one XCD (shared L2), heaviest (last) query tile first.
-//  * per 64-key tile: raw K/V rows are fetched into registers one tile ahead,
-//    the key prologue runs on them (f32), K' (bf16) and V go to LDS;
-//    S^T = K' Q'^T and O^T = V^T P^T run on v_mfma_f32_32x32x16_bf16 with
-//    f32 accumulation.  In the S^T orientation a lane owns one query row, so
-//    the row max needs one cross-lane step.  K' rows are XOR-swizzled in
-//    16-byte chunks so the MFMA operand reads are bank-conflict free.
-//  * scores live in the log2 domain (scale * log2 e folded in) and use the
-//    hardware exp2.
+//  * one workgroup = (sequence, KV head, a chunk of HC <= 8 of its query
+//    heads, a block of BQ query tokens); wave w owns 32 query rows = one head
+//    and 32 consecutive tokens, so a workgroup holds HC * BQ rows (10 waves for
+//    5 heads x 64 tokens).  Every key tile, and its key prologue, is shared by
+//    all of them.
+//  * per 32-key tile: the raw K and V rows are fetched into registers one tile
+//    ahead; K rows go through the key prologue (f32) and are stored as bf16 K'
+//    in LDS (16-byte chunks XOR-swizzled by key), V rows are stored transposed
+//    (V^T, key pairs packed per dword); both double-buffered, so one barrier
+//    per tile suffices.  S^T = K' Q'^T and O^T = V^T P^T run on
+//    v_mfma_f32_32x32x16_bf16 with f32 accumulation; in the S^T orientation a
+//    lane owns one query row, so the row max needs one cross-lane step.
+//  * scores live in the log2 domain (scale * log2 e folded into the exp2 FMA);
+//    the running output is rescaled only when a row maximum grows by more
+//    than 2^8 (the final O / l is unchanged by the choice of reference max).
+//  * a 1-D grid ordered so every (sequence, KV head) group lands on one XCD
+//    (its K/V stay in that XCD's L2), heaviest query block first.
 #include "common.hpp"
 
 namespace gqa {
 namespace {
 
-constexpr int kWaves = 4;
-constexpr int kThreads = 256;
-constexpr int BM = kPrefillBM;   // 128
-constexpr int BN = kPrefillBN;   // 64
-constexpr int kXcds = 8;         // MI355X: 8 accelerator complex dies, each with its own L2
+constexpr int kMaxWaves = kPrefillMaxWaves;
+constexpr int kMaxThreads = 64 * kMaxWaves;
+constexpr int BN = 32;                 // keys per tile
+constexpr int kXcds = 8;               // MI355X: 8 XCDs, each with its own L2
+constexpr int kVtRow = 40;             // V^T row stride in bf16 (32 keys + 8): conflict-free 16-byte reads
+constexpr float kLazyRescale = 8.0f;   // rescale O only when a row max grows by more than 2^8
+constexpr int kKUnits = 256;           // K staging units per tile (32 keys x 8 dim chunks)
+constexpr int kUnits = 512;            // + 256 V staging units (16 key pairs x 16 dim chunks)
 
 struct __attribute__((aligned(16))) PrefillSmem {
-  uint32_t kt[BN][kHeadDim / 2];   // K' tile, bf16 pairs, 16-byte chunks swizzled by key & 15
-  uint32_t vt[BN][kHeadDim / 2];   // V tile, bf16 pairs, row-major
-  double inv_rev[kHeadDim / 2];    // theta^(-2i/128) / (2 pi)
-  float gk[kHeadDim];              // key RMSNorm weight (f32)
+  uint32_t kt[2][BN][kHeadDim / 2];   // K' tiles, bf16 pairs, 16-byte chunks swizzled by key & 15
+  uint16_t vt[2][kHeadDim][kVtRow];   // V^T tiles: vt[buf][dim][vpos(key)]
+  double inv_rev[kHeadDim / 2];       // theta^(-2i/128) / (2 pi)
+  float gk[kHeadDim];                 // key RMSNorm weight (f32)
 };
 
 // Logical 16-byte chunk (of 16 per 128-dim row) holding operand slot kk of
@@ -45,20 +55,123 @@ struct __attribute__((aligned(16))) PrefillSmem {
 // [64+32hf, 64+32hf+32), so every RoPE pair (i, i+64) stays in one lane.
 __device__ __forceinline__ int qk_chunk(int kk, int hf) { return kk < 4 ? 4 * hf + kk : 8 + 4 * hf + (kk - 4); }
 
-__global__ __launch_bounds__(kThreads, 2) void prefill_kernel(const PrefillParams p) {
+// Position of key k (0..31) of a tile in a V^T row.  Key 16e + 8a + 4h + r
+// goes to 16e + 8h + 4a + r, so the 8 keys that MFMA e of lane half h takes
+// ({16e + 4h + r, 16e + 8 + 4h + r}, r < 4) are 16 contiguous bytes.
+__device__ __forceinline__ int vpos(int k) { return (k & 0x13) | ((k & 4) << 1) | ((k & 8) >> 1); }
+
+// K' chunk swizzle: a bijection on keys mod 16 (conflict-free operand reads of
+// 16 consecutive keys) that alternates the 128-byte half between neighbouring
+// keys (fewer conflicts when 8 consecutive keys are stored together).
+__device__ __forceinline__ int kswz(int key) { return (key & 15) ^ ((key & 1) << 3); }
+
+struct Raw { u32x4 a, b; };
+
+// One (sequence, KV head) slab: uniform 64-bit bases plus 32-bit byte offsets
+// (the host guarantees each slab spans less than 4 GiB).
+struct Staging {
+  const uint8_t* kslab;
+  const uint8_t* vslab;
+  uint32_t kss, vss;   // row strides in bytes
+  int n;
+};
+
+// Fetch staging unit u of tile kt.  K unit: key row u/8, dims [8(u%8), +8)
+// and [64 + 8(u%8), +8).  V unit (u >= 256): key rows 2v, 2v+1 (v = (u-256)%16),
+// dims [8((u-256)/16), +8).  Rows at or past n are zero (never read).
+__device__ __forceinline__ void fetch_unit(Raw& r, const Staging& s, int kt, int u) {
+  if (u < kKUnits) {
+    const int key = kt * BN + (u >> 3), c = u & 7;
+    if (key < s.n) {
+      const uint32_t off = (uint32_t)key * s.kss + 16u * c;
+      r.a = *(const u32x4*)(s.kslab + off);
+      r.b = *(const u32x4*)(s.kslab + off + 128u);
+    } else {
+      r.a = r.b = u32x4{0, 0, 0, 0};
+    }
+  } else {
+    const int v = u - kKUnits;
+    const int key = kt * BN + 2 * (v & 15), dc = v >> 4;
+    const uint32_t off = (uint32_t)key * s.vss + 16u * dc;
+    r.a = key < s.n ? *(const u32x4*)(s.vslab + off) : u32x4{0, 0, 0, 0};
+    r.b = key + 1 < s.n ? *(const u32x4*)(s.vslab + off + s.vss) : u32x4{0, 0, 0, 0};
+  }
+}
+
+// Stage unit u of tile kt into LDS buffer buf: the key prologue for K units
+// (RMSNorm over the row's 8 units = 8 consecutive lanes, then RoPE), the
+// transpose for V units.
+__device__ __forceinline__ void stage_unit(PrefillSmem& sm, const Raw& r, const PrefillParams& p, bool rope,
+                                           double pos0, int kt, int u, int buf) {
+  if (u < kKUnits) {
+    const int lkey = u >> 3, c = u & 7;
+    float xl[8], xh[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      xl[e] = bf16_elem(r.a, e);
+      xh[e] = bf16_elem(r.b, e);
+    }
+    if (p.k_norm_w) {
+      float ss = 0.f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) ss += xl[e] * xl[e] + xh[e] * xh[e];
+      ss += __shfl_xor(ss, 1, 8);
+      ss += __shfl_xor(ss, 2, 8);
+      ss += __shfl_xor(ss, 4, 8);
+      const float rr = 1.0f / sqrtf(ss * (1.0f / kHeadDim) + p.eps);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        xl[e] *= rr * sm.gk[8 * c + e];
+        xh[e] *= rr * sm.gk[64 + 8 * c + e];
+      }
+    }
+    if (rope) {
+      const double kpos = pos0 + (double)(kt * BN + lkey);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        float cs, sn;
+        rope_cos_sin_rev(kpos, sm.inv_rev[8 * c + e], cs, sn);
+        const float lo = xl[e], hi = xh[e];
+        xl[e] = lo * cs - hi * sn;
+        xh[e] = hi * cs + lo * sn;
+      }
+    }
+    uint32_t* krow = sm.kt[buf][lkey];
+    const int sw = kswz(lkey);
+    *(u32x4*)(krow + 4 * (c ^ sw)) = u32x4{pack_bf16x2(xl[0], xl[1]), pack_bf16x2(xl[2], xl[3]),
+                                          pack_bf16x2(xl[4], xl[5]), pack_bf16x2(xl[6], xl[7])};
+    *(u32x4*)(krow + 4 * ((8 + c) ^ sw)) = u32x4{pack_bf16x2(xh[0], xh[1]), pack_bf16x2(xh[2], xh[3]),
+                                                pack_bf16x2(xh[4], xh[5]), pack_bf16x2(xh[6], xh[7])};
+  } else {
+    const int v = u - kKUnits;
+    const int kp = v & 15, dc = v >> 4;
+    const int pos = vpos(2 * kp);   // keys 2kp, 2kp+1 stay adjacent
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {   // dims 8dc + 2j (lo halves) and 8dc + 2j + 1 (hi halves)
+      *(uint32_t*)&sm.vt[buf][8 * dc + 2 * j][pos] = pair_lo(r.a[j], r.b[j]);
+      *(uint32_t*)&sm.vt[buf][8 * dc + 2 * j + 1][pos] = pair_hi(r.a[j], r.b[j]);
+    }
+  }
+}
+
+// UNITS: staging units per thread per tile (1 when the workgroup has >= 8 waves, else 2).
+template <int UNITS>
+__global__ __launch_bounds__(kMaxThreads) void prefill_kernel(const PrefillParams p) {
   __shared__ PrefillSmem sm;
 
-  // XCD-aware workgroup order: consecutive workgroup ids are dealt round-robin
-  // to the 8 XCDs, so when the (sequence, KV head) groups divide evenly every
-  // group's workgroups share one XCD and its K/V tiles stay in that XCD's L2.
-  // Within a group: heaviest (last) query tile first, the G query heads of a
-  // tile adjacent.
-  const int G = p.group;
-  const int per_group = p.n_qtiles * G;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int nthreads = blockDim.x;
+  const int n32 = lane & 31, hf = lane >> 5;
+  const int G = p.group, HC = p.heads_per_wg, BQ = p.block_q;
+  const int tb_per_head = BQ / 32;
+
+  // ---- workgroup -> (sequence, KV head, head chunk, query block)
+  const int nchunks = G / HC;
+  const int per_group = p.n_qblocks * nchunks;
   const int groups = p.batch * p.num_kv_heads;
   const int bid = blockIdx.x;
   int grp, w;
-  if (groups % kXcds == 0) {
+  if (groups % kXcds == 0) {   // XCD-aware: a (sequence, KV head) group's workgroups share one XCD
     const int slot = bid / kXcds;
     grp = bid % kXcds + kXcds * (slot / per_group);
     w = slot % per_group;
@@ -67,277 +180,212 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(const PrefillParam
     w = bid % per_group;
   }
   const int b = grp / p.num_kv_heads, h = grp % p.num_kv_heads;
-  const int qt = p.n_qtiles - 1 - w / G;
-  const int hq = h * G + w % G;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int n32 = lane & 31, hf = lane >> 5;
+  const int qb = p.n_qblocks - 1 - w / nchunks;    // heaviest block first
+  const int hc = w % nchunks;
 
   int n = p.seq_lens[b];
   n = n < 0 ? 0 : (n > p.max_seq ? p.max_seq : n);
-  const int qs = qt * BM;
-  if (qs >= n) return;
-  const int qe = min(qs + BM, n);
-  const int kend = p.causal ? qe : n;            // keys [0, kend) can be visible
+  const int q0 = qb * BQ;
+  if (q0 >= n) return;
+  const int qe = min(q0 + BQ, n);
+  const int kend = p.causal ? qe : n;              // keys [0, kend) can be visible
   const int ntiles = (kend + BN - 1) / BN;
   const bool rope = p.rope_theta > 0.0;
   const double pos0 = (double)p.positions[b];
 
+  // this wave's rows: head hq, tokens [wq0, wq0 + 32)
+  const int hq = h * G + hc * HC + wave / tb_per_head;
+  const int wq0 = q0 + 32 * (wave % tb_per_head);
+  const int qrow = wq0 + n32;
+  const bool wave_live = wq0 < n;
+
   // ---- tables: RoPE inverse frequencies (revolutions) and key norm weight
   if (tid < 64 && rope) sm.inv_rev[tid] = pow(p.rope_theta, -2.0 * (double)tid / (double)kHeadDim) * 0.15915494309189535;
   if (tid < kHeadDim) sm.gk[tid] = p.k_norm_w ? bf16lo(((const uint16_t*)p.k_norm_w)[tid]) : 1.0f;
-  __syncthreads();
 
-  // ---- query prologue: lane (n32, hf) owns row qs + 32*wave + n32, dims
-  //      [32hf, 32hf+32) and [64+32hf, 64+32hf+32)
-  const int qrow = qs + 32 * wave + n32;
+  Staging st;
+  st.kslab = (const uint8_t*)p.k + ((int64_t)b * p.k_sb + (int64_t)h * p.k_sh) * 2;
+  st.vslab = (const uint8_t*)p.v + ((int64_t)b * p.v_sb + (int64_t)h * p.v_sh) * 2;
+  st.kss = (uint32_t)(p.k_ss * 2);
+  st.vss = (uint32_t)(p.v_ss * 2);
+  st.n = n;
+  // staging units of this thread: tid and tid + nthreads (when below 512)
+  const int u0 = tid, u1 = tid + nthreads;
+  const bool has0 = u0 < kUnits, has1 = UNITS > 1 && u1 < kUnits;
+  Raw r0, r1;
+
+  // ---- fetch tile 0, run the query prologue, stage tile 0, fetch tile 1
+  if (has0) fetch_unit(r0, st, 0, u0);
+  if (has1) fetch_unit(r1, st, 0, u1);
+
+  // query prologue: lane (n32, hf) owns row qrow of head hq, dims [32hf, 32hf+32) and [64+32hf, 64+32hf+32)
   bf16x8 qf[8];
   {
-    float xl[32], xh[32];
+    // raw row halves kept packed (16 registers each), unpacked chunk by chunk
+    u32x4 qlo[4], qhi[4];
     if (qrow < n) {
       const uint16_t* row = (const uint16_t*)p.q + ((int64_t)b * p.q_sb + (int64_t)hq * p.q_sh + (int64_t)qrow * p.q_ss);
-      #pragma unroll
+#pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const u32x4 lo = *(const u32x4*)(row + 32 * hf + 8 * j);
-        const u32x4 hi = *(const u32x4*)(row + 64 + 32 * hf + 8 * j);
-        #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          xl[8 * j + e] = bf16_elem(lo, e);
-          xh[8 * j + e] = bf16_elem(hi, e);
-        }
+        qlo[j] = *(const u32x4*)(row + 32 * hf + 8 * j);
+        qhi[j] = *(const u32x4*)(row + 64 + 32 * hf + 8 * j);
       }
     } else {
-      #pragma unroll
-      for (int e = 0; e < 32; ++e) xl[e] = xh[e] = 0.f;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) qlo[j] = qhi[j] = u32x4{0, 0, 0, 0};
     }
+    float r = 1.0f;
     if (p.q_norm_w) {
       float ss = 0.f;
-      #pragma unroll
-      for (int e = 0; e < 32; ++e) ss += xl[e] * xl[e] + xh[e] * xh[e];
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float a = bf16_elem(qlo[j], e), c = bf16_elem(qhi[j], e);
+          ss += a * a + c * c;
+        }
       ss += __shfl_xor(ss, 32, 64);
-      const float r = 1.0f / sqrtf(ss * (1.0f / kHeadDim) + p.eps);
-      const uint16_t* g = (const uint16_t*)p.q_norm_w;
-      #pragma unroll
-      for (int e = 0; e < 32; ++e) {
-        xl[e] *= r * bf16lo(g[32 * hf + e]);
-        xh[e] *= r * bf16lo(g[64 + 32 * hf + e]);
-      }
+      r = 1.0f / sqrtf(ss * (1.0f / kHeadDim) + p.eps);
     }
-    if (rope) {
-      const double qpos = pos0 + (double)qrow;
-      #pragma unroll
-      for (int e = 0; e < 32; ++e) {
-        float c, s;
-        rope_cos_sin_rev(qpos, sm.inv_rev[32 * hf + e], c, s);
-        const float lo = xl[e], hi = xh[e];
-        xl[e] = lo * c - hi * s;
-        xh[e] = hi * c + lo * s;
-      }
-    }
-    #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-      qf[kk] = as_bf16x8(u32x4{pack_bf16x2(xl[8 * kk], xl[8 * kk + 1]), pack_bf16x2(xl[8 * kk + 2], xl[8 * kk + 3]),
-                               pack_bf16x2(xl[8 * kk + 4], xl[8 * kk + 5]), pack_bf16x2(xl[8 * kk + 6], xl[8 * kk + 7])});
-      qf[4 + kk] = as_bf16x8(u32x4{pack_bf16x2(xh[8 * kk], xh[8 * kk + 1]), pack_bf16x2(xh[8 * kk + 2], xh[8 * kk + 3]),
-                                   pack_bf16x2(xh[8 * kk + 4], xh[8 * kk + 5]), pack_bf16x2(xh[8 * kk + 6], xh[8 * kk + 7])});
-    }
-  }
-
-  // ---- per-thread K/V tile loading roles
-  const int lkey = tid >> 2, part = tid & 3;     // key prologue: 16 pairs (i, i+64), i in [16 part, 16 part + 16)
-  const uint16_t* kslab = (const uint16_t*)p.k + ((int64_t)b * p.k_sb + (int64_t)h * p.k_sh);
-  const uint16_t* vslab = (const uint16_t*)p.v + ((int64_t)b * p.v_sb + (int64_t)h * p.v_sh);
-  struct Raw { u32x4 k0, k1, k2, k3, v0, v1, v2, v3; } raw;
-#define GQA_FETCH_TILE(KT)                                                       \
-  do {                                                                           \
-    const int key_ = (KT) * BN + lkey;                                           \
-    if (key_ < n) {                                                              \
-      const uint16_t* kr_ = kslab + (int64_t)key_ * p.k_ss + 16 * part;         \
-      const uint16_t* vr_ = vslab + (int64_t)key_ * p.v_ss + 32 * part;         \
-      raw.k0 = *(const u32x4*)(kr_);                                             \
-      raw.k1 = *(const u32x4*)(kr_ + 8);                                         \
-      raw.k2 = *(const u32x4*)(kr_ + 64);                                        \
-      raw.k3 = *(const u32x4*)(kr_ + 72);                                        \
-      raw.v0 = *(const u32x4*)(vr_);                                             \
-      raw.v1 = *(const u32x4*)(vr_ + 8);                                         \
-      raw.v2 = *(const u32x4*)(vr_ + 16);                                        \
-      raw.v3 = *(const u32x4*)(vr_ + 24);                                        \
-    } else {                                                                     \
-      raw.k0 = raw.k1 = raw.k2 = raw.k3 = u32x4{0, 0, 0, 0};                     \
-      raw.v0 = raw.v1 = raw.v2 = raw.v3 = u32x4{0, 0, 0, 0};                     \
-    }                                                                            \
-  } while (0)
-
-  f32x16 o[4];
-  #pragma unroll
-  for (int T = 0; T < 4; ++T)
-    #pragma unroll
-    for (int i = 0; i < 16; ++i) o[T][i] = 0.f;
-  float m_run = -INFINITY, l_run = 0.f;
-  const int wq0 = qs + 32 * wave;                 // this wave's first query
-  const bool wave_live = wq0 < n;
-
-  GQA_FETCH_TILE(0);
-  for (int kt = 0; kt < ntiles; ++kt) {
-    // ---- key prologue on the fetched rows -> K' (bf16) and V into LDS
-    {
-      float xl[16], xh[16];
-      #pragma unroll
+    __syncthreads();   // the tables are written
+    const double qpos = pos0 + (double)qrow;
+    const uint16_t* g = (const uint16_t*)p.q_norm_w;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      float xl[8], xh[8];
+#pragma unroll
       for (int e = 0; e < 8; ++e) {
-        xl[e] = bf16_elem(raw.k0, e);
-        xl[8 + e] = bf16_elem(raw.k1, e);
-        xh[e] = bf16_elem(raw.k2, e);
-        xh[8 + e] = bf16_elem(raw.k3, e);
+        xl[e] = bf16_elem(qlo[j], e);
+        xh[e] = bf16_elem(qhi[j], e);
       }
-      if (p.k_norm_w) {
-        float ss = 0.f;
-        #pragma unroll
-        for (int e = 0; e < 16; ++e) ss += xl[e] * xl[e] + xh[e] * xh[e];
-        ss += __shfl_xor(ss, 1, 4);
-        ss += __shfl_xor(ss, 2, 4);
-        const float r = 1.0f / sqrtf(ss * (1.0f / kHeadDim) + p.eps);
-        #pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          xl[e] *= r * sm.gk[16 * part + e];
-          xh[e] *= r * sm.gk[64 + 16 * part + e];
+      if (g) {
+        const u32x4 glo = *(const u32x4*)(g + 32 * hf + 8 * j);
+        const u32x4 ghi = *(const u32x4*)(g + 64 + 32 * hf + 8 * j);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          xl[e] *= r * bf16_elem(glo, e);
+          xh[e] *= r * bf16_elem(ghi, e);
         }
       }
       if (rope) {
-        const double kpos = pos0 + (double)(kt * BN + lkey);
-        #pragma unroll
-        for (int e = 0; e < 16; ++e) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
           float c, s;
-          rope_cos_sin_rev(kpos, sm.inv_rev[16 * part + e], c, s);
+          rope_cos_sin_rev(qpos, sm.inv_rev[32 * hf + 8 * j + e], c, s);
           const float lo = xl[e], hi = xh[e];
           xl[e] = lo * c - hi * s;
           xh[e] = hi * c + lo * s;
         }
       }
-      const int sw = lkey & 15;
-      uint32_t* krow = sm.kt[lkey];
-      // logical chunks 2part, 2part+1 (lo half) and 8+2part, 9+2part (hi half)
-      #pragma unroll
-      for (int cc = 0; cc < 2; ++cc) {
-        *(u32x4*)(krow + 4 * ((2 * part + cc) ^ sw)) =
-            u32x4{pack_bf16x2(xl[8 * cc], xl[8 * cc + 1]), pack_bf16x2(xl[8 * cc + 2], xl[8 * cc + 3]),
-                  pack_bf16x2(xl[8 * cc + 4], xl[8 * cc + 5]), pack_bf16x2(xl[8 * cc + 6], xl[8 * cc + 7])};
-        *(u32x4*)(krow + 4 * ((8 + 2 * part + cc) ^ sw)) =
-            u32x4{pack_bf16x2(xh[8 * cc], xh[8 * cc + 1]), pack_bf16x2(xh[8 * cc + 2], xh[8 * cc + 3]),
-                  pack_bf16x2(xh[8 * cc + 4], xh[8 * cc + 5]), pack_bf16x2(xh[8 * cc + 6], xh[8 * cc + 7])};
-      }
-      uint32_t* vrow = sm.vt[lkey] + 16 * part;
-      *(u32x4*)(vrow) = raw.v0;
-      *(u32x4*)(vrow + 4) = raw.v1;
-      *(u32x4*)(vrow + 8) = raw.v2;
-      *(u32x4*)(vrow + 12) = raw.v3;
+      qf[j] = as_bf16x8(u32x4{pack_bf16x2(xl[0], xl[1]), pack_bf16x2(xl[2], xl[3]), pack_bf16x2(xl[4], xl[5]),
+                              pack_bf16x2(xl[6], xl[7])});
+      qf[4 + j] = as_bf16x8(u32x4{pack_bf16x2(xh[0], xh[1]), pack_bf16x2(xh[2], xh[3]), pack_bf16x2(xh[4], xh[5]),
+                                  pack_bf16x2(xh[6], xh[7])});
     }
-    __syncthreads();
-    if (kt + 1 < ntiles) GQA_FETCH_TILE(kt + 1);
+  }
+  if (has0) stage_unit(sm, r0, p, rope, pos0, 0, u0, 0);
+  if (has1) stage_unit(sm, r1, p, rope, pos0, 0, u1, 0);
+  if (ntiles > 1) {
+    if (has0) fetch_unit(r0, st, 1, u0);
+    if (has1) fetch_unit(r1, st, 1, u1);
+  }
+  __syncthreads();   // tile 0 staged
 
+  f32x16 o[4];
+#pragma unroll
+  for (int T = 0; T < 4; ++T)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) o[T][i] = 0.f;
+  float m_run = -INFINITY, l_run = 0.f;
+
+  for (int kt = 0; kt < ntiles; ++kt) {
+    const int buf = kt & 1;
+    // ---- attention on tile kt for this wave's 32 query rows
     const int ks = kt * BN;
-    // tile classification for this wave's 32 queries [wq0, wq0 + 32)
     const bool future = p.causal && ks > wq0 + 31;
     if (wave_live && !future) {
-      const bool need_mask = (p.causal && ks + BN - 1 > wq0) || ks + BN > n;
-      // S^T for two 32-key subtiles: sacc[u][i] = S[key ks + 32u + 8(i/4) + 4hf + i%4][query wq0 + n32]
-      f32x16 sacc[2];
-      #pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        #pragma unroll
-        for (int i = 0; i < 16; ++i) sacc[u][i] = 0.f;
-        const int krow = 32 * u + n32;
-        const uint32_t* kr = sm.kt[krow];
-        const int sw = krow & 15;
-        #pragma unroll
+      // sacc[i] = S[key ks + 8(i/4) + 4hf + i%4][query wq0 + n32] (raw, unscaled)
+      f32x16 sacc;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) sacc[i] = 0.f;
+      {
+        const uint32_t* kr = sm.kt[buf][n32];
+        const int sw = kswz(n32);
+#pragma unroll
         for (int kk = 0; kk < 8; ++kk) {
           const u32x4 a = *(const u32x4*)(kr + 4 * (qk_chunk(kk, hf) ^ sw));
-          sacc[u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), qf[kk], sacc[u], 0, 0, 0);
+          sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), qf[kk], sacc, 0, 0, 0);
         }
       }
-      float mx = -INFINITY;
-      #pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          float s = sacc[u][i] * p.scale_log2;
-          if (need_mask) {
-            const int key = ks + 32 * u + 8 * (i >> 2) + 4 * hf + (i & 3);
-            if (key >= n || (p.causal && key > qrow)) s = -INFINITY;
-          }
-          sacc[u][i] = s;
-          mx = fmaxf(mx, s);
-        }
+      if ((p.causal && ks + BN - 1 > wq0) || ks + BN > n) {   // wave-uniform: diagonal or ragged tile
+        // key ks + off is visible iff off < lim (off = 8(i/4) + 4hf + i%4)
+        const int lim = (p.causal ? min(n, qrow + 1) : n) - ks - 4 * hf;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) sacc[i] = (8 * (i >> 2) + (i & 3) < lim) ? sacc[i] : -INFINITY;
       }
-      mx = wave_max_xor(mx, 32);
-      const float m_new = fmaxf(m_run, mx);
-      const float corr = fast_exp2(m_run - m_new);
+      float mx = fmaxf(sacc[0], sacc[1]);
+#pragma unroll
+      for (int i = 2; i < 16; i += 2) mx = fmaxf(mx, fmaxf(sacc[i], sacc[i + 1]));
+      mx = wave_max_xor(mx, 32) * p.scale_log2;       // row max in log2 units
+      // lazy rescale: keep the running max until some row's max grows by more
+      // than kLazyRescale; exponents stay <= 2^kLazyRescale meanwhile
+      if (__any(mx > m_run + kLazyRescale)) {
+        const float m_new = fmaxf(m_run, mx);
+        const float corr = fast_exp2(m_run - m_new);   // 0 on the first tile (m = -inf)
+        l_run *= corr;
+#pragma unroll
+        for (int T = 0; T < 4; ++T) o[T] *= corr;
+        m_run = m_new;
+      }
       float ps = 0.f;
-      #pragma unroll
-      for (int u = 0; u < 2; ++u)
-        #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const float e = fast_exp2(sacc[u][i] - m_new);
-          sacc[u][i] = e;
-          ps += e;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const float e = fast_exp2(fmaf(sacc[i], p.scale_log2, -m_run));
+        sacc[i] = e;
+        ps += e;
+      }
+      l_run += ps;
+      // O^T += V^T P^T: MFMA e takes keys ks + 16e + {4hf + t, 8 + 4hf + t}, t < 4,
+      // stored contiguously at V^T positions 16e + 8hf .. 16e + 8hf + 7
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        const u32x4 pf = {pack_bf16x2(sacc[8 * e + 0], sacc[8 * e + 1]), pack_bf16x2(sacc[8 * e + 2], sacc[8 * e + 3]),
+                          pack_bf16x2(sacc[8 * e + 4], sacc[8 * e + 5]), pack_bf16x2(sacc[8 * e + 6], sacc[8 * e + 7])};
+#pragma unroll
+        for (int T = 0; T < 4; ++T) {
+          const u32x4 a = *(const u32x4*)&sm.vt[buf][32 * T + n32][16 * e + 8 * hf];
+          o[T] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), as_bf16x8(pf), o[T], 0, 0, 0);
         }
-      l_run = l_run * corr + ps;
-      m_run = m_new;
-      #pragma unroll
-      for (int T = 0; T < 4; ++T) o[T] *= corr;
-
-      // O^T += V^T P^T: MFMA (u, e) takes keys ks + 32u + 16e + {4hf + t, 8 + 4hf + t}, t < 4
-      #pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        #pragma unroll
-        for (int e = 0; e < 2; ++e) {
-          const u32x4 pf = {pack_bf16x2(sacc[u][8 * e + 0], sacc[u][8 * e + 1]), pack_bf16x2(sacc[u][8 * e + 2], sacc[u][8 * e + 3]),
-                            pack_bf16x2(sacc[u][8 * e + 4], sacc[u][8 * e + 5]), pack_bf16x2(sacc[u][8 * e + 6], sacc[u][8 * e + 7])};
-          #pragma unroll
-          for (int w = 0; w < 2; ++w) {          // dword w of each row: dims 4*n32 + 2w, 4*n32 + 2w + 1
-            uint32_t r[8];
-            #pragma unroll
-            for (int t = 0; t < 8; ++t) {
-              const int key = 32 * u + 16 * e + 4 * hf + (t < 4 ? t : 4 + t);
-              r[t] = sm.vt[key][2 * n32 + w];
-            }
-            u32x4 a0, a1;
-            #pragma unroll
-            for (int uu = 0; uu < 4; ++uu) {
-              a0[uu] = pair_lo(r[2 * uu], r[2 * uu + 1]);
-              a1[uu] = pair_hi(r[2 * uu], r[2 * uu + 1]);
-            }
-            o[2 * w] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a0), as_bf16x8(pf), o[2 * w], 0, 0, 0);
-            o[2 * w + 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a1), as_bf16x8(pf), o[2 * w + 1], 0, 0, 0);
-          }
-        }
+      }
+    }
+    // ---- stage tile kt+1 into the other buffer (nobody reads it since the last
+    //      barrier); placed after the P V MFMAs are issued so that this VALU
+    //      work overlaps them
+    if (kt + 1 < ntiles) {
+      if (has0) stage_unit(sm, r0, p, rope, pos0, kt + 1, u0, buf ^ 1);
+      if (has1) stage_unit(sm, r1, p, rope, pos0, kt + 1, u1, buf ^ 1);
+      if (kt + 2 < ntiles) {
+        if (has0) fetch_unit(r0, st, kt + 2, u0);
+        if (has1) fetch_unit(r1, st, kt + 2, u1);
       }
     }
     __syncthreads();
   }
 
-#undef GQA_FETCH_TILE
-
   // ---- epilogue: O / l for this lane's query row
-  if (qrow >= n) return;
+  if (!wave_live || qrow >= n) return;
   l_run = wave_sum_xor(l_run, 32);
   const float inv = 1.0f / l_run;
   uint8_t* orow = (uint8_t*)p.out + ((int64_t)b * p.o_sb + (int64_t)hq * p.o_sh + (int64_t)qrow * p.o_ss) * (p.out_bf16 ? 2 : 4);
-  // o[T][i] = O[query][dim 4*(8(i/4) + 4hf + i%4) + T]; per a = i/4 the 16 dims [32a + 16hf, 32a + 16hf + 16)
-  #pragma unroll
-  for (int a = 0; a < 4; ++a) {
-    float v[16];
-    #pragma unroll
-    for (int r = 0; r < 4; ++r)
-      #pragma unroll
-      for (int T = 0; T < 4; ++T) v[4 * r + T] = o[T][4 * a + r] * inv;
-    const int d0 = 32 * a + 16 * hf;
-    if (p.out_bf16) {
-      u32x4* dst = (u32x4*)(orow + 2 * d0);
-      dst[0] = u32x4{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]), pack_bf16x2(v[4], v[5]), pack_bf16x2(v[6], v[7])};
-      dst[1] = u32x4{pack_bf16x2(v[8], v[9]), pack_bf16x2(v[10], v[11]), pack_bf16x2(v[12], v[13]), pack_bf16x2(v[14], v[15])};
-    } else {
-      f32x4* dst = (f32x4*)(orow + 4 * d0);
-      #pragma unroll
-      for (int j = 0; j < 4; ++j) dst[j] = f32x4{v[4 * j], v[4 * j + 1], v[4 * j + 2], v[4 * j + 3]};
+  // o[T][4a + r] = O[query][dim 32T + 8a + 4hf + r]
+#pragma unroll
+  for (int T = 0; T < 4; ++T) {
+#pragma unroll
+    for (int a = 0; a < 4; ++a) {
+      const int d0 = 32 * T + 8 * a + 4 * hf;
+      const float v0 = o[T][4 * a] * inv, v1 = o[T][4 * a + 1] * inv, v2 = o[T][4 * a + 2] * inv, v3 = o[T][4 * a + 3] * inv;
+      if (p.out_bf16) *(u32x2*)(orow + 2 * d0) = u32x2{pack_bf16x2(v0, v1), pack_bf16x2(v2, v3)};
+      else *(f32x4*)(orow + 4 * d0) = f32x4{v0, v1, v2, v3};
     }
   }
 }
@@ -345,8 +393,10 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(const PrefillParam
 }  // namespace
 
 hipError_t launch_prefill(const PrefillParams& p, hipStream_t stream) {
-  const dim3 grid(p.n_qtiles * p.num_q_heads * p.batch);
-  hipLaunchKernelGGL(prefill_kernel, grid, dim3(kThreads), 0, stream, p);
+  const int waves = p.heads_per_wg * p.block_q / 32;
+  const dim3 grid(p.n_qblocks * (p.group / p.heads_per_wg) * p.num_kv_heads * p.batch);
+  if (64 * waves >= kUnits) hipLaunchKernelGGL(prefill_kernel<1>, grid, dim3(64 * waves), 0, stream, p);
+  else hipLaunchKernelGGL(prefill_kernel<2>, grid, dim3(64 * waves), 0, stream, p);
   return hipGetLastError();
 }
 
