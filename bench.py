@@ -180,7 +180,7 @@ def cpu_baseline(case_inputs, bytes_per_call, budget_s=12.0):
                       f"{per * 1e3:.1f} ms each, host cores available {cores})"}
 
 
-def prefill_case(torch, G, synth, np):
+def prefill_case(torch, G, synth, np, two_phase=True):
     """Device inputs and a call closure of the causal prefill workload."""
     pw = synth.QWEN3_PREFILL
     pin = synth.make_prefill(pw)
@@ -190,19 +190,22 @@ def prefill_case(torch, G, synth, np):
              sl=torch.from_numpy(pin["seq_lens"]).cuda(), pos=torch.from_numpy(pin["positions"]).cuda())
     t["out"] = torch.empty(t["q"].shape, dtype=torch.float32, device="cuda")
     desc = G.prefill_desc(t["q"], t["k"], t["v"], t["out"], True, pw.eps)
+    t["ws"] = G.prefill_workspace(desc, "cuda") if two_phase else None
+    ws_ptr = t["ws"].data_ptr() if two_phase else None
+    ws_bytes = t["ws"].numel() if two_phase else 0
 
     def call(i, stream):
         st = G.gqa_attn_prefill(desc, t["q"].data_ptr(), t["k"].data_ptr(), t["v"].data_ptr(), t["sl"].data_ptr(),
                                 t["pos"].data_ptr(), t["qw"].data_ptr(), t["kw"].data_ptr(), pw.rope_theta,
-                                t["out"].data_ptr(), stream)
+                                t["out"].data_ptr(), ws_ptr, ws_bytes, stream)
         assert st == G.GQA_OK
     return pw, pin, t, call
 
 
 def profile_calls(args, torch, G, synth, np):
     """Plain back-to-back calls of one workload, for profiler runs."""
-    if args.only == "prefill":
-        _, _, _, call = prefill_case(torch, G, synth, np)
+    if args.only in ("prefill", "prefill_fused"):
+        _, _, _, call = prefill_case(torch, G, synth, np, two_phase=args.only == "prefill")
     else:
         w = {"decode": synth.QWEN3_DECODE, "long": synth.LLAMA70B_LONG, "ragged": synth.QWEN3_RAGGED}[args.only or "decode"]
         call = DecodeCase(w, 1, torch, G, synth, exact_first=(w is synth.QWEN3_DECODE)).call
@@ -226,7 +229,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-extra", action="store_true", help="skip the prefill and long-context decode fields")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--only", choices=["decode", "prefill", "long", "ragged"],
+    ap.add_argument("--only", choices=["decode", "prefill", "prefill_fused", "long", "ragged"],
                     help="with --eager-calls: the workload to run")
     ap.add_argument("--eager-calls", type=int, default=0,
                     help="profiling mode: run this many plain calls of --only's workload (no timing, no JSON)")
@@ -286,19 +289,27 @@ def main():
         extra = {}
         pw, pin, pt_inputs, pcall = prefill_case(torch, G, synth, np)
         pk_steps = max(5, K // 10)
+        flops = prefill_flops(pin["seq_lens"], pw.num_q_heads)
         pt = graph_time_ms(torch, pcall, pk_steps, max(2, W // 10))
         us_p = 1000.0 * pt / pk_steps
         (ev_p,) = event_kernel_times(torch, [pcall], pk_steps)
-        flops = prefill_flops(pin["seq_lens"], pw.num_q_heads)
         tf = flops / (us_p * 1e-6) / 1e12
         tf_k = flops / (ev_p * 1e-6) / 1e12
-        extra["prefill"] = {"workload": pw.name, "us_per_call": round(us_p, 2), "tflops": round(tf, 2),
-                            "kernel_us": round(ev_p, 2),
-                            "roofline": {"bound": "mfma", "kernel": "prefill", "achieved": round(tf_k, 2),
-                                         "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+        extra["prefill"] = {"workload": pw.name, "path": "two_phase", "us_per_call": round(us_p, 2),
+                            "tflops": round(tf, 2), "call_us_events": round(ev_p, 2),
+                            "roofline": {"bound": "mfma", "kernel": "prefill (key prologue + attention)",
+                                         "achieved": round(tf_k, 2), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                                          "frac": round(tf_k / BF16_PEAK_TFLOPS, 4), "traffic": None,
                                          "algorithmic_flops": flops}}
-        log(f"[bench] prefill {us_p:.1f} us -> {tf:.1f} TFLOP/s (kernel {ev_p:.1f} us)")
+        log(f"[bench] prefill two-phase {us_p:.1f} us -> {tf:.1f} TFLOP/s (events {ev_p:.1f} us)")
+        del pt_inputs, pcall
+        torch.cuda.empty_cache()
+        _, _, pt_inputs, pcall = prefill_case(torch, G, synth, np, two_phase=False)
+        pt = graph_time_ms(torch, pcall, pk_steps, max(2, W // 10))
+        us_f = 1000.0 * pt / pk_steps
+        extra["prefill_single_kernel"] = {"workload": pw.name, "path": "single_kernel", "us_per_call": round(us_f, 2),
+                                          "tflops": round(flops / (us_f * 1e-6) / 1e12, 2)}
+        log(f"[bench] prefill single-kernel {us_f:.1f} us -> {flops / (us_f * 1e-6) / 1e12:.1f} TFLOP/s")
         del pt_inputs, pcall
         torch.cuda.empty_cache()
 

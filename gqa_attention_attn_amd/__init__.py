@@ -38,6 +38,7 @@ EXPORTS = (
     "gqa_attn_decode",
     "gqa_attn_decode_partition",
     "gqa_attn_decode_merge",
+    "gqa_attn_prefill_workspace_size",
     "gqa_attn_prefill",
 )
 
@@ -101,8 +102,10 @@ def lib() -> ctypes.CDLL:
         L.gqa_attn_decode_partition.restype = ctypes.c_int
         L.gqa_attn_decode_merge.argtypes = [ctypes.POINTER(GqaDecodeDesc), vp, vp, vp, ctypes.c_size_t, vp]
         L.gqa_attn_decode_merge.restype = ctypes.c_int
+        L.gqa_attn_prefill_workspace_size.argtypes = [ctypes.POINTER(GqaPrefillDesc), szp]
+        L.gqa_attn_prefill_workspace_size.restype = ctypes.c_int
         L.gqa_attn_prefill.argtypes = [ctypes.POINTER(GqaPrefillDesc), vp, vp, vp, vp, vp, vp, vp, ctypes.c_float,
-                                       vp, vp]
+                                       vp, vp, ctypes.c_size_t, vp]
         L.gqa_attn_prefill.restype = ctypes.c_int
         _lib = L
     return _lib
@@ -152,9 +155,18 @@ def gqa_attn_decode_merge(desc, seq_lens, out, workspace, workspace_bytes, strea
                                            workspace, int(workspace_bytes), stream))
 
 
-def gqa_attn_prefill(desc, q, k, v, seq_lens, positions, q_norm_w, k_norm_w, rope_theta, out, stream) -> int:
+def gqa_attn_prefill_workspace_size(desc: Optional[GqaPrefillDesc]) -> Tuple[int, int]:
+    """Returns (status, bytes)."""
+    b = ctypes.c_size_t(0)
+    st = lib().gqa_attn_prefill_workspace_size(ctypes.byref(desc) if desc is not None else None, ctypes.byref(b))
+    return int(st), int(b.value)
+
+
+def gqa_attn_prefill(desc, q, k, v, seq_lens, positions, q_norm_w, k_norm_w, rope_theta, out, workspace,
+                     workspace_bytes, stream) -> int:
     return int(lib().gqa_attn_prefill(ctypes.byref(desc) if desc is not None else None, q, k, v, seq_lens, positions,
-                                      q_norm_w, k_norm_w, float(rope_theta), out, stream))
+                                      q_norm_w, k_norm_w, float(rope_theta), out, workspace, int(workspace_bytes),
+                                      stream))
 
 
 # ----------------------------------------------------------------- torch conveniences
@@ -236,15 +248,30 @@ def decode(q, k_cache, v_cache, seq_lens, positions, q_norm_w=None, k_norm_w=Non
     return out
 
 
+def prefill_workspace(desc: GqaPrefillDesc, device) -> "object":
+    """Allocate (with torch) the optional prefill workspace."""
+    import torch
+    st, nbytes = gqa_attn_prefill_workspace_size(desc)
+    if st != GQA_OK:
+        raise GqaError(st, "gqa_attn_prefill_workspace_size")
+    return torch.empty(nbytes, dtype=torch.uint8, device=device)
+
+
 def prefill(q, k, v, seq_lens, positions, q_norm_w=None, k_norm_w=None, rope_theta: float = 0.0, out=None,
-            causal: bool = True, eps: float = 1e-6, scale: float = 0.0, out_dtype=None, stream=None):
-    """gqa_attn_prefill on torch tensors (device memory); returns out."""
+            causal: bool = True, eps: float = 1e-6, scale: float = 0.0, out_dtype=None, workspace="auto",
+            stream=None):
+    """gqa_attn_prefill on torch tensors (device memory); returns out.
+    workspace: "auto" allocates one (two-phase path), None selects the
+    single-kernel path, or a uint8 device tensor."""
     import torch
     if out is None:
         out = torch.empty(q.shape, dtype=out_dtype or torch.float32, device=q.device)
     desc = prefill_desc(q, k, v, out, causal, eps, scale)
+    if isinstance(workspace, str):
+        workspace = prefill_workspace(desc, q.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     st = gqa_attn_prefill(desc, _ptr(q), _ptr(k), _ptr(v), _ptr(seq_lens), _ptr(positions), _ptr(q_norm_w),
-                          _ptr(k_norm_w), rope_theta, _ptr(out), _stream_ptr(stream))
+                          _ptr(k_norm_w), rope_theta, _ptr(out), _ptr(workspace), ws_bytes, _stream_ptr(stream))
     if st != GQA_OK:
         raise GqaError(st, "gqa_attn_prefill")
     return out

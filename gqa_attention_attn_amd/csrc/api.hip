@@ -250,9 +250,18 @@ gqa_status gqa_attn_decode(const gqa_decode_desc* d, const void* q, const void* 
   return gqa::launch_decode_merge(p, stream) == hipSuccess ? GQA_OK : GQA_ERR_HIP;
 }
 
+gqa_status gqa_attn_prefill_workspace_size(const gqa_prefill_desc* desc, size_t* bytes) {
+  if (bytes == nullptr) return GQA_ERR_NULL;
+  const gqa_status st = check_prefill_desc(desc);
+  if (st != GQA_OK) return st;
+  *bytes = gqa::prefill_workspace_bytes(desc->batch, desc->num_kv_heads, desc->max_seq);
+  return GQA_OK;
+}
+
 gqa_status gqa_attn_prefill(const gqa_prefill_desc* d, const void* q, const void* k, const void* v,
                             const int32_t* seq_lens, const int32_t* positions, const void* q_norm_w,
-                            const void* k_norm_w, float rope_theta, void* out, hipStream_t stream) {
+                            const void* k_norm_w, float rope_theta, void* out, void* workspace,
+                            size_t workspace_bytes, hipStream_t stream) {
   gqa_status st = check_prefill_desc(d);
   if (st != GQA_OK) return st;
   if (q == nullptr || k == nullptr || v == nullptr || seq_lens == nullptr || positions == nullptr || out == nullptr)
@@ -260,6 +269,10 @@ gqa_status gqa_attn_prefill(const gqa_prefill_desc* d, const void* q, const void
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) || !aligned16(q_norm_w) ||
       !aligned16(k_norm_w) || ((uintptr_t)seq_lens & 3u) || ((uintptr_t)positions & 3u))
     return GQA_ERR_ALIGN;
+  if (workspace != nullptr) {
+    if (workspace_bytes < gqa::prefill_workspace_bytes(d->batch, d->num_kv_heads, d->max_seq)) return GQA_ERR_WORKSPACE;
+    if (((uintptr_t)workspace & 255u) != 0) return GQA_ERR_ALIGN;
+  }
   gqa::PrefillParams p{};
   p.q = q;
   p.k = k;
@@ -293,7 +306,9 @@ gqa_status gqa_attn_prefill(const gqa_prefill_desc* d, const void* q, const void
   p.eps = d->eps;
   p.scale_log2 = resolve_scale_log2(d->scale);
   p.rope_theta = rope_theta > 0.f ? (double)rope_theta : 0.0;
-  return gqa::launch_prefill(p, stream) == hipSuccess ? GQA_OK : GQA_ERR_HIP;
+  const hipError_t e = workspace != nullptr ? gqa::launch_prefill_phased(p, workspace, stream)
+                                            : gqa::launch_prefill_fused(p, stream);
+  return e == hipSuccess ? GQA_OK : GQA_ERR_HIP;
 }
 
 }  // extern "C"

@@ -62,7 +62,9 @@ struct PrefillParams {
 // Launchers (return the hipGetLastError() of their launches).
 hipError_t launch_decode_partition(const DecodeParams& p, bool in_bf16, hipStream_t stream);
 hipError_t launch_decode_merge(const DecodeParams& p, hipStream_t stream);
-hipError_t launch_prefill(const PrefillParams& p, hipStream_t stream);
+hipError_t launch_prefill_fused(const PrefillParams& p, hipStream_t stream);
+hipError_t launch_prefill_phased(const PrefillParams& p, void* workspace, hipStream_t stream);
+size_t prefill_workspace_bytes(int batch, int num_kv_heads, int max_seq);
 
 // Prefill workgroups hold HC * BQ / 32 waves of 32 query rows, at most this many.
 constexpr int kPrefillMaxWaves = 10;

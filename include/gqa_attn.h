@@ -192,6 +192,12 @@ gqa_status gqa_attn_decode_merge(const gqa_decode_desc* desc, const int32_t* seq
                                  size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * Bytes of the optional prefill workspace (host only, no HIP call):
+ * B * Hkv * max_seq * 128 * 2 (one bf16 K' row per key).
+ */
+gqa_status gqa_attn_prefill_workspace_size(const gqa_prefill_desc* desc, size_t* bytes);
+
+/*
  * Grouped-query causal prefill attention with the fused QK-norm + RoPE
  * prologue (ADR-0060 sections 3 and 5.4; "Qwen3-14B Optimization" 2.1).
  *
@@ -205,11 +211,21 @@ gqa_status gqa_attn_decode_merge(const gqa_decode_desc* desc, const int32_t* seq
  * q: [B, Hq, max_seq, 128]; k, v: [B, Hkv, max_seq, 128]; out: [B, Hq,
  * max_seq, 128].  in_dtype must be GQA_BF16 (QK^T and P V run on bf16 MFMA
  * with f32 accumulation; q', k' and P are rounded to bf16 before the MFMA).
- * Errors: as gqa_attn_decode, without GQA_ERR_WORKSPACE.
+ *
+ * workspace: optional.  With a device buffer of at least
+ * gqa_attn_prefill_workspace_size bytes (256-byte aligned; contents on entry
+ * ignored) the call runs in two phases on `stream`, the GPU form of the fused
+ * stage's rope phase and attention phase separated by a grid-wide barrier:
+ * every key row's prologue is computed once into the workspace, then the
+ * attention kernel applies the query prologue as it loads query tiles.  With
+ * workspace == NULL a single kernel recomputes the key prologue for every
+ * (query block, key tile) pair (no workspace, more arithmetic).
+ * Errors: as gqa_attn_decode.
  */
 gqa_status gqa_attn_prefill(const gqa_prefill_desc* desc, const void* q, const void* k, const void* v,
                             const int32_t* seq_lens, const int32_t* positions, const void* q_norm_w,
-                            const void* k_norm_w, float rope_theta, void* out, hipStream_t stream);
+                            const void* k_norm_w, float rope_theta, void* out, void* workspace,
+                            size_t workspace_bytes, hipStream_t stream);
 
 #ifdef __cplusplus
 }

@@ -147,8 +147,8 @@ def call_decode(d, q=FAKE, k=FAKE, v=FAKE, sl=FAKE, pos=FAKE, qw=NULL, kw=NULL, 
     return G.gqa_attn_decode(d, q, k, v, sl, pos, qw, kw, 1e6, out, ws, wsb, None)
 
 
-def call_prefill(d, q=FAKE, k=FAKE, v=FAKE, sl=FAKE, pos=FAKE, qw=NULL, kw=NULL, out=FAKE):
-    return G.gqa_attn_prefill(d, q, k, v, sl, pos, qw, kw, 1e6, out, None)
+def call_prefill(d, q=FAKE, k=FAKE, v=FAKE, sl=FAKE, pos=FAKE, qw=NULL, kw=NULL, out=FAKE, ws=NULL, wsb=0):
+    return G.gqa_attn_prefill(d, q, k, v, sl, pos, qw, kw, 1e6, out, ws, wsb, None)
 
 
 @pytest.mark.parametrize("kw,status", [
@@ -249,3 +249,13 @@ def test_decode_cache_slab_limit():
               v_stride_h=(1 << 20) * 128, k_stride_b=8 * (1 << 20) * 4096, v_stride_b=8 * (1 << 20) * 128,
               kv_split_tokens=4096)
     assert call_decode(d) == G.GQA_ERR_UNSUPPORTED
+
+
+def test_prefill_workspace_size_and_errors():
+    d = pdesc()
+    st, need = G.gqa_attn_prefill_workspace_size(d)
+    assert st == G.GQA_OK and need == 1 * 8 * 256 * 128 * 2
+    assert G.gqa_attn_prefill_workspace_size(None)[0] == G.GQA_ERR_NULL
+    assert G.gqa_attn_prefill_workspace_size(pdesc(head_dim=64))[0] == G.GQA_ERR_UNSUPPORTED
+    assert call_prefill(d, ws=FAKE, wsb=need - 1) == G.GQA_ERR_WORKSPACE
+    assert call_prefill(d, ws=FAKE + 16, wsb=need) == G.GQA_ERR_ALIGN

@@ -23,11 +23,17 @@ def gpu_inputs(inp):
                 kw=dev(inp["k_norm_w"], bf), sl=ints(inp["seq_lens"]), pos=ints(inp["positions"]))
 
 
-def run(inp, out_dtype=None, g=None, out=None):
+PATHS = ["two_phase", "single_kernel"]
+
+
+def run(inp, out_dtype=None, g=None, out=None, path="two_phase"):
+    """path: two_phase (workspace given: key prologue once, then attention) or
+    single_kernel (no workspace: key prologue per key tile)."""
     torch = require_gpu()
     g = g or gpu_inputs(inp)
     o = G.prefill(g["q"], g["k"], g["v"], g["sl"], g["pos"], g["qw"], g["kw"], inp["rope_theta"], out=out,
-                  causal=inp["causal"], eps=inp["eps"], out_dtype=out_dtype or torch.float32)
+                  causal=inp["causal"], eps=inp["eps"], out_dtype=out_dtype or torch.float32,
+                  workspace="auto" if path == "two_phase" else None)
     torch.cuda.synchronize()
     return o
 
@@ -58,34 +64,38 @@ def valid_rows(out, inp):
     return o
 
 
+@pytest.mark.parametrize("path", PATHS)
 @pytest.mark.parametrize("causal", [True, False])
-def test_small_ragged_multi_tile(causal):
+def test_small_ragged_multi_tile(causal, path):
     inp = small(B=2, Hq=10, Hkv=2, S=300, lens=[300, 129], causal=causal, p0=0)
     inp["positions"] = np.array([0, 1000], dtype=np.int32)
-    log(f"case small prefill causal={causal}")
-    out = run(inp).cpu().numpy()
-    compare(valid_rows(out, inp), ref(inp), ATOL_BF16, f"prefill causal={causal}")
+    log(f"case small prefill causal={causal} path={path}")
+    out = run(inp, path=path).cpu().numpy()
+    compare(valid_rows(out, inp), ref(inp), ATOL_BF16, f"prefill causal={causal} {path}")
 
 
-@pytest.mark.parametrize("Hq,Hkv", [(8, 8), (16, 2), (8, 1)])
-def test_group_sizes(Hq, Hkv):
+@pytest.mark.parametrize("path", PATHS)
+@pytest.mark.parametrize("Hq,Hkv", [(8, 8), (16, 2), (8, 1), (12, 4), (14, 2)])
+def test_group_sizes(Hq, Hkv, path):
     inp = small(B=1, Hq=Hq, Hkv=Hkv, S=200, lens=[200])
-    out = run(inp).cpu().numpy()
-    compare(valid_rows(out, inp), ref(inp), ATOL_BF16, f"Hq={Hq} Hkv={Hkv}")
+    out = run(inp, path=path).cpu().numpy()
+    compare(valid_rows(out, inp), ref(inp), ATOL_BF16, f"Hq={Hq} Hkv={Hkv} {path}")
 
 
+@pytest.mark.parametrize("path", PATHS)
 @pytest.mark.parametrize("norm,theta", [(False, 0.0), (True, 0.0), (False, 5e5)])
-def test_prologue_switches(norm, theta):
+def test_prologue_switches(norm, theta, path):
     inp = small(B=1, Hq=10, Hkv=2, S=160, lens=[160], norm=norm, theta=theta)
-    out = run(inp).cpu().numpy()
-    compare(valid_rows(out, inp), ref(inp), ATOL_BF16, f"norm={norm} theta={theta}")
+    out = run(inp, path=path).cpu().numpy()
+    compare(valid_rows(out, inp), ref(inp), ATOL_BF16, f"norm={norm} theta={theta} {path}")
 
 
-def test_short_and_empty_sequences():
+@pytest.mark.parametrize("path", PATHS)
+def test_short_and_empty_sequences(path):
     inp = small(B=4, Hq=10, Hkv=2, S=130, lens=[1, 0, 64, 130])
     torch = require_gpu()
     out_t = torch.full((4, 10, 130, 128), 777.0, device="cuda")
-    run(inp, out=out_t)
+    run(inp, out=out_t, path=path)
     out = out_t.cpu().numpy()
     assert np.all(out[1] == 777.0)                 # n = 0: nothing written
     assert np.all(out[0, :, 1:] == 777.0)          # rows past n untouched
@@ -107,21 +117,33 @@ def test_bf16_output():
     assert np.all(np.abs(out - r) <= ATOL_BF16 + np.abs(r) * 2.0 ** -8)
 
 
-def test_deterministic_bitwise():
+@pytest.mark.parametrize("path", PATHS)
+def test_deterministic_bitwise(path):
     inp = small(B=1, Hq=10, Hkv=2, S=384, lens=[384])
     g = gpu_inputs(inp)
-    a = run(inp, g=g).cpu().numpy()
-    b = run(inp, g=g).cpu().numpy()
+    a = run(inp, g=g, path=path).cpu().numpy()
+    b = run(inp, g=g, path=path).cpu().numpy()
     assert np.array_equal(a, b)
 
 
-def test_qwen3_prefill_s4096_sampled():
+def test_paths_agree():
+    # k' is rounded to bf16 the same way on both paths, but P is rounded to
+    # bf16 against each path's own running maximum (32- vs 64-key tiles), so
+    # the two differ by P-rounding noise, of the order of the oracle bound
+    inp = small(B=1, Hq=10, Hkv=2, S=256, lens=[256])
+    a = run(inp, path="two_phase").cpu().numpy()
+    b = run(inp, path="single_kernel").cpu().numpy()
+    compare(a, b, ATOL_BF16, "two-phase vs single-kernel")
+
+
+@pytest.mark.parametrize("path", PATHS)
+def test_qwen3_prefill_s4096_sampled(path):
     # the full Qwen3-14B causal prefill (S = 4096, 40 / 8 heads), checked on
     # sampled heads and rows that span first, diagonal, ragged-tile and last rows
     w = synth.QWEN3_PREFILL
-    log(f"case {w.name}")
+    log(f"case {w.name} {path}")
     inp = synth.make_prefill(w)
-    out = run(inp).cpu().numpy()
+    out = run(inp, path=path).cpu().numpy()
     heads = [0, 4, 5, 17, 39]
     rows = np.array([0, 1, 63, 64, 127, 128, 129, 1000, 2047, 2048, 3071, 4094, 4095])
     r = ref(inp, heads=heads, rows=rows)
