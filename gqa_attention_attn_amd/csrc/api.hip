@@ -68,11 +68,17 @@ void decode_plan(const gqa_decode_desc* d, int32_t* T, int32_t* n) {
   *n = (int32_t)(((int64_t)d->max_seq + t - 1) / t);
 }
 
+// Decode workspace: [partial O: B * Hq * n * 128 f32] [partial (m, l): B * Hq * n * 2 f32].
 size_t decode_ws_bytes(const gqa_decode_desc* d, int32_t n) {
   if (n <= 1) return 0;
   const size_t slots = (size_t)d->batch * (size_t)d->num_q_heads * (size_t)n;
   return slots * (GQA_ATTN_HEAD_DIM + 2) * sizeof(float);
 }
+
+// Grids up to this many workgroups are resident at once (two per compute
+// unit) and latency-bound: they use the partition kernel variant without
+// register spills; larger grids use the one with more waves per SIMD.
+constexpr int64_t kResidentWorkgroups = 512;
 
 // Prefill workgroup blocking: HC query heads (the largest divisor of G that is
 // at most 8) times BQ query tokens, with HC * BQ / 32 <= 10 waves of 32 rows.
@@ -172,6 +178,8 @@ gqa_status prepare_decode(const gqa_decode_desc* d, const void* q, const void* k
     return GQA_ERR_ALIGN;
   int32_t T, n;
   decode_plan(d, &T, &n);
+  const int64_t wgs = (int64_t)n * d->batch * d->num_kv_heads;
+  if (wgs > INT32_MAX) return GQA_ERR_SHAPE;
   const size_t need = decode_ws_bytes(d, n);
   if (need > 0) {
     if (workspace == nullptr || workspace_bytes < need) return GQA_ERR_WORKSPACE;
@@ -186,10 +194,10 @@ gqa_status prepare_decode(const gqa_decode_desc* d, const void* q, const void* k
   p->q_norm_w = q_norm_w;
   p->k_norm_w = k_norm_w;
   p->out = out;
-  p->ws_o = need > 0 ? (float*)workspace : nullptr;
-  p->ws_ml = need > 0 ? (float*)((char*)workspace + (size_t)d->batch * d->num_q_heads * n * GQA_ATTN_HEAD_DIM *
-                                                        sizeof(float))
-                      : nullptr;
+  if (need > 0) {
+    p->ws_o = (float*)workspace;
+    p->ws_ml = p->ws_o + (size_t)d->batch * d->num_q_heads * n * GQA_ATTN_HEAD_DIM;
+  }
   p->q_sb = d->q_stride_b;
   p->q_sh = d->q_stride_h;
   p->k_sb = d->k_stride_b;
@@ -208,9 +216,11 @@ gqa_status prepare_decode(const gqa_decode_desc* d, const void* q, const void* k
   p->split = T;
   p->n_split = n;
   p->out_bf16 = d->out_dtype == GQA_BF16;
+  p->wide = wgs > kResidentWorkgroups;
   p->eps = d->eps;
   p->scale_log2 = resolve_scale_log2(d->scale);
   p->rope_theta = rope_theta > 0.f ? (double)rope_theta : 0.0;
+  p->rope_log2_theta = rope_theta > 0.f ? log2((double)rope_theta) : 0.0;
   return GQA_OK;
 }
 
@@ -306,6 +316,7 @@ gqa_status gqa_attn_prefill(const gqa_prefill_desc* d, const void* q, const void
   p.eps = d->eps;
   p.scale_log2 = resolve_scale_log2(d->scale);
   p.rope_theta = rope_theta > 0.f ? (double)rope_theta : 0.0;
+  p.rope_log2_theta = rope_theta > 0.f ? log2((double)rope_theta) : 0.0;
   const hipError_t e = workspace != nullptr ? gqa::launch_prefill_phased(p, workspace, stream)
                                             : gqa::launch_prefill_fused(p, stream);
   return e == hipSuccess ? GQA_OK : GQA_ERR_HIP;

@@ -30,9 +30,11 @@ struct DecodeParams {
   int32_t batch, num_q_heads, num_kv_heads, group, max_seq;
   int32_t split, n_split;
   int32_t out_bf16;
+  int32_t wide;           // 1: grid larger than the GPU holds at once (occupancy over latency)
   float eps;
   float scale_log2;       // softmax scale * log2(e): scores live in the log2 domain
   double rope_theta;      // <= 0: RoPE off
+  double rope_log2_theta; // log2(rope_theta) when RoPE is on
 };
 
 struct PrefillParams {
@@ -57,6 +59,7 @@ struct PrefillParams {
   float eps;
   float scale_log2;
   double rope_theta;
+  double rope_log2_theta;
 };
 
 // Launchers (return the hipGetLastError() of their launches).
@@ -104,15 +107,52 @@ __device__ __forceinline__ uint32_t pair_hi(uint32_t a, uint32_t b) { return (a 
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
-__device__ __forceinline__ float wave_max_xor(float v, int mask) {
-  return fmaxf(v, __shfl_xor(v, mask, 64));
-}
-__device__ __forceinline__ float wave_sum_xor(float v, int mask) { return v + __shfl_xor(v, mask, 64); }
+// ---- cross-lane reductions without LDS: DPP within 16-lane rows,
+//      v_permlane16_swap / v_permlane32_swap across rows (gfx950)
 
-// cos / sin of the RoPE angle p * theta^(-2i/128), formed and evaluated in
-// double precision.  Used where only a few angles are needed.
-__device__ __forceinline__ void rope_cos_sin_f64(double pos, int i, double theta, float& c, float& s) {
-  const double inv = pow(theta, -2.0 * (double)i / (double)kHeadDim);
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+
+// Sum over each group of 8 lanes 8k .. 8k+7 (result in all 8).
+__device__ __forceinline__ float sum8(float v) {
+  v += dpp_mov<0xB1>(v);    // quad_perm [1,0,3,2]: lane ^ 1
+  v += dpp_mov<0x4E>(v);    // quad_perm [2,3,0,1]: lane ^ 2
+  v += dpp_mov<0x141>(v);   // row_half_mirror: the other quad of the 8
+  return v;
+}
+
+// Sum over each 16-lane row.
+__device__ __forceinline__ float sum16(float v) {
+  v = sum8(v);
+  return v + dpp_mov<0x140>(v);   // row_mirror: the other 8 of the row
+}
+
+// {v[lane], v[lane ^ 16]} and {v[lane], v[lane ^ 32]}, in the same order in both lanes.
+__device__ __forceinline__ void pair_xor16(float v, float& a, float& b) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  a = __uint_as_float(r[0]);
+  b = __uint_as_float(r[1]);
+}
+__device__ __forceinline__ void pair_xor32(float v, float& a, float& b) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  a = __uint_as_float(r[0]);
+  b = __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float max_xor16(float v) { float a, b; pair_xor16(v, a, b); return fmaxf(a, b); }
+__device__ __forceinline__ float max_xor32(float v) { float a, b; pair_xor32(v, a, b); return fmaxf(a, b); }
+__device__ __forceinline__ float sum_xor16(float v) { float a, b; pair_xor16(v, a, b); return a + b; }
+__device__ __forceinline__ float sum_xor32(float v) { float a, b; pair_xor32(v, a, b); return a + b; }
+
+// RoPE inverse frequency theta^(-2i/128) = 2^(-(2i/128) log2 theta), in double.
+__device__ __forceinline__ double rope_inv_freq(int i, double log2_theta) {
+  return exp2(-(double)(2 * i) / (double)kHeadDim * log2_theta);
+}
+
+// cos / sin of the RoPE angle pos * inv, formed and evaluated in double
+// precision.  Used where only a few angles are needed.
+__device__ __forceinline__ void rope_cos_sin_f64(double pos, double inv, float& c, float& s) {
   double sn, cn;
   sincos(pos * inv, &sn, &cn);
   c = (float)cn;

@@ -14,73 +14,92 @@
 //    RoPE run inside the attention stage; #602: RoPE on lo/hi halves.
 //
 // gfx950 mapping (not the pages' design, which targets an NPU / simulator):
-//  * one workgroup = (chunk c, KV head h, sequence b), 4 waves of 64 lanes;
-//    wave w handles 32-key steps w, w+4, ... of the chunk and keeps its own
-//    online-softmax state; the 4 states are merged through LDS at the end.
+//  * one workgroup = (chunk c, KV head h, sequence b) on a 1-D grid whose
+//    chunks of one (b, h) share an XCD when the group count allows; 4
+//    streaming waves + 1 prologue wave.  Streaming wave w handles 32-key
+//    steps w, w+4, ... of the chunk with its own online-softmax state; the 4
+//    states are merged through LDS at the end.
+//  * The prologue wave has its own in-order memory queue: it loads q, the
+//    norm weights and the new key row while the streaming waves' K/V loads
+//    are in flight, builds the RoPE table, writes q' (f32 and bf16 hi/lo) to
+//    LDS, and computes the score of the new key (slot L-1) exactly in f32,
+//    which replaces the matrix-core score of the raw cached row.
 //  * S^T = K Q'^T and O^T = V^T P^T run on v_mfma_f32_16x16x32_bf16 (bf16
-//    inputs) or v_mfma_f32_16x16x4_f32 (f32 inputs) with the G <= 16 query
-//    rows as the 16-wide N dimension.  In this orientation a lane owns one
-//    query head (lane % 16), so the row max needs only two cross-lane steps,
-//    and V rows are read with 16 lanes covering one full 256-byte row; the
-//    8x8 bf16 transpose that V^T needs is done in registers.
-//  * K and V are streamed straight from HBM into registers: the first step is
-//    requested before the query prologue runs, and each step buffer is
-//    refilled with the wave's next step as soon as its K (then V) half has
-//    been consumed.
+//    inputs; q' and P as bf16 hi + lo pairs) or v_mfma_f32_16x16x4_f32 (f32
+//    inputs) with the G <= 16 query rows as the 16-wide N dimension; a lane
+//    owns one query head (lane % 16), and the 8x8 bf16 transpose that V^T
+//    needs is done in registers.
+//  * Memory requests of one compute unit are served in issue order, so the
+//    prologue wave issues its small loads (q, norm weights, the new key row)
+//    before the streaming waves start the K/V stream, behind a workgroup
+//    barrier; the sequence length and positions come through scalar loads.
 #include "common.hpp"
 
 namespace gqa {
 namespace {
 
-constexpr int kWaves = 4;
-constexpr int kThreads = kWaves * 64;
+constexpr int kXcds = 8;
+constexpr int kStreamWaves = 4;
+constexpr int kPrologueWave = kStreamWaves;
+constexpr int kThreads = (kStreamWaves + 1) * 64;
 constexpr int kStep = 32;        // keys per wave step
 constexpr int kORow = 132;       // padded LDS row (floats) of the in-workgroup merge
+constexpr int kQRow = 136;       // padded bf16 q' row (272 bytes): 16 rows x 16 bytes hit distinct banks
 
-struct DecodeSmem {
+struct __attribute__((aligned(16))) DecodeSmem {
   float cs[64][2];               // RoPE cos / sin at positions[b]
   float qp[16][kHeadDim];        // q' rows after the prologue (rows >= G are zero)
+  uint16_t qh[16][kQRow];        // bf16(q')            (rows >= G are zero)
+  uint16_t ql[16][kQRow];        // bf16(q' - bf16(q'))
   float kn[kHeadDim];            // the new key row after the prologue
-  float mo[kWaves][16][kORow];   // per-wave unnormalised O (in-workgroup merge)
-  float mm[kWaves][16];
-  float ml[kWaves][16];
+  float snew[16];                // score of the new key per query head (log2 units)
+  float mo[kStreamWaves][16][kORow];   // per-wave unnormalised O (in-workgroup merge)
+  float mm[kStreamWaves][16];
+  float ml[kStreamWaves][16];
 };
 
+// Half-row fetch of a 128-element row for the 16 lanes that hold it:
+// elements 4*c16 .. 4*c16+3 and 64+4*c16 .. 64+4*c16+3.  The raw words are
+// kept until unpack_half_row, so that a fetch issued early is not waited on.
+template <bool BF16> struct RawHalf;
+template <> struct RawHalf<true> { u32x2 lo, hi; };
+template <> struct RawHalf<false> { f32x4 lo, hi; };
+
 template <bool BF16>
-__device__ __forceinline__ void load_half_row(const void* row, int c16, float (&x)[8]) {
-  // x[0..3] = dims 4*c16 .. 4*c16+3; x[4..7] = dims 64+4*c16 .. 64+4*c16+3
+__device__ __forceinline__ RawHalf<BF16> fetch_half_row(const void* row, int c16) {
+  RawHalf<BF16> r;
   if constexpr (BF16) {
-    const uint16_t* r = (const uint16_t*)row;
-    const u32x2 lo = *(const u32x2*)(r + 4 * c16);
-    const u32x2 hi = *(const u32x2*)(r + 64 + 4 * c16);
-    x[0] = bf16lo(lo[0]); x[1] = bf16hi(lo[0]); x[2] = bf16lo(lo[1]); x[3] = bf16hi(lo[1]);
-    x[4] = bf16lo(hi[0]); x[5] = bf16hi(hi[0]); x[6] = bf16lo(hi[1]); x[7] = bf16hi(hi[1]);
+    r.lo = *(const u32x2*)((const uint16_t*)row + 4 * c16);
+    r.hi = *(const u32x2*)((const uint16_t*)row + 64 + 4 * c16);
   } else {
-    const float* r = (const float*)row;
-    const f32x4 lo = *(const f32x4*)(r + 4 * c16);
-    const f32x4 hi = *(const f32x4*)(r + 64 + 4 * c16);
-    #pragma unroll
-    for (int j = 0; j < 4; ++j) { x[j] = lo[j]; x[4 + j] = hi[j]; }
+    r.lo = *(const f32x4*)((const float*)row + 4 * c16);
+    r.hi = *(const f32x4*)((const float*)row + 64 + 4 * c16);
+  }
+  return r;
+}
+
+template <bool BF16>
+__device__ __forceinline__ void unpack_half_row(const RawHalf<BF16>& r, float (&x)[8]) {
+  if constexpr (BF16) {
+    x[0] = bf16lo(r.lo[0]); x[1] = bf16hi(r.lo[0]); x[2] = bf16lo(r.lo[1]); x[3] = bf16hi(r.lo[1]);
+    x[4] = bf16lo(r.hi[0]); x[5] = bf16hi(r.hi[0]); x[6] = bf16lo(r.hi[1]); x[7] = bf16hi(r.hi[1]);
+  } else {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) { x[j] = r.lo[j]; x[4 + j] = r.hi[j]; }
   }
 }
 
 // The prologue on one row held by 16 consecutive lanes (8 elements each):
-// RMSNorm over the 128 elements (skipped if gamma is null), then RoPE with
-// the cos/sin table (skipped if !rope).  All 16 lanes must be active.
-template <bool BF16>
-__device__ __forceinline__ void prologue_row(float (&x)[8], int c16, const void* gamma, float eps, bool rope,
-                                             const float (*cs)[2]) {
-  if (gamma != nullptr) {
+// RMSNorm over the 128 elements (skipped if !norm), then RoPE with the cos /
+// sin table (skipped if !rope).  All 16 lanes must be active.
+__device__ __forceinline__ void prologue_row(float (&x)[8], int c16, bool norm, const float (&g)[8], float eps,
+                                             bool rope, const float (*cs)[2]) {
+  if (norm) {
     float ss = 0.f;
     #pragma unroll
     for (int j = 0; j < 8; ++j) ss += x[j] * x[j];
-    ss += __shfl_xor(ss, 1, 16);
-    ss += __shfl_xor(ss, 2, 16);
-    ss += __shfl_xor(ss, 4, 16);
-    ss += __shfl_xor(ss, 8, 16);
-    const float r = 1.0f / sqrtf(ss * (1.0f / kHeadDim) + eps);
-    float g[8];
-    load_half_row<BF16>(gamma, c16, g);
+    ss = sum16(ss);
+    const float r = rsqrtf(ss * (1.0f / kHeadDim) + eps);
     #pragma unroll
     for (int j = 0; j < 8; ++j) x[j] = x[j] * r * g[j];
   }
@@ -213,6 +232,22 @@ __device__ __forceinline__ void load_step(Step& st, const Slab& sl, int key0, in
 struct QFragBF16 { bf16x8 hi[4], lo[4]; };
 struct QFragF32 { float q[32]; };
 
+__device__ __forceinline__ void load_qfrag(QFragBF16& qf, const DecodeSmem& sm, int n16, int q4) {
+#pragma unroll
+  for (int kb = 0; kb < 4; ++kb) {
+    qf.hi[kb] = *(const bf16x8*)&sm.qh[n16][32 * q4 + 8 * kb];
+    qf.lo[kb] = *(const bf16x8*)&sm.ql[n16][32 * q4 + 8 * kb];
+  }
+}
+
+__device__ __forceinline__ void load_qfrag(QFragF32& qf, const DecodeSmem& sm, int n16, int q4) {
+#pragma unroll
+  for (int j = 0; j < 32; j += 4) {
+    const f32x4 x = *(const f32x4*)&sm.qp[n16][32 * q4 + j];
+    qf.q[j] = x[0]; qf.q[j + 1] = x[1]; qf.q[j + 2] = x[2]; qf.q[j + 3] = x[3];
+  }
+}
+
 struct RunState {
   f32x4 o[8];      // O^T tiles: lane holds O[g = lane%16][dim (4*(lane/16)+i)*8 + T] in o[T][i]
   float m;         // running max (log2 units), same in the 4 lanes of one query head
@@ -220,62 +255,29 @@ struct RunState {
 };
 
 // scores: s[4*gi + i] = S[key key0 + 16*gi + 4*q4 + i][g = lane%16] (log2 units).
-// nk_gi >= 0 (wave-uniform): the step holds the new key (slot L-1) in group
-// nk_gi; the lane whose row it is (nk_lane) uses its prologue output, read
-// from LDS, instead of the raw cached row.
-__device__ __forceinline__ void scores(const StepBF16& st, const QFragBF16& qf, const float* knl, int nk_gi,
-                                       bool nk_lane, int q4, float scale_log2, float (&s)[8]) {
+__device__ __forceinline__ void scores(const StepBF16& st, const QFragBF16& qf, float scale_log2, float (&s)[8]) {
 #pragma unroll
   for (int gi = 0; gi < 2; ++gi) {
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    if (nk_gi == gi) {
-      // K'_new = hi + lo: hi replaces the raw row, lo adds one more product
 #pragma unroll
-      for (int kb = 0; kb < 4; ++kb) {
-        const float* x = knl + 32 * q4 + 8 * kb;
-        float hv[8], lv[8];
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          hv[j] = (float)(__bf16)x[j];
-          lv[j] = nk_lane ? x[j] - hv[j] : 0.f;
-        }
-        const u32x4 hi = {pack_bf16x2(hv[0], hv[1]), pack_bf16x2(hv[2], hv[3]), pack_bf16x2(hv[4], hv[5]),
-                          pack_bf16x2(hv[6], hv[7])};
-        const u32x4 lo = {pack_bf16x2(lv[0], lv[1]), pack_bf16x2(lv[2], lv[3]), pack_bf16x2(lv[4], lv[5]),
-                          pack_bf16x2(lv[6], lv[7])};
-        const u32x4 a = nk_lane ? hi : st.k[gi][kb];
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a), qf.hi[kb], acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a), qf.lo[kb], acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(lo), qf.hi[kb], acc, 0, 0, 0);
-      }
-    } else {
-#pragma unroll
-      for (int kb = 0; kb < 4; ++kb) {
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(st.k[gi][kb]), qf.hi[kb], acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(st.k[gi][kb]), qf.lo[kb], acc, 0, 0, 0);
-      }
+    for (int kb = 0; kb < 4; ++kb) {
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(st.k[gi][kb]), qf.hi[kb], acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(st.k[gi][kb]), qf.lo[kb], acc, 0, 0, 0);
     }
 #pragma unroll
     for (int i = 0; i < 4; ++i) s[4 * gi + i] = acc[i] * scale_log2;
   }
 }
 
-__device__ __forceinline__ void scores(const StepF32& st, const QFragF32& qf, const float* knl, int nk_gi,
-                                       bool nk_lane, int q4, float scale_log2, float (&s)[8]) {
+__device__ __forceinline__ void scores(const StepF32& st, const QFragF32& qf, float scale_log2, float (&s)[8]) {
 #pragma unroll
   for (int gi = 0; gi < 2; ++gi) {
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    const bool sub = nk_gi == gi && nk_lane;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      f32x4 a = st.k[gi][j];
-      if (sub) {
-        const float* x = knl + 32 * q4 + 4 * j;
-        a = f32x4{x[0], x[1], x[2], x[3]};
-      }
+    for (int j = 0; j < 8; ++j)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[e], qf.q[4 * j + e], acc, 0, 0, 0);
-    }
+      for (int e = 0; e < 4; ++e)
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(st.k[gi][j][e], qf.q[4 * j + e], acc, 0, 0, 0);
 #pragma unroll
     for (int i = 0; i < 4; ++i) s[4 * gi + i] = acc[i] * scale_log2;
   }
@@ -283,8 +285,8 @@ __device__ __forceinline__ void scores(const StepF32& st, const QFragF32& qf, co
 
 // O^T += V^T P^T.  bf16 path: P = hi + lo (two MFMAs per tile).
 __device__ __forceinline__ void accumulate_pv(const StepBF16& st, const float (&p)[8], RunState& rs) {
-  // P^T operand: slot t of lane group q4 <-> key vkey_bf16(q4, t) = the score
-  // order p[0..7] of this lane.
+  // P^T operand: slot t of lane group q4 <-> key vkey_t(t) of that group = the
+  // score order p[0..7] of this lane.
   float h[8], r[8];
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
@@ -316,21 +318,22 @@ __device__ __forceinline__ void accumulate_pv(const StepF32& st, const float (&p
 // One 32-key step from buffer st; afterwards st is refilled with the step at
 // next_key0 (if next_key0 < kend): its K half right after the QK^T MFMAs
 // have consumed st.k, its V half right after P V has consumed st.v.
+// kn >= 0: the score of key kn (the new key) is replaced by snew[lane % 16].
 template <class Step, class QFrag>
-__device__ __forceinline__ void sweep_step(Step& st, const QFrag& qf, const float* knl, bool has_new, int kn,
-                                           RunState& rs, float scale_log2, int key0, int kend, int next_key0,
-                                           const Slab& sl, int n16, int q4) {
+__device__ __forceinline__ void sweep_step(Step& st, const QFrag& qf, const float* snew, int kn, RunState& rs,
+                                           float scale_log2, int key0, int kend, int next_key0, const Slab& sl,
+                                           int n16, int q4) {
   const bool full = key0 + kStep <= kend;
-  int nk_gi = -1;
-  bool nk_lane = false;
-  if (has_new && kn >= key0 && kn < key0 + kStep) {   // wave-uniform
-    nk_gi = (kn - key0) >> 4;
-    nk_lane = ((kn - key0) & 15) == n16;
-  }
   float s[8];
-  scores(st, qf, knl, nk_gi, nk_lane, q4, scale_log2, s);
+  scores(st, qf, scale_log2, s);
   const bool more = next_key0 < kend;
   if (more) load_k_any(st, sl, next_key0, kend, n16, q4);
+  if (kn >= key0 && kn < key0 + kStep) {   // wave-uniform: this step holds the new key
+    const float sn = snew[n16];
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+      if (key0 + 16 * (e >> 2) + 4 * q4 + (e & 3) == kn) s[e] = sn;
+  }
   if (!full) {
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
@@ -341,8 +344,7 @@ __device__ __forceinline__ void sweep_step(Step& st, const QFrag& qf, const floa
   float mx = s[0];
 #pragma unroll
   for (int e = 1; e < 8; ++e) mx = fmaxf(mx, s[e]);
-  mx = wave_max_xor(mx, 16);
-  mx = wave_max_xor(mx, 32);
+  mx = max_xor32(max_xor16(mx));
   const float m_new = fmaxf(rs.m, mx);
   const float corr = fast_exp2(rs.m - m_new);   // 0 on the first step (m = -inf)
   float p[8];
@@ -360,40 +362,156 @@ __device__ __forceinline__ void sweep_step(Step& st, const QFrag& qf, const floa
   if (more) load_v_any(st, sl, next_key0, kend, n16, q4);
 }
 
+// ----------------------------------------------------------------- the prologue wave
+
+// Lane (r4 = lane / 16, c16 = lane % 16) handles rows r = r4 + 4 * pass of the
+// 16-row q' block (rows >= G are zero-filled) and, in lanes 0..15, the new
+// key row.  prologue_issue only requests the rows; prologue_finish (after the
+// streaming waves have queued their K/V loads) computes and writes to LDS
+// what the streaming waves read after the next workgroup barrier.
 template <bool BF16>
-__global__ __launch_bounds__(kThreads, 2) void decode_partition_kernel(const DecodeParams p) {
+struct PrologueRegs {
+  RawHalf<BF16> x[4];        // q rows r4 + 4 * pass (row min(r, G-1): rows >= G are discarded)
+  RawHalf<BF16> gq, gk, y;   // norm weights (unused when NULL), the new key row
+};
+
+// Branch-free: every lane fetches valid rows, so no fetch is waited on here.
+template <bool BF16>
+__device__ __forceinline__ void prologue_issue(const DecodeParams& p, int b, int h, int lane, int kn,
+                                               PrologueRegs<BF16>& pr) {
+  constexpr int kElem = BF16 ? 2 : 4;
+  const int r4 = lane >> 4, c16 = lane & 15;
+  const int G = p.group;
+#pragma unroll
+  for (int ps = 0; ps < 4; ++ps) {
+    const int r = min(4 * ps + r4, G - 1);
+    const uint8_t* row = (const uint8_t*)p.q + ((int64_t)b * p.q_sb + (int64_t)(h * G + r) * p.q_sh) * kElem;
+    pr.x[ps] = fetch_half_row<BF16>(row, c16);
+  }
+  pr.gq = fetch_half_row<BF16>(p.q_norm_w != nullptr ? p.q_norm_w : p.q, c16);
+  pr.gk = fetch_half_row<BF16>(p.k_norm_w != nullptr ? p.k_norm_w : p.q, c16);
+  const uint8_t* row = (const uint8_t*)p.k + ((int64_t)b * p.k_sb + (int64_t)h * p.k_sh + (int64_t)max(kn, 0) * p.k_ss) * kElem;
+  pr.y = fetch_half_row<BF16>(row, c16);
+}
+
+template <bool BF16>
+__device__ __forceinline__ void prologue_finish(const DecodeParams& p, DecodeSmem& sm, double pos, int lane,
+                                                bool rope, bool has_new, PrologueRegs<BF16>& pr) {
+  const int r4 = lane >> 4, c16 = lane & 15;
+  const int G = p.group;
+  const bool qnorm = p.q_norm_w != nullptr, knorm = p.k_norm_w != nullptr;
+  float gq[8], gk[8], q[4][8];
+  unpack_half_row<BF16>(pr.gq, gq);
+  unpack_half_row<BF16>(pr.gk, gk);
+  if (rope) {
+    // bf16: angle reduced to revolutions in double, hardware sin / cos;
+    // f32: sin / cos in double
+    const double inv = rope_inv_freq(lane, p.rope_log2_theta);
+    if constexpr (BF16) rope_cos_sin_rev(pos, inv * 0.15915494309189535, sm.cs[lane][0], sm.cs[lane][1]);
+    else rope_cos_sin_f64(pos, inv, sm.cs[lane][0], sm.cs[lane][1]);
+    // the table is read back by other lanes of this wave only
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  }
+#pragma unroll
+  for (int ps = 0; ps < 4; ++ps) {
+    const int r = 4 * ps + r4;
+    float v[8];
+    unpack_half_row<BF16>(pr.x[ps], v);
+    prologue_row(v, c16, qnorm, gq, p.eps, rope, sm.cs);
+    if (r >= G) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) v[j] = 0.f;
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) q[ps][j] = v[j];   // keep q' for the new-key score
+    *(f32x4*)&sm.qp[r][4 * c16] = f32x4{v[0], v[1], v[2], v[3]};
+    *(f32x4*)&sm.qp[r][64 + 4 * c16] = f32x4{v[4], v[5], v[6], v[7]};
+    if constexpr (BF16) {
+      float hv[8], lv[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        hv[j] = (float)(__bf16)v[j];
+        lv[j] = v[j] - hv[j];
+      }
+      *(u32x2*)&sm.qh[r][4 * c16] = u32x2{pack_bf16x2(hv[0], hv[1]), pack_bf16x2(hv[2], hv[3])};
+      *(u32x2*)&sm.qh[r][64 + 4 * c16] = u32x2{pack_bf16x2(hv[4], hv[5]), pack_bf16x2(hv[6], hv[7])};
+      *(u32x2*)&sm.ql[r][4 * c16] = u32x2{pack_bf16x2(lv[0], lv[1]), pack_bf16x2(lv[2], lv[3])};
+      *(u32x2*)&sm.ql[r][64 + 4 * c16] = u32x2{pack_bf16x2(lv[4], lv[5]), pack_bf16x2(lv[6], lv[7])};
+    }
+  }
+  if (has_new) {
+    float y[8];
+    unpack_half_row<BF16>(pr.y, y);
+    prologue_row(y, c16, knorm, gk, p.eps, rope, sm.cs);
+    if (r4 == 0) {
+      *(f32x4*)&sm.kn[4 * c16] = f32x4{y[0], y[1], y[2], y[3]};
+      *(f32x4*)&sm.kn[64 + 4 * c16] = f32x4{y[4], y[5], y[6], y[7]};
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    const f32x4 ka = *(const f32x4*)&sm.kn[4 * c16], kb = *(const f32x4*)&sm.kn[64 + 4 * c16];
+#pragma unroll
+    for (int ps = 0; ps < 4; ++ps) {
+      float d = 0.f;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) d += q[ps][j] * ka[j] + q[ps][4 + j] * kb[j];
+      d = sum16(d);
+      if (c16 == 0) sm.snew[4 * ps + r4] = d * p.scale_log2;
+    }
+  }
+}
+
+// ----------------------------------------------------------------- partition kernel
+
+__device__ __forceinline__ void write_zero_rows(const DecodeParams& p, int b, int h, int tid) {
+  const int g = tid >> 4, d8 = (tid & 15) * 8;
+  if (g >= p.group) return;
+  uint8_t* o = (uint8_t*)p.out + ((int64_t)b * p.o_sb + (int64_t)(h * p.group + g) * p.o_sh) * (p.out_bf16 ? 2 : 4);
+  if (p.out_bf16) {
+    *(u32x4*)(o + 2 * d8) = u32x4{0, 0, 0, 0};
+  } else {
+    *(f32x4*)(o + 4 * d8) = f32x4{0.f, 0.f, 0.f, 0.f};
+    *(f32x4*)(o + 4 * d8 + 16) = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+}
+
+// Launch bounds: bf16 with WIDE = three waves per SIMD (two workgroups per
+// compute unit, for grids that stream many steps per wave), else two (one
+// workgroup per compute unit, no register spills: the latency-bound grids
+// that fit on the GPU at once).  f32: one workgroup per compute unit.
+template <bool BF16, bool WIDE>
+__global__ __launch_bounds__(kThreads, BF16 ? (WIDE ? 3 : 2) : 1) void decode_partition_kernel(const DecodeParams p) {
   using Step = typename std::conditional<BF16, StepBF16, StepF32>::type;
   using QFrag = typename std::conditional<BF16, QFragBF16, QFragF32>::type;
   constexpr int kElem = BF16 ? 2 : 4;
 
   __shared__ DecodeSmem sm;
 
-  const int c = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform branches
   const int n16 = lane & 15, q4 = lane >> 4;
   const int G = p.group;
   const bool direct = p.n_split == 1;
 
-  int L = p.seq_lens[b];
-  L = L < 0 ? 0 : (L > p.max_seq ? p.max_seq : L);
-  const int c0 = c * p.split;
-  if (c0 >= L) {
-    if (direct && c == 0) {   // L == 0: defined as an all-zero output row
-      const int g = tid >> 4, d8 = (tid & 15) * 8;
-      if (g < G) {
-        uint8_t* o = (uint8_t*)p.out + ((int64_t)b * p.o_sb + (int64_t)(h * G + g) * p.o_sh) * (p.out_bf16 ? 2 : 4);
-        if (p.out_bf16) {
-          *(u32x4*)(o + 2 * d8) = u32x4{0, 0, 0, 0};
-        } else {
-          *(f32x4*)(o + 4 * d8) = f32x4{0.f, 0.f, 0.f, 0.f};
-          *(f32x4*)(o + 4 * d8 + 16) = f32x4{0.f, 0.f, 0.f, 0.f};
-        }
-      }
-    }
-    return;
+  // ---- workgroup -> (group = (b, h), chunk c)
+  const int groups = p.batch * p.num_kv_heads;
+  const int bid = blockIdx.x;
+  int grp, c;
+  if (groups % kXcds == 0) {   // the chunks of one group on one XCD (shared L2 for the merge)
+    const int slot = bid / kXcds;
+    grp = bid % kXcds + kXcds * (slot / p.n_split);
+    c = slot % p.n_split;
+  } else {
+    grp = bid / p.n_split;
+    c = bid % p.n_split;
   }
-  const int c1 = min(c0 + p.split, L);
-  const int nsteps = (c1 - c0 + kStep - 1) / kStep;
+  const int b = grp / p.num_kv_heads, h = grp % p.num_kv_heads;
+  const int c0 = c * p.split;
+  const int cap = min(c0 + p.split, p.max_seq);   // static end of the chunk
+
   Slab sl;
   sl.kb = (const uint8_t*)p.k + ((int64_t)b * p.k_sb + (int64_t)h * p.k_sh) * kElem;
   sl.vb = (const uint8_t*)p.v + ((int64_t)b * p.v_sb + (int64_t)h * p.v_sh) * kElem;
@@ -407,133 +525,99 @@ __global__ __launch_bounds__(kThreads, 2) void decode_partition_kernel(const Dec
     sl.vlane = (uint32_t)(4 * q4) * sl.vss + 32u * n16;
   }
 
-  // ---- the first K/V steps go to memory before anything else, so that their
-  //      latency overlaps the query prologue
+  // ---- the prologue wave requests its rows, then the streaming waves queue
+  //      their first K/V steps behind them (one memory queue per compute unit)
+  const bool stream = wave < kStreamWaves;
+  const bool rope = p.rope_theta > 0.0;
+  int L = p.seq_lens[b];   // scalar loads, ahead of any fence
+  L = L < 0 ? 0 : (L > p.max_seq ? p.max_seq : L);
+  const double pos = rope ? (double)p.positions[b] : 0.0;
+  const int c1 = min(cap, L);
+  const bool has_new = (rope || p.k_norm_w != nullptr) && c0 < L && c1 == L;   // chunk holds slot L-1
+  const int kn = has_new ? L - 1 : -1;
+  PrologueRegs<BF16> pr;
+  if (wave == kPrologueWave && c0 < L) prologue_issue<BF16>(p, b, h, lane, kn, pr);
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");   // keeps the loads above on this side
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+
+  if (c0 >= L) {     // no keys in this chunk
+    if (c == 0 && direct) write_zero_rows(p, b, h, tid);   // L == 0: all-zero output rows
+    return;
+  }
+  const int nsteps = (c1 - c0 + kStep - 1) / kStep;
   int s = wave;
   Step A;
-  if (s < nsteps) load_step(A, sl, c0 + s * kStep, c1, n16, q4);
+  if (stream && s < nsteps) load_step(A, sl, c0 + s * kStep, c1, n16, q4);
+  if (wave == kPrologueWave) prologue_finish<BF16>(p, sm, pos, lane, rope, has_new, pr);
+  __syncthreads();   // q', the new-key score and the tables are in LDS
 
-  const bool rope = p.rope_theta > 0.0;
-  const bool k_pro = rope || p.k_norm_w != nullptr;
-  const bool has_new = k_pro && c1 == L;   // this chunk holds slot L-1
-  const double pos = (double)p.positions[b];
-
-  // ---- prologue: RoPE table, q' (and the new key row) into LDS
-  if (rope && tid < 64) rope_cos_sin_f64(pos, tid, p.rope_theta, sm.cs[tid][0], sm.cs[tid][1]);
-  __syncthreads();
-  {
-    const int r = tid >> 4, c16 = tid & 15;
-    float x[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    if (r < G) {
-      const uint8_t* row = (const uint8_t*)p.q + ((int64_t)b * p.q_sb + (int64_t)(h * G + r) * p.q_sh) * kElem;
-      load_half_row<BF16>(row, c16, x);
-    }
-    prologue_row<BF16>(x, c16, p.q_norm_w, p.eps, rope, sm.cs);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      sm.qp[r][4 * c16 + j] = x[j];
-      sm.qp[r][64 + 4 * c16 + j] = x[4 + j];
-    }
-    if (has_new && tid < 16) {
-      const uint8_t* row = (const uint8_t*)p.k + ((int64_t)b * p.k_sb + (int64_t)h * p.k_sh + (int64_t)(L - 1) * p.k_ss) * kElem;
-      float y[8];
-      load_half_row<BF16>(row, c16, y);
-      prologue_row<BF16>(y, c16, p.k_norm_w, p.eps, rope, sm.cs);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        sm.kn[4 * c16 + j] = y[j];
-        sm.kn[64 + 4 * c16 + j] = y[4 + j];
-      }
-    }
-  }
-  __syncthreads();
-
-  QFrag qf;
-  if constexpr (BF16) {
-#pragma unroll
-    for (int kb = 0; kb < 4; ++kb) {
-      const float* x = &sm.qp[n16][32 * q4 + 8 * kb];
-      float hi[8], lo[8];
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        hi[j] = (float)(__bf16)x[j];
-        lo[j] = x[j] - hi[j];
-      }
-      qf.hi[kb] = as_bf16x8(u32x4{pack_bf16x2(hi[0], hi[1]), pack_bf16x2(hi[2], hi[3]), pack_bf16x2(hi[4], hi[5]),
-                                  pack_bf16x2(hi[6], hi[7])});
-      qf.lo[kb] = as_bf16x8(u32x4{pack_bf16x2(lo[0], lo[1]), pack_bf16x2(lo[2], lo[3]), pack_bf16x2(lo[4], lo[5]),
-                                  pack_bf16x2(lo[6], lo[7])});
-    }
-  } else {
-#pragma unroll
-    for (int j = 0; j < 32; ++j) qf.q[j] = sm.qp[n16][32 * q4 + j];
-  }
-  const int kn = L - 1;
-
-  // ---- the sweep over this chunk's keys
   RunState rs;
+  if (stream) {
+    QFrag qf;
+    load_qfrag(qf, sm, n16, q4);
 #pragma unroll
-  for (int T = 0; T < 8; ++T) rs.o[T] = f32x4{0.f, 0.f, 0.f, 0.f};
-  rs.m = -INFINITY;
-  rs.l = 0.f;
-
-  // one step buffer per wave, refilled in place: the next step's K is in
-  // flight during this step's softmax and P V, its V during the next QK^T
-  while (s < nsteps) {
-    sweep_step(A, qf, sm.kn, has_new, kn, rs, p.scale_log2, c0 + s * kStep, c1, c0 + (s + kWaves) * kStep, sl, n16,
-               q4);
-    s += kWaves;
+    for (int T = 0; T < 8; ++T) rs.o[T] = f32x4{0.f, 0.f, 0.f, 0.f};
+    rs.m = -INFINITY;
+    rs.l = 0.f;
+    // one step buffer per wave, refilled in place: the next step's K is in
+    // flight during this step's softmax and P V, its V during the next QK^T
+    while (s < nsteps) {
+      sweep_step(A, qf, sm.snew, kn, rs, p.scale_log2, c0 + s * kStep, c1, c0 + (s + kStreamWaves) * kStep, sl,
+                 n16, q4);
+      s += kStreamWaves;
+    }
+    // ---- this wave's state into LDS for the in-workgroup merge
+    rs.l = sum_xor32(sum_xor16(rs.l));
+    if (q4 == 0) {
+      sm.mm[wave][n16] = rs.m;
+      sm.ml[wave][n16] = rs.l;
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      float* dst = &sm.mo[wave][n16][(4 * q4 + i) * 8];
+      *(f32x4*)dst = f32x4{rs.o[0][i], rs.o[1][i], rs.o[2][i], rs.o[3][i]};
+      *(f32x4*)(dst + 4) = f32x4{rs.o[4][i], rs.o[5][i], rs.o[6][i], rs.o[7][i]};
+    }
   }
+  __syncthreads();
 
   // ---- merge the 4 wave states of this workgroup (ADR-0060 section 4 merge)
-  rs.l = wave_sum_xor(rs.l, 16);
-  rs.l = wave_sum_xor(rs.l, 32);
-  if (q4 == 0) {
-    sm.mm[wave][n16] = rs.m;
-    sm.ml[wave][n16] = rs.l;
-  }
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    float* dst = &sm.mo[wave][n16][(4 * q4 + i) * 8];
-    *(f32x4*)dst = f32x4{rs.o[0][i], rs.o[1][i], rs.o[2][i], rs.o[3][i]};
-    *(f32x4*)(dst + 4) = f32x4{rs.o[4][i], rs.o[5][i], rs.o[6][i], rs.o[7][i]};
-  }
-  __syncthreads();
-
   const int g = tid >> 4, d8 = (tid & 15) * 8;
-  if (g >= G) return;
-  float M = sm.mm[0][g];
+  if (g < G) {
+    float M = sm.mm[0][g];
 #pragma unroll
-  for (int w = 1; w < kWaves; ++w) M = fmaxf(M, sm.mm[w][g]);
-  float lt = 0.f;
-  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    for (int w = 1; w < kStreamWaves; ++w) M = fmaxf(M, sm.mm[w][g]);
+    float lt = 0.f;
+    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int w = 0; w < kWaves; ++w) {
-    const float sc = fast_exp2(sm.mm[w][g] - M);   // 0 for a wave that saw no key
-    lt += sc * sm.ml[w][g];
-    const float* src = &sm.mo[w][g][d8];
+    for (int w = 0; w < kStreamWaves; ++w) {
+      const float sc = fast_exp2(sm.mm[w][g] - M);   // 0 for a wave that saw no key
+      lt += sc * sm.ml[w][g];
+      const float* src = &sm.mo[w][g][d8];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) acc[j] += sc * src[j];
-  }
-  const int hq = h * G + g;
-  if (direct) {
-    const float inv = 1.0f / lt;
-    uint8_t* o = (uint8_t*)p.out + ((int64_t)b * p.o_sb + (int64_t)hq * p.o_sh) * (p.out_bf16 ? 2 : 4);
-    if (p.out_bf16) {
-      *(u32x4*)(o + 2 * d8) = u32x4{pack_bf16x2(acc[0] * inv, acc[1] * inv), pack_bf16x2(acc[2] * inv, acc[3] * inv),
-                                    pack_bf16x2(acc[4] * inv, acc[5] * inv), pack_bf16x2(acc[6] * inv, acc[7] * inv)};
-    } else {
-      *(f32x4*)(o + 4 * d8) = f32x4{acc[0] * inv, acc[1] * inv, acc[2] * inv, acc[3] * inv};
-      *(f32x4*)(o + 4 * d8 + 16) = f32x4{acc[4] * inv, acc[5] * inv, acc[6] * inv, acc[7] * inv};
+      for (int j = 0; j < 8; ++j) acc[j] += sc * src[j];
     }
-  } else {
-    const int64_t slot = ((int64_t)b * p.num_q_heads + hq) * p.n_split + c;
-    float* wo = p.ws_o + slot * kHeadDim + d8;
-    *(f32x4*)wo = f32x4{acc[0], acc[1], acc[2], acc[3]};
-    *(f32x4*)(wo + 4) = f32x4{acc[4], acc[5], acc[6], acc[7]};
-    if ((tid & 15) == 0) {
-      p.ws_ml[2 * slot] = M;
-      p.ws_ml[2 * slot + 1] = lt;
+    const int hq = h * G + g;
+    if (direct) {
+      const float inv = 1.0f / lt;
+      uint8_t* o = (uint8_t*)p.out + ((int64_t)b * p.o_sb + (int64_t)hq * p.o_sh) * (p.out_bf16 ? 2 : 4);
+      if (p.out_bf16) {
+        *(u32x4*)(o + 2 * d8) = u32x4{pack_bf16x2(acc[0] * inv, acc[1] * inv), pack_bf16x2(acc[2] * inv, acc[3] * inv),
+                                      pack_bf16x2(acc[4] * inv, acc[5] * inv), pack_bf16x2(acc[6] * inv, acc[7] * inv)};
+      } else {
+        *(f32x4*)(o + 4 * d8) = f32x4{acc[0] * inv, acc[1] * inv, acc[2] * inv, acc[3] * inv};
+        *(f32x4*)(o + 4 * d8 + 16) = f32x4{acc[4] * inv, acc[5] * inv, acc[6] * inv, acc[7] * inv};
+      }
+    } else {
+      const int64_t slot = ((int64_t)b * p.num_q_heads + hq) * p.n_split + c;
+      float* wo = p.ws_o + slot * kHeadDim + d8;
+      *(f32x4*)wo = f32x4{acc[0], acc[1], acc[2], acc[3]};
+      *(f32x4*)(wo + 4) = f32x4{acc[4], acc[5], acc[6], acc[7]};
+      if ((tid & 15) == 0) {
+        p.ws_ml[2 * slot] = M;
+        p.ws_ml[2 * slot + 1] = lt;
+      }
     }
   }
 }
@@ -624,15 +708,23 @@ __global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(const Decod
   }
 }
 
+template <bool BF16>
+void launch_partition(const DecodeParams& p, hipStream_t stream) {
+  const dim3 grid(p.n_split * p.num_kv_heads * p.batch);
+  if constexpr (BF16) {
+    if (p.wide) {
+      hipLaunchKernelGGL((decode_partition_kernel<BF16, true>), grid, dim3(kThreads), 0, stream, p);
+      return;
+    }
+  }
+  hipLaunchKernelGGL((decode_partition_kernel<BF16, false>), grid, dim3(kThreads), 0, stream, p);
+}
+
 }  // namespace
 
 hipError_t launch_decode_partition(const DecodeParams& p, bool in_bf16, hipStream_t stream) {
-  const dim3 grid(p.n_split, p.num_kv_heads, p.batch);
-  if (in_bf16) {
-    hipLaunchKernelGGL(decode_partition_kernel<true>, grid, dim3(kThreads), 0, stream, p);
-  } else {
-    hipLaunchKernelGGL(decode_partition_kernel<false>, grid, dim3(kThreads), 0, stream, p);
-  }
+  if (in_bf16) launch_partition<true>(p, stream);
+  else launch_partition<false>(p, stream);
   return hipGetLastError();
 }
 

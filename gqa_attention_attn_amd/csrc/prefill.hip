@@ -115,9 +115,7 @@ __device__ __forceinline__ void stage_unit(PrefillSmem& sm, const Raw& r, const 
       float ss = 0.f;
 #pragma unroll
       for (int e = 0; e < 8; ++e) ss += xl[e] * xl[e] + xh[e] * xh[e];
-      ss += __shfl_xor(ss, 1, 8);
-      ss += __shfl_xor(ss, 2, 8);
-      ss += __shfl_xor(ss, 4, 8);
+      ss = sum8(ss);
       const float rr = 1.0f / sqrtf(ss * (1.0f / kHeadDim) + p.eps);
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
@@ -200,7 +198,7 @@ __global__ __launch_bounds__(kMaxThreads) void prefill_kernel(const PrefillParam
   const bool wave_live = wq0 < n;
 
   // ---- tables: RoPE inverse frequencies (revolutions) and key norm weight
-  if (tid < 64 && rope) sm.inv_rev[tid] = pow(p.rope_theta, -2.0 * (double)tid / (double)kHeadDim) * 0.15915494309189535;
+  if (tid < 64 && rope) sm.inv_rev[tid] = rope_inv_freq(tid, p.rope_log2_theta) * 0.15915494309189535;
   if (tid < kHeadDim) sm.gk[tid] = p.k_norm_w ? bf16lo(((const uint16_t*)p.k_norm_w)[tid]) : 1.0f;
 
   Staging st;
@@ -244,7 +242,7 @@ __global__ __launch_bounds__(kMaxThreads) void prefill_kernel(const PrefillParam
           const float a = bf16_elem(qlo[j], e), c = bf16_elem(qhi[j], e);
           ss += a * a + c * c;
         }
-      ss += __shfl_xor(ss, 32, 64);
+      ss = sum_xor32(ss);
       r = 1.0f / sqrtf(ss * (1.0f / kHeadDim) + p.eps);
     }
     __syncthreads();   // the tables are written
@@ -326,7 +324,7 @@ __global__ __launch_bounds__(kMaxThreads) void prefill_kernel(const PrefillParam
       float mx = fmaxf(sacc[0], sacc[1]);
 #pragma unroll
       for (int i = 2; i < 16; i += 2) mx = fmaxf(mx, fmaxf(sacc[i], sacc[i + 1]));
-      mx = wave_max_xor(mx, 32) * p.scale_log2;       // row max in log2 units
+      mx = max_xor32(mx) * p.scale_log2;       // row max in log2 units
       // lazy rescale: keep the running max until some row's max grows by more
       // than kLazyRescale; exponents stay <= 2^kLazyRescale meanwhile
       if (__any(mx > m_run + kLazyRescale)) {
@@ -374,7 +372,7 @@ __global__ __launch_bounds__(kMaxThreads) void prefill_kernel(const PrefillParam
 
   // ---- epilogue: O / l for this lane's query row
   if (!wave_live || qrow >= n) return;
-  l_run = wave_sum_xor(l_run, 32);
+  l_run = sum_xor32(l_run);
   const float inv = 1.0f / l_run;
   uint8_t* orow = (uint8_t*)p.out + ((int64_t)b * p.o_sb + (int64_t)hq * p.o_sh + (int64_t)qrow * p.o_ss) * (p.out_bf16 ? 2 : 4);
   // o[T][4a + r] = O[query][dim 32T + 8a + 4hf + r]

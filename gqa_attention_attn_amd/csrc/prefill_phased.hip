@@ -44,7 +44,7 @@ __global__ __launch_bounds__(256) void key_prologue_kernel(const PrefillParams p
   const int b = blockIdx.z, h = blockIdx.y;
   const int tid = threadIdx.x, r = tid >> 4, c = tid & 15;
   const bool rope = p.rope_theta > 0.0;
-  if (tid < 64 && rope) inv_rev[tid] = pow(p.rope_theta, -2.0 * (double)tid / (double)kHeadDim) * 0.15915494309189535;
+  if (tid < 64 && rope) inv_rev[tid] = rope_inv_freq(tid, p.rope_log2_theta) * 0.15915494309189535;
   __syncthreads();
   int n = p.seq_lens[b];
   n = n < 0 ? 0 : (n > p.max_seq ? p.max_seq : n);
@@ -59,10 +59,7 @@ __global__ __launch_bounds__(256) void key_prologue_kernel(const PrefillParams p
     float ss = 0.f;
 #pragma unroll
     for (int j = 0; j < 8; ++j) ss += x[j] * x[j];
-    ss += __shfl_xor(ss, 1, 16);
-    ss += __shfl_xor(ss, 2, 16);
-    ss += __shfl_xor(ss, 4, 16);
-    ss += __shfl_xor(ss, 8, 16);
+    ss = sum16(ss);
     const float rr = 1.0f / sqrtf(ss * (1.0f / kHeadDim) + p.eps);
     const uint16_t* g = (const uint16_t*)p.k_norm_w;
     const u32x2 glo = *(const u32x2*)(g + 4 * c), ghi = *(const u32x2*)(g + 64 + 4 * c);
@@ -209,7 +206,7 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attention_kernel(const Prefil
 
   TileRegs tr;
   fetch_tile(tr, sl, 0, tid);
-  if (tid < 64 && rope) sm.inv_rev[tid] = pow(p.rope_theta, -2.0 * (double)tid / (double)kHeadDim) * 0.15915494309189535;
+  if (tid < 64 && rope) sm.inv_rev[tid] = rope_inv_freq(tid, p.rope_log2_theta) * 0.15915494309189535;
 
   // ---- query prologue: lane (n32, hf) owns row qrow of head hq, dims [32hf, 32hf+32) and [64+32hf, 64+32hf+32)
   bf16x8 qf[8];
@@ -236,7 +233,7 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attention_kernel(const Prefil
           const float a = bf16_elem(qlo[j], e), c = bf16_elem(qhi[j], e);
           ss += a * a + c * c;
         }
-      ss += __shfl_xor(ss, 32, 64);
+      ss = sum_xor32(ss);
       r = 1.0f / sqrtf(ss * (1.0f / kHeadDim) + p.eps);
     }
     stage_tile(sm, tr, 0, tid);
@@ -316,7 +313,7 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attention_kernel(const Prefil
       float mx = fmaxf(sacc[0][0], sacc[1][0]);
 #pragma unroll
       for (int i = 1; i < 16; ++i) mx = fmaxf(mx, fmaxf(sacc[0][i], sacc[1][i]));
-      mx = wave_max_xor(mx, 32) * p.scale_log2;
+      mx = max_xor32(mx) * p.scale_log2;
       if (__any(mx > m_run + kLazyRescale)) {   // lazy rescale (the final O / l is unaffected)
         const float m_new = fmaxf(m_run, mx);
         const float corr = fast_exp2(m_run - m_new);
@@ -362,7 +359,7 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attention_kernel(const Prefil
 
   // ---- epilogue: O / l for this lane's query row
   if (!wave_live || qrow >= n) return;
-  l_run = wave_sum_xor(l_run, 32);
+  l_run = sum_xor32(l_run);
   const float inv = 1.0f / l_run;
   uint8_t* orow = (uint8_t*)p.out + ((int64_t)b * p.o_sb + (int64_t)hq * p.o_sh + (int64_t)qrow * p.o_ss) * (p.out_bf16 ? 2 : 4);
   // o[T][4a + r] = O[query][dim 32T + 8a + 4hf + r]

@@ -30,8 +30,8 @@
  *  - The caller owns every buffer.  The library allocates nothing per call,
  *    keeps no mutable global state (calls are reentrant and thread-safe),
  *    never writes q / k / v / caches / norm weights, and writes only `out`
- *    (and `workspace` for decode).  Calls are asynchronous on `stream`; the
- *    library never synchronises the host.
+ *    (and `workspace`).  Calls are asynchronous on `stream`; the library
+ *    never synchronises the host.
  *  - Every argument check except GQA_ERR_HIP happens on the host before any
  *    HIP call, so a rejected call has no device side effects.  No exception
  *    and no abort crosses this ABI.
@@ -154,9 +154,11 @@ gqa_status gqa_attn_decode_workspace_size(const gqa_decode_desc* desc, size_t* b
  * in in_dtype or NULL; rope_theta <= 0 disables RoPE; out: [B, Hq, 128] in
  * out_dtype.  workspace: device buffer of at least
  * gqa_attn_decode_workspace_size bytes, 256-byte aligned (may be NULL when
- * that size is 0); its contents on entry are ignored.
- * Errors: GQA_ERR_NULL, GQA_ERR_SHAPE, GQA_ERR_UNSUPPORTED, GQA_ERR_ALIGN,
- * GQA_ERR_WORKSPACE (checked on the host), GQA_ERR_HIP (launch failure).
+ * that size is 0); its contents on entry are ignored.  Calls that share a
+ * workspace must not run concurrently.
+ * Errors: GQA_ERR_NULL, GQA_ERR_SHAPE (also: more than 2^31 - 1 workgroups),
+ * GQA_ERR_UNSUPPORTED, GQA_ERR_ALIGN, GQA_ERR_WORKSPACE (checked on the
+ * host), GQA_ERR_HIP (launch failure).
  */
 gqa_status gqa_attn_decode(const gqa_decode_desc* desc, const void* q, const void* k_cache,
                            const void* v_cache, const int32_t* seq_lens, const int32_t* positions,

@@ -193,6 +193,44 @@ def test_poisoned_workspace_and_output_canaries():
     assert np.all(got[mask] == 12345.0)
 
 
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_workspace_reuse_across_lengths(dtype):
+    # one workspace, successive calls whose lengths change the number of
+    # chunks per sequence: stale partials of earlier calls must not leak in
+    torch = require_gpu()
+    inp = small(B=3, Hq=10, Hkv=2, S=512, dtype=dtype)   # every cache row holds data
+    g = gpu_inputs(inp, dtype)
+    desc = G.decode_desc(g["q"], g["k"], g["v"], torch.empty(3, 10, 128, device="cuda"), kv_split_tokens=32)
+    ws = G.decode_workspace(desc, "cuda")
+    tol = ATOL_F32 if dtype == "f32" else ATOL_BF16
+    for lens in ([512, 200, 3], [33, 480, 64], [1, 1, 511], [512, 0, 96]):
+        case = dict(inp)
+        case["seq_lens"] = np.array(lens, dtype=np.int32)
+        case["positions"] = np.maximum(case["seq_lens"], 1) - 1 + 3
+        g2 = dict(g, sl=ints(case["seq_lens"]), pos=ints(case["positions"]))
+        out = run(case, dtype, split=32, g=g2, workspace=ws)
+        compare(out.cpu().numpy(), ref(case), tol, f"reuse lens={lens}")
+
+
+def test_decode_equals_partition_then_merge():
+    # gqa_attn_decode against gqa_attn_decode_partition + gqa_attn_decode_merge: bitwise equal
+    torch = require_gpu()
+    inp = small(B=2, Hq=16, Hkv=2, S=1000, dtype="bf16", lens=[1000, 555])
+    g = gpu_inputs(inp, "bf16")
+    a = run(inp, "bf16", split=64, g=g).cpu().numpy()
+    out = torch.empty(2, 16, 128, device="cuda")
+    desc = G.decode_desc(g["q"], g["k"], g["v"], out, kv_split_tokens=64)
+    ws = G.decode_workspace(desc, "cuda")
+    p = lambda x: None if x is None else x.data_ptr()
+    args = (desc, p(g["q"]), p(g["k"]), p(g["v"]), p(g["sl"]), p(g["pos"]), p(g["qw"]), p(g["kw"]),
+            inp["rope_theta"], p(out), p(ws), ws.numel())
+    assert G.gqa_attn_decode_partition(*args, None) == G.GQA_OK
+    assert G.gqa_attn_decode_merge(desc, p(g["sl"]), p(out), p(ws), ws.numel(), None) == G.GQA_OK
+    torch.cuda.synchronize()
+    assert np.array_equal(a, out.cpu().numpy())
+    compare(a, ref(inp), ATOL_BF16, "decode vs oracle")
+
+
 def test_token_major_cache_layout_and_strided_q():
     # caches stored [B, S, Hkv, d] (strides b, h, s = S*Hkv*d, d, Hkv*d); q with a padded head stride
     torch = require_gpu()
