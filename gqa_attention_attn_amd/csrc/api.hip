@@ -26,6 +26,7 @@ gqa_status check_decode_desc(const gqa_decode_desc* d) {
   if (d == nullptr) return GQA_ERR_NULL;
   if (d->batch < 1 || d->num_q_heads < 1 || d->num_kv_heads < 1 || d->max_seq < 1) return GQA_ERR_SHAPE;
   if (d->batch > kGridYZMax || d->num_kv_heads > kGridYZMax) return GQA_ERR_SHAPE;
+  if ((int64_t)d->batch * d->num_q_heads > INT32_MAX) return GQA_ERR_SHAPE;   // merge grid
   if (d->num_q_heads % d->num_kv_heads != 0) return GQA_ERR_SHAPE;
   if (d->kv_split_tokens < 0) return GQA_ERR_SHAPE;
   if (d->head_dim != GQA_ATTN_HEAD_DIM) return GQA_ERR_UNSUPPORTED;

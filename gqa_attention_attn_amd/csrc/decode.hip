@@ -255,18 +255,22 @@ struct RunState {
 };
 
 // scores: s[4*gi + i] = S[key key0 + 16*gi + 4*q4 + i][g = lane%16] (log2 units).
+// Four independent accumulation chains (key group x hi / lo part of q').
 __device__ __forceinline__ void scores(const StepBF16& st, const QFragBF16& qf, float scale_log2, float (&s)[8]) {
+  f32x4 ah[2], al[2];
 #pragma unroll
-  for (int gi = 0; gi < 2; ++gi) {
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  for (int gi = 0; gi < 2; ++gi) ah[gi] = al[gi] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb) {
-      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(st.k[gi][kb]), qf.hi[kb], acc, 0, 0, 0);
-      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(st.k[gi][kb]), qf.lo[kb], acc, 0, 0, 0);
+  for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+    for (int gi = 0; gi < 2; ++gi) {
+      ah[gi] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(st.k[gi][kb]), qf.hi[kb], ah[gi], 0, 0, 0);
+      al[gi] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(st.k[gi][kb]), qf.lo[kb], al[gi], 0, 0, 0);
     }
 #pragma unroll
-    for (int i = 0; i < 4; ++i) s[4 * gi + i] = acc[i] * scale_log2;
-  }
+  for (int gi = 0; gi < 2; ++gi)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) s[4 * gi + i] = (ah[gi][i] + al[gi][i]) * scale_log2;
 }
 
 __device__ __forceinline__ void scores(const StepF32& st, const QFragF32& qf, float scale_log2, float (&s)[8]) {
@@ -637,7 +641,20 @@ __global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(const Decod
   __shared__ __attribute__((aligned(16))) float racc[kMergeGroups][kHeadDim];
   __shared__ float rm[kMergeGroups], rl[kMergeGroups];
 
-  const int hq = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
+  // workgroup -> (b, q head hq): on the XCD that ran the partition workgroups
+  // of its (b, KV head) group when the group count allows it (partials in L2)
+  const int G = p.group, groups = p.batch * p.num_kv_heads;
+  const int bid = blockIdx.x, tid = threadIdx.x;
+  int b, hq;
+  if (groups % kXcds == 0) {
+    const int slot = bid / kXcds;
+    const int grp = bid % kXcds + kXcds * (slot / G);
+    b = grp / p.num_kv_heads;
+    hq = (grp % p.num_kv_heads) * G + slot % G;
+  } else {
+    b = bid / p.num_q_heads;
+    hq = bid % p.num_q_heads;
+  }
   int L = p.seq_lens[b];
   L = L < 0 ? 0 : (L > p.max_seq ? p.max_seq : L);
   const int n = (L + p.split - 1) / p.split;
@@ -730,7 +747,7 @@ hipError_t launch_decode_partition(const DecodeParams& p, bool in_bf16, hipStrea
 
 hipError_t launch_decode_merge(const DecodeParams& p, hipStream_t stream) {
   if (p.n_split == 1) return hipSuccess;
-  hipLaunchKernelGGL(decode_merge_kernel, dim3(p.num_q_heads, p.batch), dim3(kMergeThreads), 0, stream, p);
+  hipLaunchKernelGGL(decode_merge_kernel, dim3(p.num_q_heads * p.batch), dim3(kMergeThreads), 0, stream, p);
   return hipGetLastError();
 }
 
