@@ -10,7 +10,7 @@ in HBM; K/V rotate over enough distinct buffer sets (>= 1 GiB) that the
 256 MB Infinity Cache cannot serve them.  The K timed steps are replayed
 from a HIP graph.
 
-Also reported in the same line: per-kernel durations (HIP events on the
+Also reported in the same line: per-launch kernel durations (HIP events on the
 launch stream) and the roofline of the dominant kernel, the oracle timed on
 the host cores, the causal prefill of the Qwen3-14B shape (S = 4096) in
 TFLOP/s against the bf16 MFMA peak, and the long-context / ragged decodes.
@@ -33,6 +33,10 @@ METRIC = "GQA decode µs/step + achieved HBM GB/s; causal prefill TFLOP/s (1×MI
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, published
 LLC_BYTES = 1 << 30            # rotate at least this many bytes of K/V
+# rocprofv3 FETCH_SIZE / WRITE_SIZE of the decode partition kernel on the
+# headline workload, calibrated on a copy kernel
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_partition_qwen3_14b_b1_s4096_hbm_counters.json")
+KERNEL_SOURCES = ("gqa_attention_attn_amd/csrc/decode.hip", "gqa_attention_attn_amd/csrc/common.hpp")
 
 
 def log(*a):
@@ -108,6 +112,29 @@ class DecodeCase:
         assert st == self.G.GQA_OK
 
 
+def kernel_source_digest():
+    """sha256 over the sources of the decode kernels (the counters file records it)."""
+    import hashlib
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def measured_traffic(kernel):
+    """HBM bytes per launch of `kernel` from the committed counter summary, or
+    None when there is none or the kernel sources changed since it was taken."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if rec.get("kernel_key") != kernel or rec.get("source_sha256") != kernel_source_digest():
+        return None
+    return rec.get("traffic_bytes_per_launch")
+
+
 def graph_time_ms(torch, fn, steps, warmup):
     """Capture `steps` calls of fn(i, stream) in a HIP graph, replay it after a
     warmup graph, and return the elapsed GPU time of the timed replay (ms)."""
@@ -136,23 +163,11 @@ def graph_time_ms(torch, fn, steps, warmup):
     return e0.elapsed_time(e1)
 
 
-def event_kernel_times(torch, parts, steps):
-    """Average GPU durations (us) of each callable in `parts` (each fn(i, stream)),
-    bracketed by HIP events on the launch stream.  A spin kernel queued first
-    keeps the GPU behind the host so the events bracket only kernel time."""
-    s = torch.cuda.Stream()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(parts) + 1)] for _ in range(steps)]
-    torch.cuda.synchronize()
-    with torch.cuda.stream(s):
-        torch.cuda._sleep(int(2.4e9 * 0.05))     # ~50 ms of spinning while the host enqueues
-        for i in range(steps):
-            evs[i][0].record(s)
-            for j, fn in enumerate(parts):
-                fn(i, s.cuda_stream)
-                evs[i][j + 1].record(s)
-    torch.cuda.synchronize()
-    return [1000.0 * sum(evs[i][j].elapsed_time(evs[i][j + 1]) for i in range(steps)) / steps
-            for j in range(len(parts))]
+def launch_time_us(torch, fn, steps, warmup):
+    """Average duration (us) of one launch of fn(i, stream): `steps` back-to-back
+    launches replayed from a HIP graph, bracketed by HIP events on the launch
+    stream (each launch's time includes its share of the dispatch gap)."""
+    return 1000.0 * graph_time_ms(torch, fn, steps, warmup) / steps
 
 
 def cpu_baseline(case_inputs, bytes_per_call, budget_s=12.0):
@@ -263,9 +278,11 @@ def main():
     us_step = 1000.0 * t_ms / K
     gbs = case.bytes / (us_step * 1e-6) / 1e9
     log(f"[bench] decode step {us_step:.2f} us  -> {gbs:.1f} GB/s (split T={case.T}, n={case.n})")
-    t_part, t_merge = event_kernel_times(torch, [case.partition, case.merge], K)
-    log(f"[bench] event durations: partition {t_part:.2f} us, merge {t_merge:.2f} us")
+    t_part = launch_time_us(torch, case.partition, K, W)
+    t_merge = launch_time_us(torch, case.merge, K, W)
+    log(f"[bench] per-launch durations: partition {t_part:.2f} us, merge {t_merge:.2f} us")
     ach = case.bytes / (t_part * 1e-6) / 1e9
+    traffic = measured_traffic("decode_partition:" + w.name)
     result = {
         "metric": METRIC, "value": round(gbs, 2), "unit": "GB/s", "n_gpus": 1, "steps": K, "warmup": W,
         "ms_per_step": round(us_step / 1000.0, 6), "higher_is_better": True, "scaling": "weak",
@@ -278,7 +295,7 @@ def main():
         "kernel_us": {"decode_partition": round(t_part, 3), "decode_merge": round(t_merge, 3)},
         "roofline": {"bound": "hbm", "kernel": "decode_partition", "achieved": round(ach, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBS, 4),
-                     "traffic": None, "algorithmic_bytes": case.bytes},
+                     "traffic": traffic, "algorithmic_bytes": case.bytes},
     }
     cb_inputs = synth.make_decode(w) if not args.no_cpu_baseline else None
     del case
@@ -292,16 +309,14 @@ def main():
         flops = prefill_flops(pin["seq_lens"], pw.num_q_heads)
         pt = graph_time_ms(torch, pcall, pk_steps, max(2, W // 10))
         us_p = 1000.0 * pt / pk_steps
-        (ev_p,) = event_kernel_times(torch, [pcall], pk_steps)
         tf = flops / (us_p * 1e-6) / 1e12
-        tf_k = flops / (ev_p * 1e-6) / 1e12
         extra["prefill"] = {"workload": pw.name, "path": "two_phase", "us_per_call": round(us_p, 2),
-                            "tflops": round(tf, 2), "call_us_events": round(ev_p, 2),
+                            "tflops": round(tf, 2),
                             "roofline": {"bound": "mfma", "kernel": "prefill (key prologue + attention)",
-                                         "achieved": round(tf_k, 2), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                                         "frac": round(tf_k / BF16_PEAK_TFLOPS, 4), "traffic": None,
+                                         "achieved": round(tf, 2), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                                         "frac": round(tf / BF16_PEAK_TFLOPS, 4), "traffic": None,
                                          "algorithmic_flops": flops}}
-        log(f"[bench] prefill two-phase {us_p:.1f} us -> {tf:.1f} TFLOP/s (events {ev_p:.1f} us)")
+        log(f"[bench] prefill two-phase {us_p:.1f} us -> {tf:.1f} TFLOP/s")
         del pt_inputs, pcall
         torch.cuda.empty_cache()
         _, _, pt_inputs, pcall = prefill_case(torch, G, synth, np, two_phase=False)
@@ -320,7 +335,8 @@ def main():
             steps = max(5, K // 10)
             t = graph_time_ms(torch, c.call, steps, 2)
             us = 1000.0 * t / steps
-            tp, tm = event_kernel_times(torch, [c.partition, c.merge], steps)
+            tp = launch_time_us(torch, c.partition, steps, 2)
+            tm = launch_time_us(torch, c.merge, steps, 2)
             extra[dw.name] = {"us_per_step": round(us, 2), "gbs": round(c.bytes / (us * 1e-6) / 1e9, 1),
                               "kernel_us": {"decode_partition": round(tp, 2), "decode_merge": round(tm, 2)},
                               "partition_frac_of_hbm_peak": round(c.bytes / (tp * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
