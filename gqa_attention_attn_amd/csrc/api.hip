@@ -69,17 +69,29 @@ void decode_plan(const gqa_decode_desc* d, int32_t* T, int32_t* n) {
   *n = (int32_t)(((int64_t)d->max_seq + t - 1) / t);
 }
 
+// Chunks per partition workgroup.  With few (b, KV head) groups and many
+// chunks, each workgroup streams several consecutive chunks (one partial per
+// chunk) so that the grid is about one workgroup per compute unit; at least
+// 4 workgroups per group.  With many groups (batched, ragged lengths) one
+// chunk per workgroup keeps the load balanced.
+constexpr int64_t kTargetWorkgroups = 256;
+constexpr int64_t kMaxGroupsMultiChunk = 64;
+
+int32_t decode_chunks_per_workgroup(const gqa_decode_desc* d, int32_t T, int32_t n) {
+  if (n <= 1 || T % 32 != 0) return 1;
+  const int64_t groups = (int64_t)d->batch * d->num_kv_heads;
+  if (groups > kMaxGroupsMultiChunk) return 1;
+  int64_t cpw = (int64_t)n * groups / kTargetWorkgroups;
+  if (cpw > n / 4) cpw = n / 4;
+  return cpw < 1 ? 1 : (int32_t)cpw;
+}
+
 // Decode workspace: [partial O: B * Hq * n * 128 f32] [partial (m, l): B * Hq * n * 2 f32].
 size_t decode_ws_bytes(const gqa_decode_desc* d, int32_t n) {
   if (n <= 1) return 0;
   const size_t slots = (size_t)d->batch * (size_t)d->num_q_heads * (size_t)n;
   return slots * (GQA_ATTN_HEAD_DIM + 2) * sizeof(float);
 }
-
-// Grids up to this many workgroups are resident at once (two per compute
-// unit) and latency-bound: they use the partition kernel variant without
-// register spills; larger grids use the one with more waves per SIMD.
-constexpr int64_t kResidentWorkgroups = 512;
 
 // Prefill workgroup blocking: HC query heads (the largest divisor of G that is
 // at most 8) times BQ query tokens, with HC * BQ / 32 <= 10 waves of 32 rows.
@@ -216,8 +228,8 @@ gqa_status prepare_decode(const gqa_decode_desc* d, const void* q, const void* k
   p->max_seq = d->max_seq;
   p->split = T;
   p->n_split = n;
+  p->cpw = decode_chunks_per_workgroup(d, T, n);
   p->out_bf16 = d->out_dtype == GQA_BF16;
-  p->wide = wgs > kResidentWorkgroups;
   p->eps = d->eps;
   p->scale_log2 = resolve_scale_log2(d->scale);
   p->rope_theta = rope_theta > 0.f ? (double)rope_theta : 0.0;

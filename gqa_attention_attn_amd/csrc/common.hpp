@@ -29,8 +29,8 @@ struct DecodeParams {
   int64_t o_sb, o_sh;
   int32_t batch, num_q_heads, num_kv_heads, group, max_seq;
   int32_t split, n_split;
+  int32_t cpw;            // chunks swept by one partition workgroup (1, or more when split % 32 == 0)
   int32_t out_bf16;
-  int32_t wide;           // 1: grid larger than the GPU holds at once (occupancy over latency)
   float eps;
   float scale_log2;       // softmax scale * log2(e): scores live in the log2 domain
   double rope_theta;      // <= 0: RoPE off

@@ -53,9 +53,9 @@ struct __attribute__((aligned(16))) DecodeSmem {
   uint16_t ql[16][kQRow];        // bf16(q' - bf16(q'))
   float kn[kHeadDim];            // the new key row after the prologue
   float snew[16];                // score of the new key per query head (log2 units)
-  float mo[kStreamWaves][16][kORow];   // per-wave unnormalised O (in-workgroup merge)
-  float mm[kStreamWaves][16];
-  float ml[kStreamWaves][16];
+  float mo[2][kStreamWaves][16][kORow];   // per-wave unnormalised O of a chunk (double-buffered)
+  float mm[2][kStreamWaves][16];
+  float ml[2][kStreamWaves][16];
 };
 
 // Half-row fetch of a 128-element row for the 16 lanes that hold it:
@@ -482,12 +482,62 @@ __device__ __forceinline__ void write_zero_rows(const DecodeParams& p, int b, in
   }
 }
 
-// Launch bounds: bf16 with WIDE = three waves per SIMD (two workgroups per
-// compute unit, for grids that stream many steps per wave), else two (one
-// workgroup per compute unit, no register spills: the latency-bound grids
-// that fit on the GPU at once).  f32: one workgroup per compute unit.
-template <bool BF16, bool WIDE>
-__global__ __launch_bounds__(kThreads, BF16 ? (WIDE ? 3 : 2) : 1) void decode_partition_kernel(const DecodeParams p) {
+// Merge of the 4 wave states of one chunk held in LDS buffer `buf` (ADR-0060
+// section 4, in-workgroup level) by `nthr` threads: thread t takes head
+// t/16 (+ nthr/16, ...) and dims 8 (t%16) .. +7; the result is the chunk's
+// partial (or, with a single chunk, the normalised output row).
+__device__ __forceinline__ void merge_chunk(const DecodeParams& p, const DecodeSmem& sm, int buf, int b, int h, int c,
+                                            int t, int nthr) {
+  const int G = p.group, d8 = (t & 15) * 8;
+  for (int g = t >> 4; g < G; g += nthr >> 4) {
+    float M = sm.mm[buf][0][g];
+#pragma unroll
+    for (int w = 1; w < kStreamWaves; ++w) M = fmaxf(M, sm.mm[buf][w][g]);
+    float lt = 0.f;
+    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int w = 0; w < kStreamWaves; ++w) {
+      const float sc = fast_exp2(sm.mm[buf][w][g] - M);   // 0 for a wave that saw no key
+      lt += sc * sm.ml[buf][w][g];
+      const float* src = &sm.mo[buf][w][g][d8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) acc[j] += sc * src[j];
+    }
+    const int hq = h * G + g;
+    if (p.n_split == 1) {
+      const float inv = 1.0f / lt;
+      uint8_t* o = (uint8_t*)p.out + ((int64_t)b * p.o_sb + (int64_t)hq * p.o_sh) * (p.out_bf16 ? 2 : 4);
+      if (p.out_bf16) {
+        *(u32x4*)(o + 2 * d8) = u32x4{pack_bf16x2(acc[0] * inv, acc[1] * inv), pack_bf16x2(acc[2] * inv, acc[3] * inv),
+                                      pack_bf16x2(acc[4] * inv, acc[5] * inv), pack_bf16x2(acc[6] * inv, acc[7] * inv)};
+      } else {
+        *(f32x4*)(o + 4 * d8) = f32x4{acc[0] * inv, acc[1] * inv, acc[2] * inv, acc[3] * inv};
+        *(f32x4*)(o + 4 * d8 + 16) = f32x4{acc[4] * inv, acc[5] * inv, acc[6] * inv, acc[7] * inv};
+      }
+    } else {
+      const int64_t slot = ((int64_t)b * p.num_q_heads + hq) * p.n_split + c;
+      float* wo = p.ws_o + slot * kHeadDim + d8;
+      *(f32x4*)wo = f32x4{acc[0], acc[1], acc[2], acc[3]};
+      *(f32x4*)(wo + 4) = f32x4{acc[4], acc[5], acc[6], acc[7]};
+      if ((t & 15) == 0) {
+        p.ws_ml[2 * slot] = M;
+        p.ws_ml[2 * slot + 1] = lt;
+      }
+    }
+  }
+}
+
+// A workgroup sweeps `cpw` consecutive chunks of one (b, KV head) group and
+// writes one partial per chunk.  The streaming waves load continuously across
+// chunk boundaries; at the end of each chunk they leave their states in one
+// of two LDS buffers and meet the prologue wave at a barrier, after which the
+// prologue wave merges that chunk while they sweep the next one.  (Chunks are
+// multiples of 32 keys whenever cpw > 1, so no step spans two chunks.)
+// Two waves per SIMD at most (one workgroup of 5 waves per compute unit): no
+// register spills, which matters most for long sweeps (a spill reload would
+// queue behind the wave's in-flight K/V loads).
+template <bool BF16>
+__global__ __launch_bounds__(kThreads, BF16 ? 2 : 1) void decode_partition_kernel(const DecodeParams p) {
   using Step = typename std::conditional<BF16, StepBF16, StepF32>::type;
   using QFrag = typename std::conditional<BF16, QFragBF16, QFragF32>::type;
   constexpr int kElem = BF16 ? 2 : 4;
@@ -497,24 +547,25 @@ __global__ __launch_bounds__(kThreads, BF16 ? (WIDE ? 3 : 2) : 1) void decode_pa
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform branches
   const int n16 = lane & 15, q4 = lane >> 4;
-  const int G = p.group;
   const bool direct = p.n_split == 1;
 
-  // ---- workgroup -> (group = (b, h), chunk c)
+  // ---- workgroup -> (group = (b, h), chunks cf .. cf + cpw - 1)
   const int groups = p.batch * p.num_kv_heads;
+  const int wpg = (p.n_split + p.cpw - 1) / p.cpw;   // workgroups per group
   const int bid = blockIdx.x;
-  int grp, c;
-  if (groups % kXcds == 0) {   // the chunks of one group on one XCD (shared L2 for the merge)
+  int grp, wc;
+  if (groups % kXcds == 0) {   // the workgroups of one group on one XCD
     const int slot = bid / kXcds;
-    grp = bid % kXcds + kXcds * (slot / p.n_split);
-    c = slot % p.n_split;
+    grp = bid % kXcds + kXcds * (slot / wpg);
+    wc = slot % wpg;
   } else {
-    grp = bid / p.n_split;
-    c = bid % p.n_split;
+    grp = bid / wpg;
+    wc = bid % wpg;
   }
   const int b = grp / p.num_kv_heads, h = grp % p.num_kv_heads;
-  const int c0 = c * p.split;
-  const int cap = min(c0 + p.split, p.max_seq);   // static end of the chunk
+  const int cf = wc * p.cpw;
+  const int c0 = cf * p.split;
+  const int cap = min(min(cf + p.cpw, p.n_split) * p.split, p.max_seq);   // static end of the range
 
   Slab sl;
   sl.kb = (const uint8_t*)p.k + ((int64_t)b * p.k_sb + (int64_t)h * p.k_sh) * kElem;
@@ -537,7 +588,7 @@ __global__ __launch_bounds__(kThreads, BF16 ? (WIDE ? 3 : 2) : 1) void decode_pa
   L = L < 0 ? 0 : (L > p.max_seq ? p.max_seq : L);
   const double pos = rope ? (double)p.positions[b] : 0.0;
   const int c1 = min(cap, L);
-  const bool has_new = (rope || p.k_norm_w != nullptr) && c0 < L && c1 == L;   // chunk holds slot L-1
+  const bool has_new = (rope || p.k_norm_w != nullptr) && c0 < L && c1 == L;   // range holds slot L-1
   const int kn = has_new ? L - 1 : -1;
   PrologueRegs<BF16> pr;
   if (wave == kPrologueWave && c0 < L) prologue_issue<BF16>(p, b, h, lane, kn, pr);
@@ -545,85 +596,61 @@ __global__ __launch_bounds__(kThreads, BF16 ? (WIDE ? 3 : 2) : 1) void decode_pa
   __builtin_amdgcn_s_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 
-  if (c0 >= L) {     // no keys in this chunk
-    if (c == 0 && direct) write_zero_rows(p, b, h, tid);   // L == 0: all-zero output rows
+  if (c0 >= L) {     // no keys in this range
+    if (cf == 0 && direct) write_zero_rows(p, b, h, tid);   // L == 0: all-zero output rows
     return;
   }
   const int nsteps = (c1 - c0 + kStep - 1) / kStep;
+  const int nchunks = (c1 - c0 + p.split - 1) / p.split;        // chunks of this range holding keys
+  const int spc = nchunks == 1 ? nsteps : p.split / kStep;      // steps per chunk
   int s = wave;
   Step A;
   if (stream && s < nsteps) load_step(A, sl, c0 + s * kStep, c1, n16, q4);
   if (wave == kPrologueWave) prologue_finish<BF16>(p, sm, pos, lane, rope, has_new, pr);
   __syncthreads();   // q', the new-key score and the tables are in LDS
 
-  RunState rs;
   if (stream) {
     QFrag qf;
     load_qfrag(qf, sm, n16, q4);
+    for (int j = 0; j < nchunks; ++j) {
+      RunState rs;
 #pragma unroll
-    for (int T = 0; T < 8; ++T) rs.o[T] = f32x4{0.f, 0.f, 0.f, 0.f};
-    rs.m = -INFINITY;
-    rs.l = 0.f;
-    // one step buffer per wave, refilled in place: the next step's K is in
-    // flight during this step's softmax and P V, its V during the next QK^T
-    while (s < nsteps) {
-      sweep_step(A, qf, sm.snew, kn, rs, p.scale_log2, c0 + s * kStep, c1, c0 + (s + kStreamWaves) * kStep, sl,
-                 n16, q4);
-      s += kStreamWaves;
-    }
-    // ---- this wave's state into LDS for the in-workgroup merge
-    rs.l = sum_xor32(sum_xor16(rs.l));
-    if (q4 == 0) {
-      sm.mm[wave][n16] = rs.m;
-      sm.ml[wave][n16] = rs.l;
-    }
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      float* dst = &sm.mo[wave][n16][(4 * q4 + i) * 8];
-      *(f32x4*)dst = f32x4{rs.o[0][i], rs.o[1][i], rs.o[2][i], rs.o[3][i]};
-      *(f32x4*)(dst + 4) = f32x4{rs.o[4][i], rs.o[5][i], rs.o[6][i], rs.o[7][i]};
-    }
-  }
-  __syncthreads();
-
-  // ---- merge the 4 wave states of this workgroup (ADR-0060 section 4 merge)
-  const int g = tid >> 4, d8 = (tid & 15) * 8;
-  if (g < G) {
-    float M = sm.mm[0][g];
-#pragma unroll
-    for (int w = 1; w < kStreamWaves; ++w) M = fmaxf(M, sm.mm[w][g]);
-    float lt = 0.f;
-    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int w = 0; w < kStreamWaves; ++w) {
-      const float sc = fast_exp2(sm.mm[w][g] - M);   // 0 for a wave that saw no key
-      lt += sc * sm.ml[w][g];
-      const float* src = &sm.mo[w][g][d8];
-#pragma unroll
-      for (int j = 0; j < 8; ++j) acc[j] += sc * src[j];
-    }
-    const int hq = h * G + g;
-    if (direct) {
-      const float inv = 1.0f / lt;
-      uint8_t* o = (uint8_t*)p.out + ((int64_t)b * p.o_sb + (int64_t)hq * p.o_sh) * (p.out_bf16 ? 2 : 4);
-      if (p.out_bf16) {
-        *(u32x4*)(o + 2 * d8) = u32x4{pack_bf16x2(acc[0] * inv, acc[1] * inv), pack_bf16x2(acc[2] * inv, acc[3] * inv),
-                                      pack_bf16x2(acc[4] * inv, acc[5] * inv), pack_bf16x2(acc[6] * inv, acc[7] * inv)};
-      } else {
-        *(f32x4*)(o + 4 * d8) = f32x4{acc[0] * inv, acc[1] * inv, acc[2] * inv, acc[3] * inv};
-        *(f32x4*)(o + 4 * d8 + 16) = f32x4{acc[4] * inv, acc[5] * inv, acc[6] * inv, acc[7] * inv};
+      for (int T = 0; T < 8; ++T) rs.o[T] = f32x4{0.f, 0.f, 0.f, 0.f};
+      rs.m = -INFINITY;
+      rs.l = 0.f;
+      // one step buffer per wave, refilled in place: the next step's K is in
+      // flight during this step's softmax and P V, its V during the next QK^T
+      const int s_end = min(nsteps, (j + 1) * spc);
+      while (s < s_end) {
+        sweep_step(A, qf, sm.snew, kn, rs, p.scale_log2, c0 + s * kStep, c1, c0 + (s + kStreamWaves) * kStep, sl,
+                   n16, q4);
+        s += kStreamWaves;
       }
-    } else {
-      const int64_t slot = ((int64_t)b * p.num_q_heads + hq) * p.n_split + c;
-      float* wo = p.ws_o + slot * kHeadDim + d8;
-      *(f32x4*)wo = f32x4{acc[0], acc[1], acc[2], acc[3]};
-      *(f32x4*)(wo + 4) = f32x4{acc[4], acc[5], acc[6], acc[7]};
-      if ((tid & 15) == 0) {
-        p.ws_ml[2 * slot] = M;
-        p.ws_ml[2 * slot + 1] = lt;
+      // ---- this wave's state of chunk j into LDS buffer j % 2
+      const int buf = j & 1;
+      rs.l = sum_xor32(sum_xor16(rs.l));
+      if (q4 == 0) {
+        sm.mm[buf][wave][n16] = rs.m;
+        sm.ml[buf][wave][n16] = rs.l;
       }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        float* dst = &sm.mo[buf][wave][n16][(4 * q4 + i) * 8];
+        *(f32x4*)dst = f32x4{rs.o[0][i], rs.o[1][i], rs.o[2][i], rs.o[3][i]};
+        *(f32x4*)(dst + 4) = f32x4{rs.o[4][i], rs.o[5][i], rs.o[6][i], rs.o[7][i]};
+      }
+      __syncthreads();
     }
+  } else {
+    // the prologue wave merges chunk j while the streaming waves sweep chunk j+1
+    for (int j = 0; j + 1 < nchunks; ++j) {
+      __syncthreads();
+      merge_chunk(p, sm, j & 1, b, h, cf + j, lane, 64);
+    }
+    __syncthreads();
   }
+  // ---- the last chunk: every thread of the workgroup merges
+  merge_chunk(p, sm, (nchunks - 1) & 1, b, h, cf + nchunks - 1, tid, kThreads);
 }
 
 // ----------------------------------------------------------------- merge kernel
@@ -727,14 +754,9 @@ __global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(const Decod
 
 template <bool BF16>
 void launch_partition(const DecodeParams& p, hipStream_t stream) {
-  const dim3 grid(p.n_split * p.num_kv_heads * p.batch);
-  if constexpr (BF16) {
-    if (p.wide) {
-      hipLaunchKernelGGL((decode_partition_kernel<BF16, true>), grid, dim3(kThreads), 0, stream, p);
-      return;
-    }
-  }
-  hipLaunchKernelGGL((decode_partition_kernel<BF16, false>), grid, dim3(kThreads), 0, stream, p);
+  const int wpg = (p.n_split + p.cpw - 1) / p.cpw;
+  const dim3 grid(wpg * p.num_kv_heads * p.batch);
+  hipLaunchKernelGGL((decode_partition_kernel<BF16>), grid, dim3(kThreads), 0, stream, p);
 }
 
 }  // namespace

@@ -106,6 +106,17 @@ def test_group_sizes(dtype, G_):
         compare(out.cpu().numpy(), ref(inp), ATOL_F32 if dtype == "f32" else ATOL_BF16, f"G={G_} split={split}")
 
 
+@pytest.mark.parametrize("split", [32, 96, 100, 512])
+def test_many_chunks_per_workgroup_ragged(split):
+    # enough chunks that a partition workgroup sweeps several consecutive chunks
+    # (split a multiple of 32), with lengths ending inside a workgroup's range;
+    # split 100 keeps one chunk per workgroup
+    inp = small(B=2, Hq=40, Hkv=8, S=4096, dtype="bf16", lens=[4096, 1000], seed=17)
+    log(f"case many chunks split={split}")
+    out = run(inp, "bf16", split=split)
+    compare(out.cpu().numpy(), ref(inp), ATOL_BF16, f"many chunks split {split}")
+
+
 @pytest.mark.parametrize("split", [1, 7, 32, 100, 128, 300, 1000])
 def test_split_sweep_ragged(split):
     inp = small(B=3, Hq=10, Hkv=2, S=300, dtype="bf16", lens=[300, 133, 1])
