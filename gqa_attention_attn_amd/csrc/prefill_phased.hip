@@ -186,6 +186,24 @@ __device__ __forceinline__ void qk_tile(f32x16 (&s)[2], const LDS_AS uint8_t* kt
 // with the exponentials.
 struct RowState { float m, l; };
 
+// IEEE maximum (NaN-propagating) needs no quieting of its MFMA-produced
+// operands, and pairs of it fuse into v_maximum3: 17 instructions for the
+// 32 scores a lane holds.
+__device__ __forceinline__ float max3(float a, float b, float c) {
+  return __builtin_elementwise_maximum(__builtin_elementwise_maximum(a, b), c);
+}
+
+__device__ __forceinline__ float row_max32(const f32x16 (&s)[2]) {
+  float t[11];
+#pragma unroll
+  for (int u = 0; u < 2; ++u)
+#pragma unroll
+    for (int i = 0; i < 5; ++i) t[5 * u + i] = max3(s[u][3 * i], s[u][3 * i + 1], s[u][3 * i + 2]);
+  t[10] = __builtin_elementwise_maximum(s[0][15], s[1][15]);
+  return max3(max3(t[0], t[1], t[2]), max3(t[3], t[4], t[5]),
+              max3(t[6], t[7], __builtin_elementwise_maximum(t[8], __builtin_elementwise_maximum(t[9], t[10]))));
+}
+
 __device__ __forceinline__ void softmax_max(f32x16 (&s)[2], RowState& st, f32x16 (&o)[4], bool mask, int lim,
                                             float scale_log2) {
   if (mask) {   // keys at tile offsets >= lim (this lane's half) are invisible
@@ -194,9 +212,7 @@ __device__ __forceinline__ void softmax_max(f32x16 (&s)[2], RowState& st, f32x16
 #pragma unroll
       for (int i = 0; i < 16; ++i) s[u][i] = (32 * u + 8 * (i >> 2) + (i & 3) < lim) ? s[u][i] : -INFINITY;
   }
-  float mx = fmaxf(s[0][0], s[1][0]);
-#pragma unroll
-  for (int i = 1; i < 16; ++i) mx = fmaxf(mx, fmaxf(s[0][i], s[1][i]));
+  float mx = row_max32(s);
   mx = max_xor32(mx) * scale_log2;
   if (__any(mx > st.m + kLazyRescale)) {   // lazy rescale (the final O / l is unaffected)
     const float m_new = fmaxf(st.m, mx);
@@ -208,23 +224,30 @@ __device__ __forceinline__ void softmax_max(f32x16 (&s)[2], RowState& st, f32x16
   }
 }
 
+// The row sum l is taken over the bf16-rounded P that the P V products use
+// (v_dot2 of each packed pair with (1, 1)), so numerator and denominator see
+// the same weights.
 __device__ __forceinline__ void softmax_exp(f32x16 (&s)[2], RowState& st, u32x4 (&pf)[2][2], float scale_log2) {
-  float ps = 0.f;
 #pragma unroll
   for (int u = 0; u < 2; ++u)
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const float e = fast_exp2(fmaf(s[u][i], scale_log2, -st.m));
-      s[u][i] = e;
-      ps += e;
-    }
-  st.l += ps;
+    for (int i = 0; i < 16; ++i) s[u][i] = fast_exp2(fmaf(s[u][i], scale_log2, -st.m));
 #pragma unroll
   for (int u = 0; u < 2; ++u)
 #pragma unroll
     for (int e = 0; e < 2; ++e)
       pf[u][e] = u32x4{pack_bf16x2(s[u][8 * e + 0], s[u][8 * e + 1]), pack_bf16x2(s[u][8 * e + 2], s[u][8 * e + 3]),
                        pack_bf16x2(s[u][8 * e + 4], s[u][8 * e + 5]), pack_bf16x2(s[u][8 * e + 6], s[u][8 * e + 7])};
+  const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
+  float ps[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int u = 0; u < 2; ++u)
+#pragma unroll
+    for (int e = 0; e < 2; ++e)
+#pragma unroll
+      for (int w = 0; w < 4; ++w)   // the (uint32_t) copy matters: hipcc bit-casts element 0 of a vector lvalue
+        ps[w] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, (uint32_t)pf[u][e][w]), one, ps[w], false);
+  st.l += (ps[0] + ps[1]) + (ps[2] + ps[3]);
 }
 
 // O^T += V^T P^T.  The V^T operand of MFMA (u, e), dim tile T comes from two
