@@ -6,41 +6,66 @@
 // separated by an in-kernel grid-wide barrier.  On the GPU the grid-wide
 // barrier is the boundary between two dispatches on one stream:
 //  * phase 1 (key_prologue_kernel): every key row of every (sequence, KV head)
-//    goes through RMSNorm + RoPE once and is stored as bf16 K' in a workspace;
+//    goes through RMSNorm + RoPE once and is stored as bf16 K' in a workspace,
+//    beside a copy of its V row, both already in the padded row layout the
+//    attention tiles have in LDS;
 //  * phase 2 (attention_kernel): tiled online softmax ("ADR-0060: AHBM GQA
 //    Fused Attention Kernel (Llama3-70B)", sections 3 and 5.4) over K' and V,
 //    with each query row's prologue applied when the query tile is loaded.
 // Compared with recomputing the key prologue for every (query block, key
 // tile) pair, each key row is transformed once (about 32x less VALU work for
-// a 4096-token causal prefill) at the cost of writing and re-reading K'.
+// a 4096-token causal prefill) at the cost of writing and re-reading K' and V.
 //
 // Attention mapping: a workgroup = (sequence, query head, 128-query block) of
-// 4 waves x 32 query rows, two workgroups per compute unit; 64-key tiles
-// filled by direct-to-LDS loads (no register staging): K' rows at a padded
-// pitch, V in natural [key][dim] rows read back transposed by
-// ds_read_b64_tr_b16 as the V^T operand; S^T = K' Q'^T and O^T = V^T P^T on
-// v_mfma_f32_32x32x16_bf16.  Software pipeline: the scores of tile t+1 are
-// computed while the softmax of tile t runs; K' is loaded two tiles ahead and
-// V one tile ahead, so one barrier per tile suffices.  A 1-D grid ordered so a
-// (sequence, KV head) group's workgroups share one XCD's L2, heaviest block
-// first.
+// 4 waves x 32 query rows, two waves per SIMD (two workgroups per compute
+// unit).  32-key tiles are filled by linear direct-to-LDS copies (no register
+// staging) from the padded workspace; V is read back transposed by
+// ds_read_b64_tr_b16 as the V^T operand.  S^T = K' Q'^T and O^T = V^T P^T run
+// on v_mfma_f32_32x32x16_bf16.  Software pipeline of a wave, per tile t: the
+// scores of tile t+1 are computed beside the exponentials of tile t, then P V
+// of tile t, then the row maxima of tile t+1; K' is loaded two tiles ahead
+// and V one tile ahead, so one barrier per tile suffices.  A 1-D grid ordered
+// so a (sequence, KV head) group's workgroups share one XCD's L2, heaviest
+// block first.
 #include "common.hpp"
 
 namespace gqa {
 namespace {
 
 constexpr int kXcds = 8;
-constexpr int kAttnThreads = 256;      // 4 waves of 32 query rows
-constexpr int kBM = 128;               // query rows per workgroup
-constexpr int kBN = 64;                // keys per tile
-constexpr float kLazyRescale = 8.0f;   // rescale O only when a row max grows by more than 2^8
+constexpr int kBM = 128;                 // query rows per workgroup
+// 32-row MFMA blocks per wave.  Two blocks per wave would share every K' and
+// V operand read from LDS (half the LDS traffic per product), but their
+// registers leave one wave per SIMD, whose in-order issue serialises the
+// matrix and vector work; one block per wave with two waves per SIMD is
+// faster.
+constexpr int kRB = 1;
+constexpr int kWaves = kBM / (32 * kRB);  // waves per workgroup
+constexpr int kWavesPerSimd = 2;
+constexpr int kAttnThreads = 64 * kWaves;
+constexpr int kBN = 32;                  // keys per tile
+constexpr float kLazyRescale = 8.0f;     // rescale O only when a row max grows by more than 2^8
+
+// Workspace: per (sequence, KV head), tiles of 32 keys, each 9 KiB: K' rows
+// of 256 bytes at a 272-byte pitch (8.5 KiB, the rest slack) and V rows of
+// 256 bytes at a 288-byte pitch, in separate regions; padding bytes are never
+// written nor read.  max_seq is rounded up to whole tiles; rows in
+// [n, round_up(n, 32)) hold zeros.  A tile is copied to LDS as is: there 16
+// consecutive K' rows read 16 bytes each on distinct banks, and the
+// transposing V reads of 4 consecutive rows x 32 bytes hit distinct banks.
+constexpr int kKPitch = 272;
+constexpr int kVPitch = 288;
+constexpr int kTileBytes = 9216;             // 9 direct-to-LDS copies of 1 KiB
+static_assert(kBN * kKPitch <= kTileBytes && kBN * kVPitch == kTileBytes, "tile layout");
+
+__host__ __device__ inline int64_t ws_tiles(int max_seq) { return ((int64_t)max_seq + kBN - 1) / kBN; }
 
 // ----------------------------------------------------------------- phase 1: key prologue
 
 // 16 key rows per workgroup; a row is held by 16 lanes (dims 4c..4c+3 and
 // 64+4c..64+4c+3), so RMSNorm reduces over 16 lanes and RoPE pairs (i, i+64)
-// stay in one lane.
-__global__ __launch_bounds__(256) void key_prologue_kernel(const PrefillParams p, uint16_t* kws) {
+// stay in one lane.  The same lanes copy the row's V (16 bytes each).
+__global__ __launch_bounds__(256) void key_prologue_kernel(const PrefillParams p, uint8_t* kws, uint8_t* vws) {
   __shared__ double inv_rev[kHeadDim / 2];
   const int b = blockIdx.z, h = blockIdx.y;
   const int tid = threadIdx.x, r = tid >> 4, c = tid & 15;
@@ -50,7 +75,19 @@ __global__ __launch_bounds__(256) void key_prologue_kernel(const PrefillParams p
   int n = p.seq_lens[b];
   n = n < 0 ? 0 : (n > p.max_seq ? p.max_seq : n);
   const int key = blockIdx.x * 16 + r;
-  if (key >= n) return;   // whole 16-lane groups leave together
+  const int64_t tile = ((int64_t)b * p.num_kv_heads + h) * ws_tiles(p.max_seq) + key / kBN;
+  uint8_t* kd = kws + tile * kTileBytes + (key % kBN) * kKPitch;
+  uint8_t* vd = vws + tile * kTileBytes + (key % kBN) * kVPitch;
+  if (key >= n) {   // whole 16-lane groups take this branch together
+    if (key < (n + kBN - 1) / kBN * kBN) {   // rows of the last, partial tile: zeros
+      *(u32x4*)(kd + 16 * c) = u32x4{0, 0, 0, 0};
+      *(u32x4*)(vd + 16 * c) = u32x4{0, 0, 0, 0};
+    }
+    return;
+  }
+  *(u32x4*)(vd + 16 * c) =
+      *(const u32x4*)((const uint8_t*)p.v + ((int64_t)b * p.v_sb + (int64_t)h * p.v_sh + (int64_t)key * p.v_ss) * 2 +
+                      16 * c);
   const uint16_t* src = (const uint16_t*)p.k + ((int64_t)b * p.k_sb + (int64_t)h * p.k_sh + (int64_t)key * p.k_ss);
   const u32x2 lo = *(const u32x2*)(src + 4 * c);
   const u32x2 hi = *(const u32x2*)(src + 64 + 4 * c);
@@ -80,237 +117,214 @@ __global__ __launch_bounds__(256) void key_prologue_kernel(const PrefillParams p
       x[4 + j] = bb * cs + a * sn;
     }
   }
-  uint16_t* dst = kws + (((int64_t)b * p.num_kv_heads + h) * p.max_seq + key) * kHeadDim;
-  *(u32x2*)(dst + 4 * c) = u32x2{pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3])};
-  *(u32x2*)(dst + 64 + 4 * c) = u32x2{pack_bf16x2(x[4], x[5]), pack_bf16x2(x[6], x[7])};
+  *(u32x2*)(kd + 8 * c) = u32x2{pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3])};
+  *(u32x2*)(kd + 128 + 8 * c) = u32x2{pack_bf16x2(x[4], x[5]), pack_bf16x2(x[6], x[7])};
 }
 
 // ----------------------------------------------------------------- phase 2: attention
 
-// Logical 16-byte chunk (of 16 per 128-dim row) holding QK operand slot kk of
-// lane half hf: the lane's slots cover dims [32hf, 32hf+32) and
-// [64+32hf, 64+32hf+32), so every query RoPE pair (i, i+64) stays in one lane.
-__device__ __forceinline__ int qk_chunk(int kk, int hf) { return kk < 4 ? 4 * hf + kk : 8 + 4 * hf + (kk - 4); }
-
-// LDS tiles of 64 keys, double-buffered.  K' rows are 256 bytes at a 272-byte
-// pitch (16 consecutive rows read 16 bytes each on distinct banks), V rows
-// (natural [key][dim] order) 256 bytes at a 288-byte pitch (the transposing
-// reads of 4 consecutive rows x 32 bytes hit distinct banks).  Every operand
-// read is then one lane base address plus an immediate offset.
-constexpr int kKPitch = 272;
-constexpr int kVPitch = 288;
-constexpr int kKTileBytes = kBN * kKPitch;   // 17 KiB: 17 direct-to-LDS loads of 1 KiB
-constexpr int kVTileBytes = kBN * kVPitch;   // 18 KiB: 18 loads
-
 #define LDS_AS __attribute__((address_space(3)))
 
-// One 1 KiB direct-to-LDS load: lane l's 16 bytes from `src` land at LDS
-// bytes lds + 16 l.  Issued from inline assembly so that the compiler does not
-// wait for it before unrelated LDS reads; completion is waited for explicitly
-// (s_waitcnt vmcnt) before the barrier that publishes the tile.  M0 carries
-// the LDS address; nothing else in these kernels uses M0.
-__device__ __forceinline__ void dma16(uint32_t lds, const void* src) {
+// One 1 KiB direct-to-LDS copy: lane l's 16 bytes at src + lane_off (lane_off
+// = 16 l) land at LDS bytes lds + 16 l.  Issued from inline assembly so that
+// the compiler does not wait for it before unrelated LDS reads; completion is
+// waited for explicitly (s_waitcnt vmcnt) before the barrier that publishes
+// the tile.  M0 carries the LDS address; nothing else in these kernels uses M0.
+__device__ __forceinline__ void dma16(uint32_t lds, const uint8_t* src, uint32_t lane_off) {
 #pragma clang diagnostic push
 #pragma clang diagnostic ignored "-Winline-asm"
-  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(lds), "v"(src) : "memory", "m0");
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(lds), "v"(lane_off), "s"(src)
+               : "memory", "m0");
 #pragma clang diagnostic pop
 }
 
-// Fill of one tile: LDS byte A = 1024 i + 16 l of the tile is row A / pitch,
-// 16-byte chunk (A % pitch) / 16; chunks past the 16 of a row are padding and
-// take a copy of chunk 15.  Wave w issues loads i = w, w + 4, ...; DmaLane
-// holds the row and source byte offset of each of them for this lane.  Rows
-// at or past n read row n-1 (valid data; their scores are masked and their P
-// is zero).
-template <int PITCH>
-struct DmaLane {
-  static constexpr int kCh = PITCH / 16;            // 17 or 18 chunks per row
-  static constexpr int kLoads = kBN * kCh / 64;     // 17 or 18 loads per tile
-  static constexpr int kPerWave = (kLoads + 3) / 4; // at most 5 per wave
-  int row[kPerWave];
-  uint32_t off[kPerWave];                           // row * stride + 16 * chunk
-  __device__ __forceinline__ void init(uint32_t row_stride, int wave, int lane) {
+// A tile is NLD KiB contiguous in the workspace and in LDS; wave w issues
+// copies w, w + 2, ...
+template <int NLD>
+__device__ __forceinline__ void dma_tile(uint32_t lds, const uint8_t* src, uint32_t lane_off, int wave) {
 #pragma unroll
-    for (int m = 0; m < kPerWave; ++m) {
-      const int a = 64 * (wave + 4 * m) + lane;
-      const int r = a / kCh, ch = min(a - r * kCh, 15);
-      row[m] = r;
-      off[m] = (uint32_t)r * row_stride + 16u * ch;
-    }
-  }
-};
-
-template <int PITCH>
-__device__ __forceinline__ void dma_tile(uint32_t lds, const uint8_t* slab, uint32_t row_stride, const DmaLane<PITCH>& dl,
-                                         int key0, int n, int wave) {
-  constexpr int kLoads = DmaLane<PITCH>::kLoads;
-  const uint8_t* base = slab + (uint32_t)key0 * row_stride;
-  if (key0 + kBN <= n) {   // wave-uniform: every row of the tile is valid
-#pragma unroll
-    for (int m = 0; m < DmaLane<PITCH>::kPerWave; ++m)
-      if (wave + 4 * m < kLoads) dma16(lds + 1024u * (wave + 4 * m), base + dl.off[m]);
-  } else {
-#pragma unroll
-    for (int m = 0; m < DmaLane<PITCH>::kPerWave; ++m) {
-      if (wave + 4 * m >= kLoads) continue;
-      const int over = key0 + dl.row[m] - (n - 1);   // rows past n-1 move back to n-1
-      const uint32_t off = over > 0 ? dl.off[m] - (uint32_t)over * row_stride : dl.off[m];
-      dma16(lds + 1024u * (wave + 4 * m), base + off);
-    }
+  for (int i = 0; i < (NLD + kWaves - 1) / kWaves; ++i) {
+    const int c = kWaves * i + wave;
+    if (c < NLD) dma16(lds + 1024u * c, src + 1024 * c, lane_off);
   }
 }
 
-// S^T for the 64 keys of a K' tile and the wave's 32 query rows:
-// s[kb][i] = S[key 32kb + 8(i/4) + 4hf + i%4][query n32] (raw dot products).
-__device__ __forceinline__ void qk_tile(f32x16 (&s)[2], const LDS_AS uint8_t* kt, const bf16x8 (&qf)[8], int n32,
+// Query operand slots: lane (n32, hf) holds, for slot kk, dims 32hf + 8kk ..
+// +7 (kk < 4) and 64 + 32hf + 8(kk-4) .. +7 (kk >= 4), so every query RoPE
+// pair (i, i+64) stays in one lane; the K' operand of slot kk is read from the
+// same dims of the lane's key row.
+
+// S^T for the 32 keys of a K' tile and the wave's two 32-row blocks:
+// s[rb][i] = S[key 8(i/4) + 4hf + i%4][query 32rb + n32] (raw dot products).
+// Each K' fragment read from LDS feeds both blocks.
+__device__ __forceinline__ void qk_tile(f32x16 (&s)[kRB], const LDS_AS uint8_t* kt, const bf16x8 (&qf)[kRB][8], int n32,
                                         int hf) {
   const LDS_AS uint8_t* base = kt + kKPitch * n32 + 64 * hf;
 #pragma unroll
-  for (int kb = 0; kb < 2; ++kb)
+  for (int rb = 0; rb < kRB; ++rb)
 #pragma unroll
-    for (int i = 0; i < 16; ++i) s[kb][i] = 0.f;
+    for (int i = 0; i < 16; ++i) s[rb][i] = 0.f;
 #pragma unroll
-  for (int kk = 0; kk < 8; ++kk)
+  for (int kk = 0; kk < 8; ++kk) {
+    const u32x4 a = *(const LDS_AS u32x4*)(base + 16 * ((kk & 3) + 8 * (kk >> 2)));
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      const u32x4 a = *(const LDS_AS u32x4*)(base + kKPitch * 32 * kb + 16 * ((kk & 3) + 8 * (kk >> 2)));
-      s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), qf[kk], s[kb], 0, 0, 0);
-    }
+    for (int rb = 0; rb < kRB; ++rb)
+      s[rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), qf[rb][kk], s[rb], 0, 0, 0);
+  }
 }
 
-// Online softmax of one tile in two parts (log2 units, lazy rescale):
-// softmax_max masks, takes the row maximum and rescales O when it grew by
-// more than 2^8; softmax_exp forms P and leaves P^T as bf16 MFMA operands
-// pf[u][e] (keys 32u + 16e + {4hf+t, 8+4hf+t}, t < 4).  The scores of the
-// next tile are computed between the two so that they share a basic block
-// with the exponentials.
-struct RowState { float m, l; };
-
 // IEEE maximum (NaN-propagating) needs no quieting of its MFMA-produced
-// operands, and pairs of it fuse into v_maximum3: 17 instructions for the
-// 32 scores a lane holds.
+// operands, and pairs of it fuse into v_maximum3: 8 instructions for the 16
+// scores a lane holds of one row.
 __device__ __forceinline__ float max3(float a, float b, float c) {
   return __builtin_elementwise_maximum(__builtin_elementwise_maximum(a, b), c);
 }
 
-__device__ __forceinline__ float row_max32(const f32x16 (&s)[2]) {
-  float t[11];
+__device__ __forceinline__ float row_max16(const f32x16& s) {
+  float t[5];
 #pragma unroll
-  for (int u = 0; u < 2; ++u)
-#pragma unroll
-    for (int i = 0; i < 5; ++i) t[5 * u + i] = max3(s[u][3 * i], s[u][3 * i + 1], s[u][3 * i + 2]);
-  t[10] = __builtin_elementwise_maximum(s[0][15], s[1][15]);
-  return max3(max3(t[0], t[1], t[2]), max3(t[3], t[4], t[5]),
-              max3(t[6], t[7], __builtin_elementwise_maximum(t[8], __builtin_elementwise_maximum(t[9], t[10]))));
+  for (int i = 0; i < 5; ++i) t[i] = max3(s[3 * i], s[3 * i + 1], s[3 * i + 2]);
+  return max3(max3(t[0], t[1], t[2]), t[3], __builtin_elementwise_maximum(t[4], s[15]));
 }
 
-__device__ __forceinline__ void softmax_max(f32x16 (&s)[2], RowState& st, f32x16 (&o)[4], bool mask, int lim,
+// Online softmax in log2 units with a lazy rescale.  Keys at tile offsets at
+// or past lim[rb] (per lane half) are invisible; row_max is the row maximum
+// of each block times scale * log2(e).
+__device__ __forceinline__ void apply_mask(f32x16 (&s)[kRB], const int (&lim)[kRB]) {
+#pragma unroll
+  for (int rb = 0; rb < kRB; ++rb)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) s[rb][i] = (8 * (i >> 2) + (i & 3) < lim[rb]) ? s[rb][i] : -INFINITY;
+}
+
+__device__ __forceinline__ void row_max(const f32x16 (&s)[kRB], float (&mx)[kRB], float scale_log2) {
+#pragma unroll
+  for (int rb = 0; rb < kRB; ++rb) mx[rb] = max_xor32(row_max16(s[rb])) * scale_log2;
+}
+
+// P = exp2(S scale log2(e) - m) as bf16 MFMA operands pf[rb][e] (keys 16e +
+// {4hf+t, 8+4hf+t}, t < 4).  The row sum l is taken over the bf16-rounded P
+// that the P V products use (v_dot2 of each packed pair with (1, 1)), so
+// numerator and denominator see the same weights.
+__device__ __forceinline__ void softmax_exp(f32x16 (&s)[kRB], const float (&m)[kRB], float (&l)[kRB], u32x4 (&pf)[kRB][2],
                                             float scale_log2) {
-  if (mask) {   // keys at tile offsets >= lim (this lane's half) are invisible
+  const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
 #pragma unroll
-    for (int u = 0; u < 2; ++u)
+  for (int rb = 0; rb < kRB; ++rb) {
 #pragma unroll
-      for (int i = 0; i < 16; ++i) s[u][i] = (32 * u + 8 * (i >> 2) + (i & 3) < lim) ? s[u][i] : -INFINITY;
-  }
-  float mx = row_max32(s);
-  mx = max_xor32(mx) * scale_log2;
-  if (__any(mx > st.m + kLazyRescale)) {   // lazy rescale (the final O / l is unaffected)
-    const float m_new = fmaxf(st.m, mx);
-    const float corr = fast_exp2(st.m - m_new);
-    st.l *= corr;
-#pragma unroll
-    for (int T = 0; T < 4; ++T) o[T] *= corr;
-    st.m = m_new;
-  }
-}
-
-// The row sum l is taken over the bf16-rounded P that the P V products use
-// (v_dot2 of each packed pair with (1, 1)), so numerator and denominator see
-// the same weights.
-__device__ __forceinline__ void softmax_exp(f32x16 (&s)[2], RowState& st, u32x4 (&pf)[2][2], float scale_log2) {
-#pragma unroll
-  for (int u = 0; u < 2; ++u)
-#pragma unroll
-    for (int i = 0; i < 16; ++i) s[u][i] = fast_exp2(fmaf(s[u][i], scale_log2, -st.m));
-#pragma unroll
-  for (int u = 0; u < 2; ++u)
+    for (int i = 0; i < 16; ++i) s[rb][i] = fast_exp2(fmaf(s[rb][i], scale_log2, -m[rb]));
 #pragma unroll
     for (int e = 0; e < 2; ++e)
-      pf[u][e] = u32x4{pack_bf16x2(s[u][8 * e + 0], s[u][8 * e + 1]), pack_bf16x2(s[u][8 * e + 2], s[u][8 * e + 3]),
-                       pack_bf16x2(s[u][8 * e + 4], s[u][8 * e + 5]), pack_bf16x2(s[u][8 * e + 6], s[u][8 * e + 7])};
-  const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
-  float ps[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-  for (int u = 0; u < 2; ++u)
+      pf[rb][e] = u32x4{pack_bf16x2(s[rb][8 * e + 0], s[rb][8 * e + 1]), pack_bf16x2(s[rb][8 * e + 2], s[rb][8 * e + 3]),
+                        pack_bf16x2(s[rb][8 * e + 4], s[rb][8 * e + 5]), pack_bf16x2(s[rb][8 * e + 6], s[rb][8 * e + 7])};
+    float ps[2] = {0.f, 0.f};
 #pragma unroll
     for (int e = 0; e < 2; ++e)
 #pragma unroll
       for (int w = 0; w < 4; ++w)   // the (uint32_t) copy matters: hipcc bit-casts element 0 of a vector lvalue
-        ps[w] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, (uint32_t)pf[u][e][w]), one, ps[w], false);
-  st.l += (ps[0] + ps[1]) + (ps[2] + ps[3]);
+        ps[w & 1] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, (uint32_t)pf[rb][e][w]), one,
+                                                    ps[w & 1], false);
+    l[rb] += ps[0] + ps[1];
+  }
 }
 
-// O^T += V^T P^T.  The V^T operand of MFMA (u, e), dim tile T comes from two
+// O^T += V^T P^T.  The V^T operand of MFMA e, dim tile T comes from two
 // transposing reads of natural V rows: lane group g (16 lanes) covers dims
-// 32T + 16(g%2) .. +15 and keys R = 32u + 16e + 8a + 4(g/2) .. R+3 for
-// a = 0, 1 (slots 4a .. 4a+3); source lane j of the group points at key
-// R + j/4, dims + 4(j%4) .. +3.
+// 32T + 16(g%2) .. +15 and keys R = 16e + 8a + 4(g/2) .. R+3 for a = 0, 1
+// (slots 4a .. 4a+3); source lane j of the group points at key R + j/4,
+// dims + 4(j%4) .. +3.  Each V^T fragment feeds both row blocks.
 typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 bf16x4_v;
 
-__device__ __forceinline__ void pv_tile(f32x16 (&o)[4], const LDS_AS uint8_t* vt, const u32x4 (&pf)[2][2], int lane) {
+__device__ __forceinline__ void pv_tile(f32x16 (&o)[kRB][4], const LDS_AS uint8_t* vt, const u32x4 (&pf)[kRB][2],
+                                        int lane) {
   const int g = lane >> 4, j = lane & 15;
   const LDS_AS uint8_t* base = vt + kVPitch * (4 * (g >> 1) + (j >> 2)) + 2 * (16 * (g & 1) + 4 * (j & 3));
 #pragma unroll
-  for (int u = 0; u < 2; ++u)
+  for (int e = 0; e < 2; ++e)
 #pragma unroll
-    for (int e = 0; e < 2; ++e)
+    for (int T = 0; T < 4; ++T) {
+      const bf16x4_v x0 =
+          __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LDS_AS bf16x4_v*)(base + kVPitch * (16 * e) + 64 * T));
+      const bf16x4_v x1 =
+          __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LDS_AS bf16x4_v*)(base + kVPitch * (16 * e + 8) + 64 * T));
+      const bf16x8 a = __builtin_shufflevector(x0, x1, 0, 1, 2, 3, 4, 5, 6, 7);
 #pragma unroll
-      for (int T = 0; T < 4; ++T) {
-        const bf16x4_v x0 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
-            (LDS_AS bf16x4_v*)(base + kVPitch * (32 * u + 16 * e) + 64 * T));
-        const bf16x4_v x1 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
-            (LDS_AS bf16x4_v*)(base + kVPitch * (32 * u + 16 * e + 8) + 64 * T));
-        const bf16x8 a = __builtin_shufflevector(x0, x1, 0, 1, 2, 3, 4, 5, 6, 7);
-        o[T] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, as_bf16x8(pf[u][e]), o[T], 0, 0, 0);
-      }
+      for (int rb = 0; rb < kRB; ++rb)
+        o[rb][T] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, as_bf16x8(pf[rb][e]), o[rb][T], 0, 0, 0);
+    }
 }
 
-struct WaveCtx {
-  int qrow;       // this lane's query row
-  int wq0;        // first query row of the wave
-  int n;          // sequence length
-  bool causal;
-  float scale_log2;
+struct WaveState {
+  f32x16 o[kRB][4];   // O^T: o[rb][T][4a + r] = O[query 32rb + n32][dim 32T + 8a + 4hf + r]
+  float m[kRB], l[kRB];
 };
 
-// Tile t of the wave: softmax of s_cur (tile t) and P V from vt (V_t);
-// s_next receives the scores of the tile in kt_next (tile t+1; on the wave's
-// last tile the products are computed and discarded, which keeps the matrix
-// work in the same basic block as the exponentials it overlaps).
-__device__ __forceinline__ void wave_tile(int t, f32x16 (&s_cur)[2], f32x16 (&s_next)[2],
+struct WaveCtx {
+  int wq0;          // first query row of the wave
+  int qrow[kRB];    // this lane's query row in each block
+  int n;            // sequence length
+  int wtiles;       // tiles holding keys this wave sees
+  bool causal;
+  float scale_log2;
+  // tile offsets at or past lim are invisible to this lane (per block)
+  __device__ __forceinline__ void limits(int ks, int hf, int (&lim)[kRB]) const {
+#pragma unroll
+    for (int rb = 0; rb < kRB; ++rb) lim[rb] = (causal ? min(n, qrow[rb] + 1) : n) - ks - 4 * hf;
+  }
+  __device__ __forceinline__ bool needs_mask(int ks) const {   // wave-uniform
+    return (causal && ks + kBN - 1 > wq0) || ks + kBN > n;
+  }
+};
+
+// Tile t of the wave (t < wtiles): the scores of tile t+1 (K'_{t+1} in
+// kt_next) go to s_next beside the exponentials of s_cur (tile t), then P V of
+// tile t (V_t in vt) beside the row maxima of tile t+1.  On the wave's last
+// tile the scores and maxima are computed from whatever kt_next holds and
+// discarded, which keeps the loop body one basic block apart from the masking
+// of the diagonal tiles and the (rare) rescale.  m grows to the new maxima
+// when any of them exceeds m by more than 2^8 (wave-uniform decision); O and
+// l follow, after the P V products that used the old m.
+__device__ __forceinline__ void wave_tile(int t, f32x16 (&s_cur)[kRB], f32x16 (&s_next)[kRB],
                                           const LDS_AS uint8_t* kt_next, const LDS_AS uint8_t* vt,
-                                          const bf16x8 (&qf)[8], f32x16 (&o)[4], RowState& st, const WaveCtx& w,
-                                          int lane) {
+                                          const bf16x8 (&qf)[kRB][8], WaveState& ws, const WaveCtx& w, int lane) {
   const int n32 = lane & 31, hf = lane >> 5;
-  const int ks = t * kBN;
-  const bool mask = (w.causal && ks + kBN - 1 > w.wq0) || ks + kBN > w.n;   // wave-uniform
-  const int lim = (w.causal ? min(w.n, w.qrow + 1) : w.n) - ks - 4 * hf;
-  softmax_max(s_cur, st, o, mask, lim, w.scale_log2);
+  u32x4 pf[kRB][2];
   qk_tile(s_next, kt_next, qf, n32, hf);
-  u32x4 pf[2][2];
-  softmax_exp(s_cur, st, pf, w.scale_log2);
-  pv_tile(o, vt, pf, lane);
+  softmax_exp(s_cur, ws.m, ws.l, pf, w.scale_log2);
+  pv_tile(ws.o, vt, pf, lane);
+  const int ks = (t + 1) * kBN;
+  if (w.needs_mask(ks)) {
+    int lim[kRB];
+    w.limits(ks, hf, lim);
+    apply_mask(s_next, lim);
+  }
+  float mx[kRB];
+  row_max(s_next, mx, w.scale_log2);
+  bool grow = false;
+#pragma unroll
+  for (int rb = 0; rb < kRB; ++rb) grow = grow || mx[rb] > ws.m[rb] + kLazyRescale;
+  if (t + 1 < w.wtiles && __any(grow)) {
+#pragma unroll
+    for (int rb = 0; rb < kRB; ++rb) {
+      const float m_new = __builtin_elementwise_maximum(ws.m[rb], mx[rb]);
+      const float corr = fast_exp2(ws.m[rb] - m_new);
+      ws.l[rb] *= corr;
+#pragma unroll
+      for (int T = 0; T < 4; ++T) ws.o[rb][T] *= corr;
+      ws.m[rb] = m_new;
+    }
+  }
 }
 
-// Workgroup: 4 waves x 32 query rows of one query head, 64-key tiles, two
-// workgroups per compute unit.  Pipeline per tile t (one barrier): at the
-// start of step t the loads of K'_{t+2} (into the buffer of K'_t, whose scores
-// were computed in step t-1) and of V_{t+1} (into the buffer of V_{t-1}) are
-// issued; step t computes the scores of tile t+1 and the softmax and P V of
-// tile t; the loads are waited for before the closing barrier.
-__global__ __launch_bounds__(kAttnThreads, 2) void attention_kernel(const PrefillParams p, const uint16_t* kws) {
-  __shared__ __attribute__((aligned(16))) uint8_t kt0[kKTileBytes], kt1[kKTileBytes];
-  __shared__ __attribute__((aligned(16))) uint8_t vt0[kVTileBytes], vt1[kVTileBytes];
+// Pipeline per tile t (one barrier): at the start of step t the copies of
+// K'_{t+2} (into the buffer of K'_t, whose scores were computed in step t-1)
+// and of V_{t+1} (into the buffer of V_{t-1}) are issued; step t computes the
+// scores of tile t+1 and the softmax and P V of tile t; the copies are waited
+// for before the closing barrier.
+__global__ __launch_bounds__(kAttnThreads, kWavesPerSimd) void attention_kernel(const PrefillParams p, const uint8_t* kws,
+                                                                     const uint8_t* vws) {
+  __shared__ __attribute__((aligned(16))) uint8_t kt0[kTileBytes], kt1[kTileBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t vt0[kTileBytes], vt1[kTileBytes];
   __shared__ double inv_rev[kHeadDim / 2];   // query RoPE: theta^(-2i/128) / (2 pi)
   LDS_AS uint8_t* const K0 = (LDS_AS uint8_t*)kt0;
   LDS_AS uint8_t* const K1 = (LDS_AS uint8_t*)kt1;
@@ -329,18 +343,18 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attention_kernel(const Prefil
   const int per_group = nqb * G;
   const int groups = p.batch * p.num_kv_heads;
   const int bid = blockIdx.x;
-  int grp, w;
+  int grp, wi;
   if (groups % kXcds == 0) {   // XCD-aware: a (sequence, KV head) group's workgroups share one XCD
     const int slot = bid / kXcds;
     grp = bid % kXcds + kXcds * (slot / per_group);
-    w = slot % per_group;
+    wi = slot % per_group;
   } else {
     grp = bid / per_group;
-    w = bid % per_group;
+    wi = bid % per_group;
   }
   const int b = grp / p.num_kv_heads, h = grp % p.num_kv_heads;
-  const int qb = nqb - 1 - w / G;   // heaviest block first
-  const int hq = h * G + w % G;
+  const int qb = nqb - 1 - wi / G;   // heaviest block first
+  const int hq = h * G + wi % G;
 
   int n = p.seq_lens[b];
   n = n < 0 ? 0 : (n > p.max_seq ? p.max_seq : n);
@@ -353,139 +367,157 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attention_kernel(const Prefil
   const double pos0 = (double)p.positions[b];
 
   WaveCtx wc;
-  wc.wq0 = q0 + 32 * wave;
-  wc.qrow = wc.wq0 + n32;
+  wc.wq0 = q0 + 32 * kRB * wave;
+#pragma unroll
+  for (int rb = 0; rb < kRB; ++rb) wc.qrow[rb] = wc.wq0 + 32 * rb + n32;
   wc.n = n;
   wc.causal = p.causal != 0;
   wc.scale_log2 = p.scale_log2;
   const bool wave_live = wc.wq0 < n;
-  const int wkend = !wave_live ? 0 : (wc.causal ? min(n, wc.wq0 + 32) : n);
-  const int wtiles = (wkend + kBN - 1) / kBN;   // tiles 0 .. wtiles-1 hold keys this wave sees
+  const int wkend = !wave_live ? 0 : (wc.causal ? min(n, wc.wq0 + 32 * kRB) : n);
+  wc.wtiles = (wkend + kBN - 1) / kBN;
 
-  const uint8_t* kslab = (const uint8_t*)(kws + ((int64_t)b * p.num_kv_heads + h) * p.max_seq * kHeadDim);
-  const uint8_t* vslab = (const uint8_t*)p.v + ((int64_t)b * p.v_sb + (int64_t)h * p.v_sh) * 2;
-  const uint32_t vss = (uint32_t)(p.v_ss * 2);
+  const int64_t slab = ((int64_t)b * p.num_kv_heads + h) * ws_tiles(p.max_seq) * kTileBytes;
+  const uint8_t* kslab = kws + slab;
+  const uint8_t* vslab = vws + slab;
+  const uint32_t lane_off = 16u * lane;
 
   // ---- first tiles requested before the query prologue
-  DmaLane<kKPitch> dk;
-  DmaLane<kVPitch> dv;
-  dk.init(256u, wave, lane);
-  dv.init(vss, wave, lane);
-  dma_tile<kKPitch>(k0a, kslab, 256u, dk, 0, n, wave);
-  dma_tile<kVPitch>(v0a, vslab, vss, dv, 0, n, wave);
-  if (ntiles > 1) dma_tile<kKPitch>(k1a, kslab, 256u, dk, kBN, n, wave);
+  dma_tile<kTileBytes / 1024>(k0a, kslab, lane_off, wave);
+  dma_tile<kTileBytes / 1024>(v0a, vslab, lane_off, wave);
+  if (ntiles > 1) dma_tile<kTileBytes / 1024>(k1a, kslab + kTileBytes, lane_off, wave);
   if (tid < 64 && rope) inv_rev[tid] = rope_inv_freq(tid, p.rope_log2_theta) * 0.15915494309189535;
 
-  // ---- query prologue: lane (n32, hf) owns row wq0 + n32 of head hq,
-  //      dims [32hf, 32hf+32) and [64+32hf, 64+32hf+32)
-  bf16x8 qf[8];
+  // ---- query prologue: lane (n32, hf) owns rows wq0 + n32 and wq0 + 32 + n32
+  //      of head hq, dims [32hf, 32hf+32) and [64+32hf, 64+32hf+32)
+  bf16x8 qf[kRB][8];
   {
-    u32x4 qlo[4], qhi[4];
-    if (wc.qrow < n) {
-      const uint16_t* row = (const uint16_t*)p.q + ((int64_t)b * p.q_sb + (int64_t)hq * p.q_sh + (int64_t)wc.qrow * p.q_ss);
+    u32x4 qlo[kRB][4], qhi[kRB][4];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        qlo[j] = *(const u32x4*)(row + 32 * hf + 8 * j);
-        qhi[j] = *(const u32x4*)(row + 64 + 32 * hf + 8 * j);
+    for (int rb = 0; rb < kRB; ++rb) {
+      if (wc.qrow[rb] < n) {
+        const uint16_t* row =
+            (const uint16_t*)p.q + ((int64_t)b * p.q_sb + (int64_t)hq * p.q_sh + (int64_t)wc.qrow[rb] * p.q_ss);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          qlo[rb][j] = *(const u32x4*)(row + 32 * hf + 8 * j);
+          qhi[rb][j] = *(const u32x4*)(row + 64 + 32 * hf + 8 * j);
+        }
+      } else {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) qlo[rb][j] = qhi[rb][j] = u32x4{0, 0, 0, 0};
       }
-    } else {
-#pragma unroll
-      for (int j = 0; j < 4; ++j) qlo[j] = qhi[j] = u32x4{0, 0, 0, 0};
     }
-    __builtin_amdgcn_s_waitcnt(0);   // this thread's tile loads (and q row) have landed
+    __builtin_amdgcn_s_waitcnt(0);   // this thread's tile copies (and q rows) have landed
     __syncthreads();                 // tables, K'_0, K'_1, V_0
     const uint16_t* g = (const uint16_t*)p.q_norm_w;
-    float r = 1.0f;
-    if (g) {
-      float ss = 0.f;
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const float a = bf16_elem(qlo[j], e), c = bf16_elem(qhi[j], e);
-          ss += a * a + c * c;
-        }
-      ss = sum_xor32(ss);
-      r = rsqrtf(ss * (1.0f / kHeadDim) + p.eps);
-    }
-    const double qpos = pos0 + (double)wc.qrow;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      float xl[8], xh[8];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        xl[e] = bf16_elem(qlo[j], e);
-        xh[e] = bf16_elem(qhi[j], e);
-      }
+    for (int rb = 0; rb < kRB; ++rb) {
+      float r = 1.0f;
       if (g) {
-        const u32x4 glo = *(const u32x4*)(g + 32 * hf + 8 * j);
-        const u32x4 ghi = *(const u32x4*)(g + 64 + 32 * hf + 8 * j);
+        float ss = 0.f;
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const float a = bf16_elem(qlo[rb][j], e), c = bf16_elem(qhi[rb][j], e);
+            ss += a * a + c * c;
+          }
+        ss = sum_xor32(ss);
+        r = rsqrtf(ss * (1.0f / kHeadDim) + p.eps);
+      }
+      const double qpos = pos0 + (double)wc.qrow[rb];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        float xl[8], xh[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          xl[e] *= r * bf16_elem(glo, e);
-          xh[e] *= r * bf16_elem(ghi, e);
+          xl[e] = bf16_elem(qlo[rb][j], e);
+          xh[e] = bf16_elem(qhi[rb][j], e);
         }
-      }
-      if (rope) {
+        if (g) {
+          const u32x4 glo = *(const u32x4*)(g + 32 * hf + 8 * j);
+          const u32x4 ghi = *(const u32x4*)(g + 64 + 32 * hf + 8 * j);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          float c, s;
-          rope_cos_sin_rev(qpos, inv_rev[32 * hf + 8 * j + e], c, s);
-          const float lo = xl[e], hi = xh[e];
-          xl[e] = lo * c - hi * s;
-          xh[e] = hi * c + lo * s;
+          for (int e = 0; e < 8; ++e) {
+            xl[e] *= r * bf16_elem(glo, e);
+            xh[e] *= r * bf16_elem(ghi, e);
+          }
         }
+        if (rope) {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            float c, s;
+            rope_cos_sin_rev(qpos, inv_rev[32 * hf + 8 * j + e], c, s);
+            const float lo = xl[e], hi = xh[e];
+            xl[e] = lo * c - hi * s;
+            xh[e] = hi * c + lo * s;
+          }
+        }
+        qf[rb][j] = as_bf16x8(u32x4{pack_bf16x2(xl[0], xl[1]), pack_bf16x2(xl[2], xl[3]),
+                                    pack_bf16x2(xl[4], xl[5]), pack_bf16x2(xl[6], xl[7])});
+        qf[rb][4 + j] = as_bf16x8(u32x4{pack_bf16x2(xh[0], xh[1]), pack_bf16x2(xh[2], xh[3]),
+                                        pack_bf16x2(xh[4], xh[5]), pack_bf16x2(xh[6], xh[7])});
       }
-      qf[j] = as_bf16x8(u32x4{pack_bf16x2(xl[0], xl[1]), pack_bf16x2(xl[2], xl[3]), pack_bf16x2(xl[4], xl[5]),
-                              pack_bf16x2(xl[6], xl[7])});
-      qf[4 + j] = as_bf16x8(u32x4{pack_bf16x2(xh[0], xh[1]), pack_bf16x2(xh[2], xh[3]), pack_bf16x2(xh[4], xh[5]),
-                                  pack_bf16x2(xh[6], xh[7])});
     }
   }
 
-  f32x16 o[4];
+  WaveState ws;
 #pragma unroll
-  for (int T = 0; T < 4; ++T)
+  for (int rb = 0; rb < kRB; ++rb) {
 #pragma unroll
-    for (int i = 0; i < 16; ++i) o[T][i] = 0.f;
-  RowState st = {-INFINITY, 0.f};
+    for (int T = 0; T < 4; ++T)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) ws.o[rb][T][i] = 0.f;
+    ws.l[rb] = 0.f;
+  }
 
-  f32x16 sa[2], sb[2];
-  if (wtiles > 0) qk_tile(sa, K0, qf, n32, hf);
+  f32x16 sa[kRB], sb[kRB];
+  if (wc.wtiles > 0) {   // scores and row maxima of tile 0 (every row sees key 0, so m is finite)
+    qk_tile(sa, K0, qf, n32, hf);
+    if (wc.needs_mask(0)) {
+      int lim[kRB];
+      wc.limits(0, hf, lim);
+      apply_mask(sa, lim);
+    }
+    row_max(sa, ws.m, wc.scale_log2);
+  }
   __syncthreads();   // every read of K'_0 done: its buffer takes K'_2
 
   // two tiles per trip: buffers and score registers have fixed roles in each half
   for (int t = 0; t < ntiles; t += 2) {
-    if (t + 2 < ntiles) dma_tile<kKPitch>(k0a, kslab, 256u, dk, (t + 2) * kBN, n, wave);
-    if (t + 1 < ntiles) dma_tile<kVPitch>(v1a, vslab, vss, dv, (t + 1) * kBN, n, wave);
-    if (t < wtiles) wave_tile(t, sa, sb, K1, V0, qf, o, st, wc, lane);
+    if (t + 2 < ntiles) dma_tile<kTileBytes / 1024>(k0a, kslab + (t + 2) * kTileBytes, lane_off, wave);
+    if (t + 1 < ntiles) dma_tile<kTileBytes / 1024>(v1a, vslab + (t + 1) * kTileBytes, lane_off, wave);
+    if (t < wc.wtiles) wave_tile(t, sa, sb, K1, V0, qf, ws, wc, lane);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     const int t1 = t + 1;
     if (t1 >= ntiles) break;
-    if (t1 + 2 < ntiles) dma_tile<kKPitch>(k1a, kslab, 256u, dk, (t1 + 2) * kBN, n, wave);
-    if (t1 + 1 < ntiles) dma_tile<kVPitch>(v0a, vslab, vss, dv, (t1 + 1) * kBN, n, wave);
-    if (t1 < wtiles) wave_tile(t1, sb, sa, K0, V1, qf, o, st, wc, lane);
+    if (t1 + 2 < ntiles) dma_tile<kTileBytes / 1024>(k1a, kslab + (t1 + 2) * kTileBytes, lane_off, wave);
+    if (t1 + 1 < ntiles) dma_tile<kTileBytes / 1024>(v0a, vslab + (t1 + 1) * kTileBytes, lane_off, wave);
+    if (t1 < wc.wtiles) wave_tile(t1, sb, sa, K0, V1, qf, ws, wc, lane);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
   }
-
-  // ---- epilogue: O / l for this lane's query row
+  // ---- epilogue: O / l for this lane's query rows
   if (!wave_live) return;
-  const float l = sum_xor32(st.l);
-  if (wc.qrow >= n) return;
-  const float inv = 1.0f / l;
-  uint8_t* orow = (uint8_t*)p.out + ((int64_t)b * p.o_sb + (int64_t)hq * p.o_sh + (int64_t)wc.qrow * p.o_ss) * (p.out_bf16 ? 2 : 4);
-  // o[T][4a + r] = O[query][dim 32T + 8a + 4hf + r]
 #pragma unroll
-  for (int T = 0; T < 4; ++T) {
+  for (int rb = 0; rb < kRB; ++rb) {
+    const float l = sum_xor32(ws.l[rb]);
+    if (wc.qrow[rb] >= n) continue;
+    const float inv = 1.0f / l;
+    uint8_t* orow = (uint8_t*)p.out +
+                    ((int64_t)b * p.o_sb + (int64_t)hq * p.o_sh + (int64_t)wc.qrow[rb] * p.o_ss) * (p.out_bf16 ? 2 : 4);
 #pragma unroll
-    for (int a = 0; a < 4; ++a) {
-      const int d0 = 32 * T + 8 * a + 4 * hf;
-      const float v0 = o[T][4 * a] * inv, v1 = o[T][4 * a + 1] * inv;
-      const float v2 = o[T][4 * a + 2] * inv, v3 = o[T][4 * a + 3] * inv;
-      if (p.out_bf16) *(u32x2*)(orow + 2 * d0) = u32x2{pack_bf16x2(v0, v1), pack_bf16x2(v2, v3)};
-      else *(f32x4*)(orow + 4 * d0) = f32x4{v0, v1, v2, v3};
+    for (int T = 0; T < 4; ++T) {
+#pragma unroll
+      for (int a = 0; a < 4; ++a) {
+        const int d0 = 32 * T + 8 * a + 4 * hf;
+        const float v0 = ws.o[rb][T][4 * a] * inv, v1 = ws.o[rb][T][4 * a + 1] * inv;
+        const float v2 = ws.o[rb][T][4 * a + 2] * inv, v3 = ws.o[rb][T][4 * a + 3] * inv;
+        if (p.out_bf16) *(u32x2*)(orow + 2 * d0) = u32x2{pack_bf16x2(v0, v1), pack_bf16x2(v2, v3)};
+        else *(f32x4*)(orow + 4 * d0) = f32x4{v0, v1, v2, v3};
+      }
     }
   }
 }
@@ -493,19 +525,20 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attention_kernel(const Prefil
 }  // namespace
 
 size_t prefill_workspace_bytes(int batch, int num_kv_heads, int max_seq) {
-  return (size_t)batch * num_kv_heads * max_seq * kHeadDim * 2;
+  return (size_t)batch * num_kv_heads * ws_tiles(max_seq) * kTileBytes * 2;
 }
 
 hipError_t launch_prefill_phased(const PrefillParams& p, void* workspace, hipStream_t stream) {
-  uint16_t* kws = (uint16_t*)workspace;
-  hipLaunchKernelGGL(key_prologue_kernel, dim3((p.max_seq + 15) / 16, p.num_kv_heads, p.batch), dim3(256), 0, stream, p,
-                     kws);
+  uint8_t* kws = (uint8_t*)workspace;
+  uint8_t* vws = kws + (size_t)p.batch * p.num_kv_heads * ws_tiles(p.max_seq) * kTileBytes;
+  hipLaunchKernelGGL(key_prologue_kernel, dim3((unsigned)(ws_tiles(p.max_seq) * kBN / 16), p.num_kv_heads, p.batch), dim3(256),
+                     0, stream, p, kws, vws);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   PrefillParams q = p;
   q.n_qblocks = (p.max_seq + kBM - 1) / kBM;
   hipLaunchKernelGGL(attention_kernel, dim3(q.n_qblocks * p.num_q_heads * p.batch), dim3(kAttnThreads), 0, stream, q,
-                     (const uint16_t*)kws);
+                     (const uint8_t*)kws, (const uint8_t*)vws);
   return hipGetLastError();
 }
 

@@ -195,7 +195,9 @@ gqa_status gqa_attn_decode_merge(const gqa_decode_desc* desc, const int32_t* seq
 
 /*
  * Bytes of the optional prefill workspace (host only, no HIP call):
- * B * Hkv * max_seq * 128 * 2 (one bf16 K' row per key).
+ * B * Hkv * ceil(max_seq / 32) * 9216 * 2: per 32-key tile, the bf16 K'
+ * rows (norm + RoPE applied) and a copy of the V rows, in the padded row
+ * layout the attention tiles have in on-chip memory.
  */
 gqa_status gqa_attn_prefill_workspace_size(const gqa_prefill_desc* desc, size_t* bytes);
 

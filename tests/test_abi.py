@@ -254,7 +254,8 @@ def test_decode_cache_slab_limit():
 def test_prefill_workspace_size_and_errors():
     d = pdesc()
     st, need = G.gqa_attn_prefill_workspace_size(d)
-    assert st == G.GQA_OK and need == 1 * 8 * 256 * 128 * 2
+    # K' and V regions, each 256 / 32 tiles of 9216 bytes per (sequence, KV head)
+    assert st == G.GQA_OK and need == 1 * 8 * (256 // 32) * 9216 * 2
     assert G.gqa_attn_prefill_workspace_size(None)[0] == G.GQA_ERR_NULL
     assert G.gqa_attn_prefill_workspace_size(pdesc(head_dim=64))[0] == G.GQA_ERR_UNSUPPORTED
     assert call_prefill(d, ws=FAKE, wsb=need - 1) == G.GQA_ERR_WORKSPACE
