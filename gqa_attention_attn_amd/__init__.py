@@ -28,7 +28,7 @@ GQA_F32 = 0
 GQA_BF16 = 1
 GQA_ATTN_HEAD_DIM = 128
 GQA_ATTN_MAX_GROUP = 16
-GQA_ATTN_VERSION = 1
+GQA_ATTN_VERSION = 2
 
 EXPORTS = (
     "gqa_attn_status_string",
@@ -58,7 +58,7 @@ class GqaDecodeDesc(ctypes.Structure):
         ("k_stride_b", ctypes.c_int64), ("k_stride_h", ctypes.c_int64), ("k_stride_s", ctypes.c_int64),
         ("v_stride_b", ctypes.c_int64), ("v_stride_h", ctypes.c_int64), ("v_stride_s", ctypes.c_int64),
         ("out_stride_b", ctypes.c_int64), ("out_stride_h", ctypes.c_int64),
-        ("eps", ctypes.c_float), ("scale", ctypes.c_float),
+        ("eps", ctypes.c_float), ("scale", ctypes.c_float), ("write_new_k", ctypes.c_int32),
     ]
 
 
@@ -185,7 +185,7 @@ def _ptr(t) -> Optional[int]:
 
 
 def decode_desc(q, k_cache, v_cache, out, kv_split_tokens: int = 0, eps: float = 1e-6,
-                scale: float = 0.0) -> GqaDecodeDesc:
+                scale: float = 0.0, write_new_k: bool = False) -> GqaDecodeDesc:
     """Descriptor for q [B, Hq, 128], caches [B, Hkv, S, 128], out [B, Hq, 128]."""
     B, Hq, d = q.shape
     _, Hkv, S, _ = k_cache.shape
@@ -195,7 +195,8 @@ def decode_desc(q, k_cache, v_cache, out, kv_split_tokens: int = 0, eps: float =
         q_stride_b=q.stride(0), q_stride_h=q.stride(1),
         k_stride_b=k_cache.stride(0), k_stride_h=k_cache.stride(1), k_stride_s=k_cache.stride(2),
         v_stride_b=v_cache.stride(0), v_stride_h=v_cache.stride(1), v_stride_s=v_cache.stride(2),
-        out_stride_b=out.stride(0), out_stride_h=out.stride(1), eps=float(eps), scale=float(scale))
+        out_stride_b=out.stride(0), out_stride_h=out.stride(1), eps=float(eps), scale=float(scale),
+        write_new_k=1 if write_new_k else 0)
 
 
 def prefill_desc(q, k, v, out, causal: bool = True, eps: float = 1e-6, scale: float = 0.0) -> GqaPrefillDesc:
@@ -231,12 +232,13 @@ def decode_workspace(desc: GqaDecodeDesc, device) -> "object":
 
 def decode(q, k_cache, v_cache, seq_lens, positions, q_norm_w=None, k_norm_w=None, rope_theta: float = 0.0,
            out=None, workspace=None, kv_split_tokens: int = 0, eps: float = 1e-6, scale: float = 0.0,
-           out_dtype=None, stream=None):
-    """gqa_attn_decode on torch tensors (device memory); returns out."""
+           out_dtype=None, stream=None, write_new_k: bool = False):
+    """gqa_attn_decode on torch tensors (device memory); returns out.  With
+    write_new_k, k_cache[b, :, seq_lens[b]-1] receives its post-prologue row."""
     import torch
     if out is None:
         out = torch.empty(q.shape, dtype=out_dtype or torch.float32, device=q.device)
-    desc = decode_desc(q, k_cache, v_cache, out, kv_split_tokens, eps, scale)
+    desc = decode_desc(q, k_cache, v_cache, out, kv_split_tokens, eps, scale, write_new_k)
     if workspace is None:
         workspace = decode_workspace(desc, q.device)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()

@@ -230,6 +230,7 @@ gqa_status prepare_decode(const gqa_decode_desc* d, const void* q, const void* k
   p->n_split = n;
   p->cpw = decode_chunks_per_workgroup(d, T, n);
   p->out_bf16 = d->out_dtype == GQA_BF16;
+  p->write_new_k = d->write_new_k != 0;
   p->eps = d->eps;
   p->scale_log2 = resolve_scale_log2(d->scale);
   p->rope_theta = rope_theta > 0.f ? (double)rope_theta : 0.0;

@@ -31,6 +31,7 @@ struct DecodeParams {
   int32_t split, n_split;
   int32_t cpw;            // chunks swept by one partition workgroup (1, or more when split % 32 == 0)
   int32_t out_bf16;
+  int32_t write_new_k;    // store the new key's transformed row back into the cache slot
   float eps;
   float scale_log2;       // softmax scale * log2(e): scores live in the log2 domain
   double rope_theta;      // <= 0: RoPE off

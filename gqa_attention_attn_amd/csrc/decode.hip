@@ -649,6 +649,15 @@ __global__ __launch_bounds__(kThreads, BF16 ? 2 : 1) void decode_partition_kerne
     }
     __syncthreads();
   }
+  // ---- the new key's transformed row replaces the raw one in its cache slot:
+  //      every read of that row (the prologue's and the streaming waves' step
+  //      holding it) is complete, and no other workgroup reads it
+  if (p.write_new_k && has_new && wave == kPrologueWave && lane < 32) {
+    uint8_t* row = (uint8_t*)p.k + ((int64_t)b * p.k_sb + (int64_t)h * p.k_sh + (int64_t)kn * p.k_ss) * kElem;
+    const f32x4 y = *(const f32x4*)&sm.kn[4 * lane];
+    if (BF16) *(u32x2*)(row + 8 * lane) = u32x2{pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3])};
+    else *(f32x4*)(row + 16 * lane) = y;
+  }
   // ---- the last chunk: every thread of the workgroup merges
   merge_chunk(p, sm, (nchunks - 1) & 1, b, h, cf + nchunks - 1, tid, kThreads);
 }

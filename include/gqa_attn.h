@@ -29,8 +29,9 @@
  *    loads.
  *  - The caller owns every buffer.  The library allocates nothing per call,
  *    keeps no mutable global state (calls are reentrant and thread-safe),
- *    never writes q / k / v / caches / norm weights, and writes only `out`
- *    (and `workspace`).  Calls are asynchronous on `stream`; the library
+ *    never writes q / k / v / norm weights, writes `out` (and `workspace`),
+ *    and writes a cache only where a decode descriptor asks for it
+ *    (write_new_k: the new key's own row).  Calls are asynchronous on `stream`; the library
  *    never synchronises the host.
  *  - Every argument check except GQA_ERR_HIP happens on the host before any
  *    HIP call, so a rejected call has no device side effects.  No exception
@@ -59,7 +60,7 @@ extern "C" {
 
 #define GQA_ATTN_HEAD_DIM 128
 #define GQA_ATTN_MAX_GROUP 16      /* largest supported G = Hq / Hkv in decode */
-#define GQA_ATTN_VERSION 1
+#define GQA_ATTN_VERSION 2
 
 typedef enum gqa_status {
   GQA_OK = 0,
@@ -94,6 +95,7 @@ typedef struct gqa_decode_desc {
   int64_t out_stride_b, out_stride_h;           /* out[b, h, :]                    */
   float eps;               /* RMSNorm epsilon (e.g. 1e-6)                          */
   float scale;             /* softmax scale; <= 0 selects 1/sqrt(head_dim)         */
+  int32_t write_new_k;     /* 1: store K'_{L-1} into k_cache[b, kv, L-1] (below)   */
 } gqa_decode_desc;
 
 /* Prefill: self-attention over seq_lens[b] tokens per sequence (T_q = S_kv). */
@@ -147,7 +149,16 @@ gqa_status gqa_attn_decode_workspace_size(const gqa_decode_desc* desc, size_t* b
  *   K'_{L-1} = prologue(k_cache[b, kv, L-1, :], k_norm_w, positions[b])
  *          (the raw projected key of the token being decoded)
  *   out[b, h, :] = sum_j softmax_j(scale * q' . K'_j) v_cache[b, kv, j, :]
- * Rows j >= L of the caches are never read.  The cache is not written back.
+ * Rows j >= L of the caches are never read.  With desc->write_new_k == 0 the
+ * caches are not written.  With write_new_k == 1, k_cache[b, kv, L-1, :] is
+ * overwritten with K'_{L-1} rounded to in_dtype once the call has read it
+ * ("Qwen3-14B Optimization" Shape 4: the rope phase writes the rotated key
+ * into the KV-cache slot), so that the cache holds post-prologue keys for the
+ * next step; only the one workgroup whose chunk holds slot L-1 reads or
+ * writes that row, after its own reads.  v_cache is never written (V has no
+ * prologue; its row L-1 is already in place).  When the prologue is off (no
+ * k_norm_w and rope_theta <= 0) K'_{L-1} is the raw row and nothing is
+ * written.
  *
  * q: [B, Hq, 128] (strides q_stride_*); k_cache, v_cache: [B, Hkv, max_seq,
  * 128]; seq_lens, positions: [B] int32 (device); q_norm_w, k_norm_w: [128]
