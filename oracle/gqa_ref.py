@@ -35,11 +35,13 @@ RMSNorm is x * (mean(x^2) + eps)^-1/2 * gamma over one head's d elements
 rotation of pairs (i, i + d/2) by angle p * theta^(-2i/d); in decode only the
 new token's K row (slot L-1) goes through the prologue; L = 0 gives a zero
 output row and L is clamped to the cache capacity; the causal rule includes
-the diagonal (key j visible to query i iff j <= i).
+the diagonal (key j visible to query i iff j <= i); a prefill chunk of T_q
+new tokens after P cached ones is aligned at the bottom right (query t is
+token P + t), and P, T_q are clamped to the cache capacity.
 
 Parity status: every function below is pinned by the CPU tests in
-``tests/test_oracle.py`` (closed forms, worked examples, invariants and a
-pure-Python brute force).  The composite "whole stage equals the pages' own
+``tests/test_oracle.py`` and ``tests/test_oracle_chunk.py`` (closed forms,
+worked examples, invariants and a pure-Python brute force).  The composite "whole stage equals the pages' own
 kernel" claim is parity unpinned: the pages print no attention outputs.
 """
 
@@ -62,10 +64,12 @@ __all__ = [
     "decode_ref",
     "decode_split_ref",
     "prefill_ref",
+    "prefill_chunk_ref",
     "causal_tile_class",
     "causal_tile_pairs",
     "brute_decode",
     "brute_prefill",
+    "brute_prefill_chunk",
 ]
 
 
@@ -292,6 +296,58 @@ def prefill_ref(q, k, v, seq_lens, positions, q_norm_w, k_norm_w, rope_theta: fl
     return out
 
 
+def prefill_chunk_ref(q, k_cache, v_cache, past_lens, chunk_lens, positions, q_norm_w, k_norm_w,
+                      rope_theta: float, eps: float = 1e-6, scale: Optional[float] = None,
+                      causal: bool = True, heads: Optional[Sequence[int]] = None,
+                      rows: Optional[np.ndarray] = None):
+    """Chunked prefill (ADR-0060 §5.4: a query block of T_q tokens that may be
+    a chunk of a longer sequence; §0.5.1 P2: cached K is post-RoPE and never
+    re-rotated; V is raw).
+
+    q: [B, Hq, T_max, d] raw queries of the chunk; k_cache, v_cache:
+    [B, Hkv, S_max, d].  For sequence b with P = past_lens[b] tokens already
+    in the cache and T = chunk_lens[b] new tokens (both clamped: P to
+    [0, S_max], T to [0, min(T_max, S_max - P)]), cache rows j < P hold
+    post-prologue keys, rows P <= j < P + T the raw keys of the chunk, and row
+    j sits at RoPE position positions[b] + j.  Query t of the chunk is token
+    P + t: it attends keys j <= P + t (causal, aligned at the bottom right of
+    the score matrix) or all j < P + T.  Returns out [B, Hq, T_max, d] float64
+    (rows t >= T are 0); ``heads`` / ``rows`` restrict the work as in
+    ``prefill_ref``.
+    """
+    q = np.asarray(q)
+    B, Hq, T_max, d = q.shape
+    _, Hkv, S_max, _ = k_cache.shape
+    assert Hq % Hkv == 0
+    G = Hq // Hkv
+    sc = _resolve_scale(scale, d)
+    out = np.zeros((B, Hq, T_max, d), dtype=np.float64)
+    hsel = range(Hq) if heads is None else heads
+    for b in range(B):
+        P = _clamp_len(past_lens[b], S_max)
+        T = _clamp_len(chunk_lens[b], min(T_max, S_max - P))
+        if T == 0:
+            continue
+        n = P + T
+        pos = float(positions[b]) + np.arange(n, dtype=np.float64)
+        tsel = np.arange(T) if rows is None else np.asarray([r for r in rows if r < T], dtype=np.int64)
+        if tsel.size == 0:
+            continue
+        kv = {}
+        for hq in hsel:
+            h = hq // G
+            if h not in kv:
+                K = _f64(k_cache[b, h, :n]).copy()
+                K[P:] = prologue(K[P:], k_norm_w, pos[P:], rope_theta, eps)
+                kv[h] = (K, _f64(v_cache[b, h, :n]))
+            K, V = kv[h]
+            Q = prologue(q[b, hq, tsel], q_norm_w, pos[P + tsel], rope_theta, eps)
+            vis = (np.arange(n)[None, :] <= (P + tsel)[:, None]) if causal else None
+            o, _, _ = attend(Q, K, V, sc, vis)
+            out[b, hq, tsel] = o
+    return out
+
+
 def causal_tile_class(qs: int, qe: int, ks: int, ke: int) -> str:
     """ADR-0060 §5.4: query block [qs, qe) vs key tile [ks, ke).
     ke <= qs -> 'past' (no mask, full compute); ks >= qe -> 'future' (skip);
@@ -397,4 +453,31 @@ def brute_prefill(q, k, v, seq_lens, positions, q_norm_w, k_norm_w, rope_theta: 
                 qr = _bf_prologue_row(list(q[b][hq][i]), q_norm_w, float(positions[b]) + i, rope_theta, eps)
                 m = i + 1 if causal else n
                 out[b][hq][i] = _bf_softmax_weighted(qr, keys[:m], vals[:m], sc)
+    return out
+
+
+def brute_prefill_chunk(q, k_cache, v_cache, past_lens, chunk_lens, positions, q_norm_w, k_norm_w,
+                        rope_theta: float, eps: float = 1e-6, scale: Optional[float] = None,
+                        causal: bool = True):
+    """Scalar-loop chunked prefill; returns nested lists [B][Hq][T_max][d]."""
+    B, Hq, T_max, d = len(q), len(q[0]), len(q[0][0]), len(q[0][0][0])
+    Hkv, S_max = len(k_cache[0]), len(k_cache[0][0])
+    G = Hq // Hkv
+    sc = 1.0 / math.sqrt(d) if (scale is None or scale <= 0) else scale
+    out = [[[[0.0] * d for _ in range(T_max)] for _ in range(Hq)] for _ in range(B)]
+    for b in range(B):
+        P = min(max(int(past_lens[b]), 0), S_max)
+        T = min(max(int(chunk_lens[b]), 0), min(T_max, S_max - P))
+        p0 = float(positions[b])
+        for hq in range(Hq):
+            h = hq // G
+            keys = []
+            for j in range(P + T):
+                row = [float(x) for x in k_cache[b][h][j]]
+                keys.append(row if j < P else _bf_prologue_row(row, k_norm_w, p0 + j, rope_theta, eps))
+            vals = [[float(x) for x in v_cache[b][h][j]] for j in range(P + T)]
+            for t in range(T):
+                qr = _bf_prologue_row(list(q[b][hq][t]), q_norm_w, p0 + P + t, rope_theta, eps)
+                m = P + t + 1 if causal else P + T
+                out[b][hq][t] = _bf_softmax_weighted(qr, keys[:m], vals[:m], sc)
     return out
