@@ -217,6 +217,33 @@ def prefill_case(torch, G, synth, np, two_phase=True):
     return pw, pin, t, call
 
 
+def prefill_chunk_case(torch, G, synth, np, past=3072, chunk=1024):
+    """The last `chunk` tokens of the Qwen3-14B prefill prompt as one chunk after
+    `past` cached tokens (a cache of past + chunk rows; seeded synthetic rows)."""
+    pw = synth.QWEN3_PREFILL
+    rng = np.random.Generator(np.random.PCG64(pw.seed + 100))
+    bf = torch.bfloat16
+    S = past + chunk
+    mk = lambda *shape: torch.from_numpy(rng.standard_normal(shape, dtype=np.float32)).cuda().to(bf)
+    t = dict(q=mk(1, pw.num_q_heads, chunk, 128), k=mk(1, pw.num_kv_heads, S, 128), v=mk(1, pw.num_kv_heads, S, 128),
+             qw=(1 + 0.1 * mk(128).float()).to(bf), kw=(1 + 0.1 * mk(128).float()).to(bf),
+             past=torch.tensor([past], dtype=torch.int32, device="cuda"),
+             cl=torch.tensor([chunk], dtype=torch.int32, device="cuda"),
+             pos=torch.tensor([0], dtype=torch.int32, device="cuda"))
+    t["out"] = torch.empty(t["q"].shape, dtype=torch.float32, device="cuda")
+    desc = G.prefill_chunk_desc(t["q"], t["k"], t["v"], t["out"], True, pw.eps)
+    t["ws"] = G.prefill_workspace(desc, "cuda")
+    flops = 4 * 128 * pw.num_q_heads * sum(past + i + 1 for i in range(chunk))
+
+    def call(i, stream):
+        st = G.gqa_attn_prefill_chunk(desc, t["q"].data_ptr(), t["k"].data_ptr(), t["v"].data_ptr(),
+                                      t["past"].data_ptr(), t["cl"].data_ptr(), t["pos"].data_ptr(),
+                                      t["qw"].data_ptr(), t["kw"].data_ptr(), pw.rope_theta, t["out"].data_ptr(),
+                                      t["ws"].data_ptr(), t["ws"].numel(), stream)
+        assert st == G.GQA_OK
+    return t, call, flops
+
+
 def profile_calls(args, torch, G, synth, np):
     """Plain back-to-back calls of one workload, for profiler runs."""
     if args.only in ("prefill", "prefill_fused"):
@@ -326,6 +353,17 @@ def main():
                                           "tflops": round(flops / (us_f * 1e-6) / 1e12, 2)}
         log(f"[bench] prefill single-kernel {us_f:.1f} us -> {flops / (us_f * 1e-6) / 1e12:.1f} TFLOP/s")
         del pt_inputs, pcall
+        torch.cuda.empty_cache()
+
+        ct, ccall, cflops = prefill_chunk_case(torch, G, synth, np)
+        pt = graph_time_ms(torch, ccall, pk_steps, max(2, W // 10))
+        us_c = 1000.0 * pt / pk_steps
+        tf_c = cflops / (us_c * 1e-6) / 1e12
+        extra["prefill_chunk"] = {"workload": "qwen3_14b_prefill_chunk_3072_cached_1024_new", "us_per_call": round(us_c, 2),
+                                  "tflops": round(tf_c, 2), "frac_of_bf16_peak": round(tf_c / BF16_PEAK_TFLOPS, 4),
+                                  "algorithmic_flops": cflops}
+        log(f"[bench] prefill chunk (3072 cached + 1024 new) {us_c:.1f} us -> {tf_c:.1f} TFLOP/s")
+        del ct, ccall
         torch.cuda.empty_cache()
 
         for dw in (synth.LLAMA70B_LONG, synth.QWEN3_RAGGED):

@@ -40,6 +40,7 @@ EXPORTS = (
     "gqa_attn_decode_merge",
     "gqa_attn_prefill_workspace_size",
     "gqa_attn_prefill",
+    "gqa_attn_prefill_chunk",
 )
 
 
@@ -71,7 +72,7 @@ class GqaPrefillDesc(ctypes.Structure):
         ("k_stride_b", ctypes.c_int64), ("k_stride_h", ctypes.c_int64), ("k_stride_s", ctypes.c_int64),
         ("v_stride_b", ctypes.c_int64), ("v_stride_h", ctypes.c_int64), ("v_stride_s", ctypes.c_int64),
         ("out_stride_b", ctypes.c_int64), ("out_stride_h", ctypes.c_int64), ("out_stride_s", ctypes.c_int64),
-        ("eps", ctypes.c_float), ("scale", ctypes.c_float),
+        ("eps", ctypes.c_float), ("scale", ctypes.c_float), ("max_chunk", ctypes.c_int32),
     ]
 
 
@@ -107,6 +108,9 @@ def lib() -> ctypes.CDLL:
         L.gqa_attn_prefill.argtypes = [ctypes.POINTER(GqaPrefillDesc), vp, vp, vp, vp, vp, vp, vp, ctypes.c_float,
                                        vp, vp, ctypes.c_size_t, vp]
         L.gqa_attn_prefill.restype = ctypes.c_int
+        L.gqa_attn_prefill_chunk.argtypes = [ctypes.POINTER(GqaPrefillDesc), vp, vp, vp, vp, vp, vp, vp, vp,
+                                             ctypes.c_float, vp, vp, ctypes.c_size_t, vp]
+        L.gqa_attn_prefill_chunk.restype = ctypes.c_int
         _lib = L
     return _lib
 
@@ -169,6 +173,13 @@ def gqa_attn_prefill(desc, q, k, v, seq_lens, positions, q_norm_w, k_norm_w, rop
                                       stream))
 
 
+def gqa_attn_prefill_chunk(desc, q, k_cache, v_cache, past_lens, chunk_lens, positions, q_norm_w, k_norm_w,
+                           rope_theta, out, workspace, workspace_bytes, stream) -> int:
+    return int(lib().gqa_attn_prefill_chunk(ctypes.byref(desc) if desc is not None else None, q, k_cache, v_cache,
+                                            past_lens, chunk_lens, positions, q_norm_w, k_norm_w, float(rope_theta),
+                                            out, workspace, int(workspace_bytes), stream))
+
+
 # ----------------------------------------------------------------- torch conveniences
 
 def _dtype_code(t) -> int:
@@ -211,6 +222,21 @@ def prefill_desc(q, k, v, out, causal: bool = True, eps: float = 1e-6, scale: fl
         v_stride_b=v.stride(0), v_stride_h=v.stride(1), v_stride_s=v.stride(2),
         out_stride_b=out.stride(0), out_stride_h=out.stride(1), out_stride_s=out.stride(2),
         eps=float(eps), scale=float(scale))
+
+
+def prefill_chunk_desc(q, k_cache, v_cache, out, causal: bool = True, eps: float = 1e-6,
+                       scale: float = 0.0) -> GqaPrefillDesc:
+    """Descriptor for a chunk: q / out [B, Hq, T_max, 128], caches [B, Hkv, S, 128]."""
+    B, Hq, T, d = q.shape
+    _, Hkv, S, _ = k_cache.shape
+    return GqaPrefillDesc(
+        batch=B, num_q_heads=Hq, num_kv_heads=Hkv, head_dim=d, max_seq=S, in_dtype=_dtype_code(q),
+        out_dtype=_dtype_code(out), causal=1 if causal else 0,
+        q_stride_b=q.stride(0), q_stride_h=q.stride(1), q_stride_s=q.stride(2),
+        k_stride_b=k_cache.stride(0), k_stride_h=k_cache.stride(1), k_stride_s=k_cache.stride(2),
+        v_stride_b=v_cache.stride(0), v_stride_h=v_cache.stride(1), v_stride_s=v_cache.stride(2),
+        out_stride_b=out.stride(0), out_stride_h=out.stride(1), out_stride_s=out.stride(2),
+        eps=float(eps), scale=float(scale), max_chunk=T)
 
 
 def _stream_ptr(stream) -> int:
@@ -276,4 +302,24 @@ def prefill(q, k, v, seq_lens, positions, q_norm_w=None, k_norm_w=None, rope_the
                           _ptr(k_norm_w), rope_theta, _ptr(out), _ptr(workspace), ws_bytes, _stream_ptr(stream))
     if st != GQA_OK:
         raise GqaError(st, "gqa_attn_prefill")
+    return out
+
+
+def prefill_chunk(q, k_cache, v_cache, past_lens, chunk_lens, positions, q_norm_w=None, k_norm_w=None,
+                  rope_theta: float = 0.0, out=None, causal: bool = True, eps: float = 1e-6, scale: float = 0.0,
+                  out_dtype=None, workspace=None, stream=None):
+    """gqa_attn_prefill_chunk on torch tensors (device memory); returns out.
+    workspace: a uint8 device tensor, or None to allocate one."""
+    import torch
+    if out is None:
+        out = torch.empty(q.shape, dtype=out_dtype or torch.float32, device=q.device)
+    desc = prefill_chunk_desc(q, k_cache, v_cache, out, causal, eps, scale)
+    if workspace is None:
+        workspace = prefill_workspace(desc, q.device)
+    ws_bytes = workspace.numel() * workspace.element_size()
+    st = gqa_attn_prefill_chunk(desc, _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(past_lens), _ptr(chunk_lens),
+                                _ptr(positions), _ptr(q_norm_w), _ptr(k_norm_w), rope_theta, _ptr(out),
+                                _ptr(workspace), ws_bytes, _stream_ptr(stream))
+    if st != GQA_OK:
+        raise GqaError(st, "gqa_attn_prefill_chunk")
     return out

@@ -282,26 +282,34 @@ gqa_status gqa_attn_prefill_workspace_size(const gqa_prefill_desc* desc, size_t*
   return GQA_OK;
 }
 
-gqa_status gqa_attn_prefill(const gqa_prefill_desc* d, const void* q, const void* k, const void* v,
-                            const int32_t* seq_lens, const int32_t* positions, const void* q_norm_w,
-                            const void* k_norm_w, float rope_theta, void* out, void* workspace,
-                            size_t workspace_bytes, hipStream_t stream) {
+}  // extern "C"
+
+namespace {
+
+// Shared checks and parameters of gqa_attn_prefill and gqa_attn_prefill_chunk
+// (past_lens != nullptr selects the chunked form).
+gqa_status prepare_prefill(const gqa_prefill_desc* d, const void* q, const void* k, const void* v,
+                           const int32_t* lens, const int32_t* past_lens, const int32_t* positions,
+                           const void* q_norm_w, const void* k_norm_w, float rope_theta, void* out, void* workspace,
+                           size_t workspace_bytes, gqa::PrefillParams* pp) {
   gqa_status st = check_prefill_desc(d);
   if (st != GQA_OK) return st;
-  if (q == nullptr || k == nullptr || v == nullptr || seq_lens == nullptr || positions == nullptr || out == nullptr)
+  if (q == nullptr || k == nullptr || v == nullptr || lens == nullptr || positions == nullptr || out == nullptr)
     return GQA_ERR_NULL;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) || !aligned16(q_norm_w) ||
-      !aligned16(k_norm_w) || ((uintptr_t)seq_lens & 3u) || ((uintptr_t)positions & 3u))
+      !aligned16(k_norm_w) || ((uintptr_t)lens & 3u) || ((uintptr_t)positions & 3u) || ((uintptr_t)past_lens & 3u))
     return GQA_ERR_ALIGN;
   if (workspace != nullptr) {
     if (workspace_bytes < gqa::prefill_workspace_bytes(d->batch, d->num_kv_heads, d->max_seq)) return GQA_ERR_WORKSPACE;
     if (((uintptr_t)workspace & 255u) != 0) return GQA_ERR_ALIGN;
   }
-  gqa::PrefillParams p{};
+  gqa::PrefillParams& p = *pp;
+  p = gqa::PrefillParams{};
   p.q = q;
   p.k = k;
   p.v = v;
-  p.seq_lens = seq_lens;
+  p.seq_lens = lens;
+  p.past_lens = past_lens;
   p.positions = positions;
   p.q_norm_w = q_norm_w;
   p.k_norm_w = k_norm_w;
@@ -323,6 +331,7 @@ gqa_status gqa_attn_prefill(const gqa_prefill_desc* d, const void* q, const void
   p.num_kv_heads = d->num_kv_heads;
   p.group = d->num_q_heads / d->num_kv_heads;
   p.max_seq = d->max_seq;
+  p.max_chunk = past_lens != nullptr && d->max_chunk > 0 ? d->max_chunk : d->max_seq;
   p.causal = d->causal;
   p.out_bf16 = d->out_dtype == GQA_BF16;
   prefill_blocking(p.group, &p.heads_per_wg, &p.block_q);
@@ -331,9 +340,42 @@ gqa_status gqa_attn_prefill(const gqa_prefill_desc* d, const void* q, const void
   p.scale_log2 = resolve_scale_log2(d->scale);
   p.rope_theta = rope_theta > 0.f ? (double)rope_theta : 0.0;
   p.rope_log2_theta = rope_theta > 0.f ? log2((double)rope_theta) : 0.0;
+  return GQA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+gqa_status gqa_attn_prefill(const gqa_prefill_desc* d, const void* q, const void* k, const void* v,
+                            const int32_t* seq_lens, const int32_t* positions, const void* q_norm_w,
+                            const void* k_norm_w, float rope_theta, void* out, void* workspace,
+                            size_t workspace_bytes, hipStream_t stream) {
+  gqa::PrefillParams p;
+  const gqa_status st = prepare_prefill(d, q, k, v, seq_lens, nullptr, positions, q_norm_w, k_norm_w, rope_theta,
+                                        out, workspace, workspace_bytes, &p);
+  if (st != GQA_OK) return st;
   const hipError_t e = workspace != nullptr ? gqa::launch_prefill_phased(p, workspace, stream)
                                             : gqa::launch_prefill_fused(p, stream);
   return e == hipSuccess ? GQA_OK : GQA_ERR_HIP;
+}
+
+gqa_status gqa_attn_prefill_chunk(const gqa_prefill_desc* d, const void* q, const void* k_cache,
+                                  const void* v_cache, const int32_t* past_lens, const int32_t* chunk_lens,
+                                  const int32_t* positions, const void* q_norm_w, const void* k_norm_w,
+                                  float rope_theta, void* out, void* workspace, size_t workspace_bytes,
+                                  hipStream_t stream) {
+  if (d == nullptr) return GQA_ERR_NULL;
+  if (d->max_chunk < 0) return GQA_ERR_SHAPE;
+  const int64_t tmax = d->max_chunk > 0 ? d->max_chunk : d->max_seq;
+  if ((int64_t)d->batch * d->num_q_heads * ((tmax + 31) / 32) > INT32_MAX) return GQA_ERR_SHAPE;
+  if (past_lens == nullptr) return GQA_ERR_NULL;
+  if (workspace == nullptr) return GQA_ERR_WORKSPACE;
+  gqa::PrefillParams p;
+  const gqa_status st = prepare_prefill(d, q, k_cache, v_cache, chunk_lens, past_lens, positions, q_norm_w, k_norm_w,
+                                        rope_theta, out, workspace, workspace_bytes, &p);
+  if (st != GQA_OK) return st;
+  return gqa::launch_prefill_phased(p, workspace, stream) == hipSuccess ? GQA_OK : GQA_ERR_HIP;
 }
 
 }  // extern "C"

@@ -54,6 +54,8 @@ struct PrefillParams {
   int32_t batch, num_q_heads, num_kv_heads, group, max_seq;
   int32_t causal;
   int32_t out_bf16;
+  const int32_t* past_lens;  // chunked prefill: keys already in the cache per sequence (null: none)
+  int32_t max_chunk;      // query / output rows per sequence (max_seq for a plain prefill)
   int32_t heads_per_wg;   // HC: query heads of one KV head batched in a workgroup
   int32_t block_q;        // BQ: query tokens per workgroup (multiple of 32)
   int32_t n_qblocks;      // ceil(max_seq / BQ)

@@ -60,11 +60,28 @@ static_assert(kBN * kKPitch <= kTileBytes && kBN * kVPitch == kTileBytes, "tile 
 
 __host__ __device__ inline int64_t ws_tiles(int max_seq) { return ((int64_t)max_seq + kBN - 1) / kBN; }
 
+// Extent of sequence b: P keys already in the cache (post-prologue, chunked
+// prefill only) and T new tokens; keys [0, P + T), query t is token P + t.
+// A plain prefill has P = 0.
+struct SeqExtent {
+  int past, T, n;
+};
+
+__device__ __forceinline__ SeqExtent seq_extent(const PrefillParams& p, int b) {
+  int P = p.past_lens ? p.past_lens[b] : 0;
+  P = P < 0 ? 0 : (P > p.max_seq ? p.max_seq : P);
+  const int tcap = min(p.max_chunk, p.max_seq - P);
+  int T = p.seq_lens[b];
+  T = T < 0 ? 0 : (T > tcap ? tcap : T);
+  return SeqExtent{P, T, P + T};
+}
+
 // ----------------------------------------------------------------- phase 1: key prologue
 
 // 16 key rows per workgroup; a row is held by 16 lanes (dims 4c..4c+3 and
 // 64+4c..64+4c+3), so RMSNorm reduces over 16 lanes and RoPE pairs (i, i+64)
-// stay in one lane.  The same lanes copy the row's V (16 bytes each).
+// stay in one lane.  The same lanes copy the row's V (16 bytes each).  Rows
+// below P (chunked prefill) are already post-prologue and are copied as is.
 __global__ __launch_bounds__(256) void key_prologue_kernel(const PrefillParams p, uint8_t* kws, uint8_t* vws) {
   __shared__ double inv_rev[kHeadDim / 2];
   const int b = blockIdx.z, h = blockIdx.y;
@@ -72,8 +89,8 @@ __global__ __launch_bounds__(256) void key_prologue_kernel(const PrefillParams p
   const bool rope = p.rope_theta > 0.0;
   if (tid < 64 && rope) inv_rev[tid] = rope_inv_freq(tid, p.rope_log2_theta) * 0.15915494309189535;
   __syncthreads();
-  int n = p.seq_lens[b];
-  n = n < 0 ? 0 : (n > p.max_seq ? p.max_seq : n);
+  const SeqExtent ext = seq_extent(p, b);
+  const int n = ext.n;
   const int key = blockIdx.x * 16 + r;
   const int64_t tile = ((int64_t)b * p.num_kv_heads + h) * ws_tiles(p.max_seq) + key / kBN;
   uint8_t* kd = kws + tile * kTileBytes + (key % kBN) * kKPitch;
@@ -89,6 +106,10 @@ __global__ __launch_bounds__(256) void key_prologue_kernel(const PrefillParams p
       *(const u32x4*)((const uint8_t*)p.v + ((int64_t)b * p.v_sb + (int64_t)h * p.v_sh + (int64_t)key * p.v_ss) * 2 +
                       16 * c);
   const uint16_t* src = (const uint16_t*)p.k + ((int64_t)b * p.k_sb + (int64_t)h * p.k_sh + (int64_t)key * p.k_ss);
+  if (key < ext.past) {   // cached key: already transformed
+    *(u32x4*)(kd + 16 * c) = *(const u32x4*)((const uint8_t*)src + 16 * c);
+    return;
+  }
   const u32x2 lo = *(const u32x2*)(src + 4 * c);
   const u32x2 hi = *(const u32x2*)(src + 64 + 4 * c);
   float x[8] = {bf16lo(lo[0]), bf16hi(lo[0]), bf16lo(lo[1]), bf16hi(lo[1]),
@@ -260,19 +281,20 @@ struct WaveState {
 };
 
 struct WaveCtx {
-  int wq0;          // first query row of the wave
+  int wq0;          // first query row of the wave (of the T new tokens)
   int qrow[kRB];    // this lane's query row in each block
-  int n;            // sequence length
+  int past;         // keys before the first query (query t is key P + t)
+  int n;            // keys: P + T
   int wtiles;       // tiles holding keys this wave sees
   bool causal;
   float scale_log2;
   // tile offsets at or past lim are invisible to this lane (per block)
   __device__ __forceinline__ void limits(int ks, int hf, int (&lim)[kRB]) const {
 #pragma unroll
-    for (int rb = 0; rb < kRB; ++rb) lim[rb] = (causal ? min(n, qrow[rb] + 1) : n) - ks - 4 * hf;
+    for (int rb = 0; rb < kRB; ++rb) lim[rb] = (causal ? min(n, past + qrow[rb] + 1) : n) - ks - 4 * hf;
   }
   __device__ __forceinline__ bool needs_mask(int ks) const {   // wave-uniform
-    return (causal && ks + kBN - 1 > wq0) || ks + kBN > n;
+    return (causal && ks + kBN - 1 > past + wq0) || ks + kBN > n;
   }
 };
 
@@ -356,12 +378,12 @@ __global__ __launch_bounds__(kAttnThreads, kWavesPerSimd) void attention_kernel(
   const int qb = nqb - 1 - wi / G;   // heaviest block first
   const int hq = h * G + wi % G;
 
-  int n = p.seq_lens[b];
-  n = n < 0 ? 0 : (n > p.max_seq ? p.max_seq : n);
+  const SeqExtent ext = seq_extent(p, b);
+  const int n = ext.n, T = ext.T;
   const int q0 = qb * kBM;
-  if (q0 >= n) return;
-  const int qe = min(q0 + kBM, n);
-  const int kend = p.causal ? qe : n;
+  if (q0 >= T) return;
+  const int qe = min(q0 + kBM, T);
+  const int kend = p.causal ? ext.past + qe : n;
   const int ntiles = (kend + kBN - 1) / kBN;
   const bool rope = p.rope_theta > 0.0;
   const double pos0 = (double)p.positions[b];
@@ -370,11 +392,12 @@ __global__ __launch_bounds__(kAttnThreads, kWavesPerSimd) void attention_kernel(
   wc.wq0 = q0 + 32 * kRB * wave;
 #pragma unroll
   for (int rb = 0; rb < kRB; ++rb) wc.qrow[rb] = wc.wq0 + 32 * rb + n32;
+  wc.past = ext.past;
   wc.n = n;
   wc.causal = p.causal != 0;
   wc.scale_log2 = p.scale_log2;
-  const bool wave_live = wc.wq0 < n;
-  const int wkend = !wave_live ? 0 : (wc.causal ? min(n, wc.wq0 + 32 * kRB) : n);
+  const bool wave_live = wc.wq0 < T;
+  const int wkend = !wave_live ? 0 : (wc.causal ? min(n, ext.past + wc.wq0 + 32 * kRB) : n);
   wc.wtiles = (wkend + kBN - 1) / kBN;
 
   const int64_t slab = ((int64_t)b * p.num_kv_heads + h) * ws_tiles(p.max_seq) * kTileBytes;
@@ -395,7 +418,7 @@ __global__ __launch_bounds__(kAttnThreads, kWavesPerSimd) void attention_kernel(
     u32x4 qlo[kRB][4], qhi[kRB][4];
 #pragma unroll
     for (int rb = 0; rb < kRB; ++rb) {
-      if (wc.qrow[rb] < n) {
+      if (wc.qrow[rb] < T) {
         const uint16_t* row =
             (const uint16_t*)p.q + ((int64_t)b * p.q_sb + (int64_t)hq * p.q_sh + (int64_t)wc.qrow[rb] * p.q_ss);
 #pragma unroll
@@ -426,7 +449,7 @@ __global__ __launch_bounds__(kAttnThreads, kWavesPerSimd) void attention_kernel(
         ss = sum_xor32(ss);
         r = rsqrtf(ss * (1.0f / kHeadDim) + p.eps);
       }
-      const double qpos = pos0 + (double)wc.qrow[rb];
+      const double qpos = pos0 + (double)(ext.past + wc.qrow[rb]);
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         float xl[8], xh[8];
@@ -504,7 +527,7 @@ __global__ __launch_bounds__(kAttnThreads, kWavesPerSimd) void attention_kernel(
 #pragma unroll
   for (int rb = 0; rb < kRB; ++rb) {
     const float l = sum_xor32(ws.l[rb]);
-    if (wc.qrow[rb] >= n) continue;
+    if (wc.qrow[rb] >= T) continue;
     const float inv = 1.0f / l;
     uint8_t* orow = (uint8_t*)p.out +
                     ((int64_t)b * p.o_sb + (int64_t)hq * p.o_sh + (int64_t)wc.qrow[rb] * p.o_ss) * (p.out_bf16 ? 2 : 4);
@@ -536,7 +559,7 @@ hipError_t launch_prefill_phased(const PrefillParams& p, void* workspace, hipStr
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   PrefillParams q = p;
-  q.n_qblocks = (p.max_seq + kBM - 1) / kBM;
+  q.n_qblocks = (p.max_chunk + kBM - 1) / kBM;
   hipLaunchKernelGGL(attention_kernel, dim3(q.n_qblocks * p.num_q_heads * p.batch), dim3(kAttnThreads), 0, stream, q,
                      (const uint8_t*)kws, (const uint8_t*)vws);
   return hipGetLastError();

@@ -114,6 +114,8 @@ typedef struct gqa_prefill_desc {
   int64_t out_stride_b, out_stride_h, out_stride_s;
   float eps;
   float scale;             /* <= 0 selects 1/sqrt(head_dim)                        */
+  int32_t max_chunk;       /* gqa_attn_prefill_chunk only: query / output rows per
+                              sequence (T_max); 0 means max_seq                   */
 } gqa_prefill_desc;
 
 /* Human-readable name of a status code (static storage; never NULL). */
@@ -241,6 +243,41 @@ gqa_status gqa_attn_prefill(const gqa_prefill_desc* desc, const void* q, const v
                             const int32_t* seq_lens, const int32_t* positions, const void* q_norm_w,
                             const void* k_norm_w, float rope_theta, void* out, void* workspace,
                             size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * Chunked prefill ("ADR-0060: AHBM GQA Fused Attention Kernel (Llama3-70B)"
+ * section 5.4: a query block of T_q tokens that may be a chunk of a longer
+ * sequence; section 0.5.1 P2: cached keys are post-RoPE and never re-rotated).
+ *
+ * For sequence b, P = clamp(past_lens[b], 0, max_seq) tokens are already in
+ * the cache and T = clamp(chunk_lens[b], 0, min(T_max, max_seq - P)) new
+ * tokens follow (T_max = desc->max_chunk, or max_seq when 0).  Cache row j
+ * sits at RoPE position positions[b] + j.  Rows j < P of k_cache hold
+ * post-prologue keys; rows P <= j < P + T hold the raw projected keys of the
+ * chunk, v_cache rows j < P + T the values.  Query t of the chunk (q[b, h, t],
+ * raw) is token P + t: it goes through the prologue at position
+ * positions[b] + P + t and attends keys j <= P + t (causal: the causal mask
+ * is aligned at the bottom right of the T x (P + T) score matrix) or all
+ * j < P + T (non-causal), of KV head floor(h / G):
+ *   out[b, h, t, :] = sum_j softmax_j(scale * q'_t . K'_j) v_cache[b, kv, j, :]
+ * Rows t >= T of out are not written; cache rows j >= P + T are not read; the
+ * caches are not written.  With P = 0 this is gqa_attn_prefill over the chunk.
+ *
+ * q, out: [B, Hq, T_max, 128] (strides q_stride_* / out_stride_*); k_cache,
+ * v_cache: [B, Hkv, max_seq, 128]; past_lens, chunk_lens, positions: [B]
+ * int32 (device).  in_dtype must be GQA_BF16.  workspace is required
+ * (gqa_attn_prefill_workspace_size bytes for the same descriptor, 256-byte
+ * aligned, contents on entry ignored): the key prologue of the chunk rows
+ * and the copy of the cached rows into the attention tile layout run first,
+ * then the attention kernel.
+ * Errors: as gqa_attn_prefill; GQA_ERR_NULL also for past_lens,
+ * GQA_ERR_WORKSPACE for a missing workspace, GQA_ERR_SHAPE for max_chunk < 0.
+ */
+gqa_status gqa_attn_prefill_chunk(const gqa_prefill_desc* desc, const void* q, const void* k_cache,
+                                  const void* v_cache, const int32_t* past_lens, const int32_t* chunk_lens,
+                                  const int32_t* positions, const void* q_norm_w, const void* k_norm_w,
+                                  float rope_theta, void* out, void* workspace, size_t workspace_bytes,
+                                  hipStream_t stream);
 
 #ifdef __cplusplus
 }

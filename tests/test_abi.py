@@ -260,3 +260,25 @@ def test_prefill_workspace_size_and_errors():
     assert G.gqa_attn_prefill_workspace_size(pdesc(head_dim=64))[0] == G.GQA_ERR_UNSUPPORTED
     assert call_prefill(d, ws=FAKE, wsb=need - 1) == G.GQA_ERR_WORKSPACE
     assert call_prefill(d, ws=FAKE + 16, wsb=need) == G.GQA_ERR_ALIGN
+
+
+def call_chunk(d, q=FAKE, k=FAKE, v=FAKE, past=FAKE, cl=FAKE, pos=FAKE, qw=NULL, kw=NULL, out=FAKE, ws=FAKE,
+               wsb=1 << 40):
+    return G.gqa_attn_prefill_chunk(d, q, k, v, past, cl, pos, qw, kw, 1e6, out, ws, wsb, None)
+
+
+def test_prefill_chunk_errors():
+    d = pdesc(max_chunk=64)
+    assert G.gqa_attn_prefill_chunk(None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, NULL, NULL, 1e6, FAKE, FAKE, 1, None) \
+        == G.GQA_ERR_NULL
+    assert call_chunk(d, past=NULL) == G.GQA_ERR_NULL
+    assert call_chunk(d, cl=NULL) == G.GQA_ERR_NULL
+    assert call_chunk(d, ws=NULL) == G.GQA_ERR_WORKSPACE                  # the chunked form needs a workspace
+    assert call_chunk(pdesc(max_chunk=-1)) == G.GQA_ERR_SHAPE
+    st, need = G.gqa_attn_prefill_workspace_size(d)                        # sized by the cache capacity
+    assert st == G.GQA_OK and need == G.gqa_attn_prefill_workspace_size(pdesc())[1]
+    assert call_chunk(d, wsb=need - 1) == G.GQA_ERR_WORKSPACE
+    assert call_chunk(d, ws=FAKE + 16, wsb=need) == G.GQA_ERR_ALIGN
+    assert call_chunk(d, past=FAKE + 2, wsb=need) == G.GQA_ERR_ALIGN
+    assert call_chunk(pdesc(max_chunk=64, head_dim=64), wsb=need) == G.GQA_ERR_UNSUPPORTED
+    assert call_chunk(pdesc(max_chunk=64, in_dtype=G.GQA_F32), wsb=need) == G.GQA_ERR_UNSUPPORTED
