@@ -63,6 +63,8 @@ __all__ = [
     "finalize",
     "decode_ref",
     "decode_split_ref",
+    "paged_gather",
+    "decode_paged_ref",
     "prefill_ref",
     "prefill_chunk_ref",
     "causal_tile_class",
@@ -250,6 +252,32 @@ def decode_split_ref(q, k_cache, v_cache, seq_lens, positions, q_norm_w, k_norm_
                 st = merge(st, parts[c])
             out[b, h * G:(h + 1) * G] = finalize(st)
     return out
+
+
+def paged_gather(pages, block_table, seq_lens, block_size: int, max_seq: int) -> np.ndarray:
+    """Logical cache [B, Hkv, max_seq, d] of a paged cache: logical row j of
+    sequence b is pages[block_table[b, j // bs], :, j % bs].  Only the blocks
+    that hold rows below seq_lens[b] are read; other rows are NaN."""
+    pages = np.asarray(pages)
+    _, Hkv, bs, d = pages.shape
+    assert bs == block_size and max_seq % bs == 0
+    B = len(seq_lens)
+    out = np.full((B, Hkv, max_seq, d), np.nan, dtype=np.float64)
+    for b in range(B):
+        L = _clamp_len(seq_lens[b], max_seq)
+        for i in range(-(-L // bs)):
+            out[b, :, i * bs:(i + 1) * bs] = pages[int(block_table[b][i])]
+    return out
+
+
+def decode_paged_ref(q, k_pages, v_pages, block_table, seq_lens, positions, q_norm_w, k_norm_w,
+                     rope_theta: float, block_size: int, eps: float = 1e-6, scale: Optional[float] = None):
+    """Decode over a paged cache: the plain decode of the logical cache that
+    the block table describes (paging is addressing only)."""
+    max_seq = np.asarray(block_table).shape[1] * block_size
+    K = paged_gather(k_pages, block_table, seq_lens, block_size, max_seq)
+    V = paged_gather(v_pages, block_table, seq_lens, block_size, max_seq)
+    return decode_ref(q, K, V, seq_lens, positions, q_norm_w, k_norm_w, rope_theta, eps, scale)
 
 
 # --------------------------------------------------------------------------
