@@ -244,6 +244,50 @@ def prefill_chunk_case(torch, G, synth, np, past=3072, chunk=1024):
     return t, call, flops
 
 
+def paged_decode_case(torch, G, synth, np, w, bs):
+    """A decode workload over a paged cache of bs-row pages (shuffled pool with
+    exactly the pages the lengths need; seeded synthetic rows)."""
+    rng = np.random.Generator(np.random.PCG64(w.seed + 200))
+    lens = synth.lengths_of(w)
+    nb = w.max_seq // bs
+    used = [-(-int(L) // bs) for L in lens]
+    npages = sum(used)
+    bf = torch.bfloat16
+    kp = torch.randn(npages, w.num_kv_heads, bs, 128, device="cuda", dtype=bf)
+    vp = torch.randn(npages, w.num_kv_heads, bs, 128, device="cuda", dtype=bf)
+    perm = rng.permutation(npages)
+    table = np.full((w.batch, nb), -1, dtype=np.int32)
+    k = 0
+    for b, u in enumerate(used):
+        table[b, :u] = perm[k:k + u]
+        k += u
+    t = dict(q=torch.randn(w.batch, w.num_q_heads, 128, device="cuda", dtype=bf), kp=kp, vp=vp,
+             table=torch.from_numpy(table).cuda(), sl=torch.from_numpy(lens).cuda(),
+             pos=torch.from_numpy(np.maximum(lens, 1) - 1).cuda(),
+             qw=(1 + 0.1 * torch.randn(128, device="cuda")).to(bf) if w.qk_norm else None,
+             kw=(1 + 0.1 * torch.randn(128, device="cuda")).to(bf) if w.qk_norm else None)
+    t["out"] = torch.empty(w.batch, w.num_q_heads, 128, device="cuda", dtype=torch.float32)
+    q, out = t["q"], t["out"]
+    desc = G.GqaDecodeDesc(batch=w.batch, num_q_heads=w.num_q_heads, num_kv_heads=w.num_kv_heads, head_dim=128,
+                           max_seq=w.max_seq, in_dtype=G.GQA_BF16, out_dtype=G.GQA_F32,
+                           kv_split_tokens=w.split_tokens, q_stride_b=q.stride(0), q_stride_h=q.stride(1),
+                           k_stride_b=kp.stride(0), k_stride_h=kp.stride(1), k_stride_s=kp.stride(2),
+                           v_stride_b=vp.stride(0), v_stride_h=vp.stride(1), v_stride_s=vp.stride(2),
+                           out_stride_b=out.stride(0), out_stride_h=out.stride(1), eps=w.eps, scale=0.0,
+                           block_size=bs)
+    st, nbytes = G.gqa_attn_decode_workspace_size(desc)
+    assert st == G.GQA_OK
+    t["ws"] = torch.empty(max(nbytes, 256), dtype=torch.uint8, device="cuda")
+    ptr = lambda x: None if x is None else x.data_ptr()
+
+    def call(i, stream):
+        st = G.gqa_attn_decode_paged(desc, q.data_ptr(), kp.data_ptr(), vp.data_ptr(), t["table"].data_ptr(),
+                                     t["sl"].data_ptr(), t["pos"].data_ptr(), ptr(t["qw"]), ptr(t["kw"]),
+                                     w.rope_theta, out.data_ptr(), t["ws"].data_ptr(), t["ws"].numel(), stream)
+        assert st == G.GQA_OK
+    return t, call, decode_bytes(lens, w.num_kv_heads, w.num_q_heads, w.batch)
+
+
 def profile_calls(args, torch, G, synth, np):
     """Plain back-to-back calls of one workload, for profiler runs."""
     if args.only in ("prefill", "prefill_fused"):
@@ -365,6 +409,17 @@ def main():
         log(f"[bench] prefill chunk (3072 cached + 1024 new) {us_c:.1f} us -> {tf_c:.1f} TFLOP/s")
         del ct, ccall
         torch.cuda.empty_cache()
+
+        for dw, bs in ((synth.LLAMA70B_LONG, 256), (synth.QWEN3_RAGGED, 64)):
+            pt_, pcall_, pbytes = paged_decode_case(torch, G, synth, np, dw, bs)
+            steps = max(5, K // 10)
+            t = graph_time_ms(torch, pcall_, steps, 2)
+            us = 1000.0 * t / steps
+            extra[dw.name + "_paged"] = {"block_size": bs, "us_per_step": round(us, 2),
+                                         "gbs": round(pbytes / (us * 1e-6) / 1e9, 1), "algorithmic_bytes": pbytes}
+            log(f"[bench] {dw.name} paged (bs={bs}): {us:.1f} us/step, {pbytes / (us * 1e-6) / 1e9:.0f} GB/s")
+            del pt_, pcall_
+            torch.cuda.empty_cache()
 
         for dw in (synth.LLAMA70B_LONG, synth.QWEN3_RAGGED):
             nb = decode_bytes(synth.lengths_of(dw), dw.num_kv_heads, dw.num_q_heads, dw.batch)

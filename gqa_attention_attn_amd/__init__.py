@@ -38,6 +38,7 @@ EXPORTS = (
     "gqa_attn_decode",
     "gqa_attn_decode_partition",
     "gqa_attn_decode_merge",
+    "gqa_attn_decode_paged",
     "gqa_attn_prefill_workspace_size",
     "gqa_attn_prefill",
     "gqa_attn_prefill_chunk",
@@ -60,6 +61,7 @@ class GqaDecodeDesc(ctypes.Structure):
         ("v_stride_b", ctypes.c_int64), ("v_stride_h", ctypes.c_int64), ("v_stride_s", ctypes.c_int64),
         ("out_stride_b", ctypes.c_int64), ("out_stride_h", ctypes.c_int64),
         ("eps", ctypes.c_float), ("scale", ctypes.c_float), ("write_new_k", ctypes.c_int32),
+        ("block_size", ctypes.c_int32),
     ]
 
 
@@ -103,6 +105,9 @@ def lib() -> ctypes.CDLL:
         L.gqa_attn_decode_partition.restype = ctypes.c_int
         L.gqa_attn_decode_merge.argtypes = [ctypes.POINTER(GqaDecodeDesc), vp, vp, vp, ctypes.c_size_t, vp]
         L.gqa_attn_decode_merge.restype = ctypes.c_int
+        L.gqa_attn_decode_paged.argtypes = [ctypes.POINTER(GqaDecodeDesc), vp, vp, vp, vp, vp, vp, vp, vp,
+                                            ctypes.c_float, vp, vp, ctypes.c_size_t, vp]
+        L.gqa_attn_decode_paged.restype = ctypes.c_int
         L.gqa_attn_prefill_workspace_size.argtypes = [ctypes.POINTER(GqaPrefillDesc), szp]
         L.gqa_attn_prefill_workspace_size.restype = ctypes.c_int
         L.gqa_attn_prefill.argtypes = [ctypes.POINTER(GqaPrefillDesc), vp, vp, vp, vp, vp, vp, vp, ctypes.c_float,
@@ -157,6 +162,13 @@ def gqa_attn_decode_partition(desc, q, k_cache, v_cache, seq_lens, positions, q_
 def gqa_attn_decode_merge(desc, seq_lens, out, workspace, workspace_bytes, stream) -> int:
     return int(lib().gqa_attn_decode_merge(ctypes.byref(desc) if desc is not None else None, seq_lens, out,
                                            workspace, int(workspace_bytes), stream))
+
+
+def gqa_attn_decode_paged(desc, q, k_pages, v_pages, block_table, seq_lens, positions, q_norm_w, k_norm_w,
+                          rope_theta, out, workspace, workspace_bytes, stream) -> int:
+    return int(lib().gqa_attn_decode_paged(ctypes.byref(desc) if desc is not None else None, q, k_pages, v_pages,
+                                           block_table, seq_lens, positions, q_norm_w, k_norm_w, float(rope_theta),
+                                           out, workspace, int(workspace_bytes), stream))
 
 
 def gqa_attn_prefill_workspace_size(desc: Optional[GqaPrefillDesc]) -> Tuple[int, int]:
@@ -322,4 +334,34 @@ def prefill_chunk(q, k_cache, v_cache, past_lens, chunk_lens, positions, q_norm_
                                 _ptr(workspace), ws_bytes, _stream_ptr(stream))
     if st != GQA_OK:
         raise GqaError(st, "gqa_attn_prefill_chunk")
+    return out
+
+
+def decode_paged(q, k_pages, v_pages, block_table, seq_lens, positions, q_norm_w=None, k_norm_w=None,
+                 rope_theta: float = 0.0, out=None, workspace=None, kv_split_tokens: int = 0, eps: float = 1e-6,
+                 scale: float = 0.0, out_dtype=None, stream=None, write_new_k: bool = False):
+    """gqa_attn_decode_paged on torch tensors: k_pages / v_pages [num_pages, Hkv, bs, 128],
+    block_table [B, max_blocks] int32 (max_seq = max_blocks * bs); returns out."""
+    import torch
+    if out is None:
+        out = torch.empty(q.shape, dtype=out_dtype or torch.float32, device=q.device)
+    B, Hq, d = q.shape
+    _, Hkv, bs, _ = k_pages.shape
+    max_seq = block_table.shape[1] * bs
+    desc = GqaDecodeDesc(
+        batch=B, num_q_heads=Hq, num_kv_heads=Hkv, head_dim=d, max_seq=max_seq, in_dtype=_dtype_code(q),
+        out_dtype=_dtype_code(out), kv_split_tokens=int(kv_split_tokens),
+        q_stride_b=q.stride(0), q_stride_h=q.stride(1),
+        k_stride_b=k_pages.stride(0), k_stride_h=k_pages.stride(1), k_stride_s=k_pages.stride(2),
+        v_stride_b=v_pages.stride(0), v_stride_h=v_pages.stride(1), v_stride_s=v_pages.stride(2),
+        out_stride_b=out.stride(0), out_stride_h=out.stride(1), eps=float(eps), scale=float(scale),
+        write_new_k=1 if write_new_k else 0, block_size=bs)
+    if workspace is None:
+        workspace = decode_workspace(desc, q.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = gqa_attn_decode_paged(desc, _ptr(q), _ptr(k_pages), _ptr(v_pages), _ptr(block_table), _ptr(seq_lens),
+                               _ptr(positions), _ptr(q_norm_w), _ptr(k_norm_w), rope_theta, _ptr(out),
+                               _ptr(workspace), ws_bytes, _stream_ptr(stream))
+    if st != GQA_OK:
+        raise GqaError(st, "gqa_attn_decode_paged")
     return out

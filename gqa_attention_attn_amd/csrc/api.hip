@@ -29,6 +29,10 @@ gqa_status check_decode_desc(const gqa_decode_desc* d) {
   if ((int64_t)d->batch * d->num_q_heads > INT32_MAX) return GQA_ERR_SHAPE;   // merge grid
   if (d->num_q_heads % d->num_kv_heads != 0) return GQA_ERR_SHAPE;
   if (d->kv_split_tokens < 0) return GQA_ERR_SHAPE;
+  if (d->block_size != 0) {   // paged: a power of two >= 32 rows per page, whole pages
+    if (d->block_size < 32 || (d->block_size & (d->block_size - 1)) != 0 || d->max_seq % d->block_size != 0)
+      return GQA_ERR_SHAPE;
+  }
   if (d->head_dim != GQA_ATTN_HEAD_DIM) return GQA_ERR_UNSUPPORTED;
   if (d->num_q_heads / d->num_kv_heads > GQA_ATTN_MAX_GROUP) return GQA_ERR_UNSUPPORTED;
   if (!dtype_ok(d->in_dtype) || !dtype_ok(d->out_dtype)) return GQA_ERR_UNSUPPORTED;
@@ -65,6 +69,8 @@ void decode_plan(const gqa_decode_desc* d, int32_t* T, int32_t* n) {
     if (t < 128) t = 128;
     if (t > d->max_seq) t = d->max_seq;
   }
+  if (d->block_size != 0 && t < d->max_seq) t = (t + 31) / 32 * 32;   // paged: steps never straddle pages
+  if (t > d->max_seq) t = d->max_seq;
   *T = (int32_t)t;
   *n = (int32_t)(((int64_t)d->max_seq + t - 1) / t);
 }
@@ -180,9 +186,13 @@ namespace {
 gqa_status prepare_decode(const gqa_decode_desc* d, const void* q, const void* k_cache, const void* v_cache,
                           const int32_t* seq_lens, const int32_t* positions, const void* q_norm_w,
                           const void* k_norm_w, float rope_theta, void* out, void* workspace,
-                          size_t workspace_bytes, bool need_inputs, gqa::DecodeParams* p) {
+                          size_t workspace_bytes, bool need_inputs, gqa::DecodeParams* p,
+                          const int32_t* block_table = nullptr) {
   const gqa_status st = check_decode_desc(d);
   if (st != GQA_OK) return st;
+  // a paged descriptor (block_size > 0) goes with gqa_attn_decode_paged only
+  if (need_inputs && (d->block_size != 0) != (block_table != nullptr)) return GQA_ERR_SHAPE;
+  if ((uintptr_t)block_table & 3u) return GQA_ERR_ALIGN;
   if (seq_lens == nullptr || out == nullptr) return GQA_ERR_NULL;
   if (need_inputs && (q == nullptr || k_cache == nullptr || v_cache == nullptr || positions == nullptr))
     return GQA_ERR_NULL;
@@ -231,6 +241,11 @@ gqa_status prepare_decode(const gqa_decode_desc* d, const void* q, const void* k
   p->cpw = decode_chunks_per_workgroup(d, T, n);
   p->out_bf16 = d->out_dtype == GQA_BF16;
   p->write_new_k = d->write_new_k != 0;
+  if (block_table != nullptr) {
+    p->block_table = block_table;
+    p->block_log2 = __builtin_ctz((unsigned)d->block_size);
+    p->max_blocks = d->max_seq / d->block_size;
+  }
   p->eps = d->eps;
   p->scale_log2 = resolve_scale_log2(d->scale);
   p->rope_theta = rope_theta > 0.f ? (double)rope_theta : 0.0;
@@ -269,6 +284,21 @@ gqa_status gqa_attn_decode(const gqa_decode_desc* d, const void* q, const void* 
   gqa::DecodeParams p;
   const gqa_status st = prepare_decode(d, q, k_cache, v_cache, seq_lens, positions, q_norm_w, k_norm_w, rope_theta,
                                        out, workspace, workspace_bytes, true, &p);
+  if (st != GQA_OK) return st;
+  if (gqa::launch_decode_partition(p, d->in_dtype == GQA_BF16, stream) != hipSuccess) return GQA_ERR_HIP;
+  return gqa::launch_decode_merge(p, stream) == hipSuccess ? GQA_OK : GQA_ERR_HIP;
+}
+
+gqa_status gqa_attn_decode_paged(const gqa_decode_desc* d, const void* q, const void* k_pages, const void* v_pages,
+                                 const int32_t* block_table, const int32_t* seq_lens, const int32_t* positions,
+                                 const void* q_norm_w, const void* k_norm_w, float rope_theta, void* out,
+                                 void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  if (d == nullptr) return GQA_ERR_NULL;
+  if (d->block_size == 0) return GQA_ERR_SHAPE;
+  if (block_table == nullptr) return GQA_ERR_NULL;
+  gqa::DecodeParams p;
+  const gqa_status st = prepare_decode(d, q, k_pages, v_pages, seq_lens, positions, q_norm_w, k_norm_w, rope_theta,
+                                       out, workspace, workspace_bytes, true, &p, block_table);
   if (st != GQA_OK) return st;
   if (gqa::launch_decode_partition(p, d->in_dtype == GQA_BF16, stream) != hipSuccess) return GQA_ERR_HIP;
   return gqa::launch_decode_merge(p, stream) == hipSuccess ? GQA_OK : GQA_ERR_HIP;

@@ -32,6 +32,9 @@ struct DecodeParams {
   int32_t cpw;            // chunks swept by one partition workgroup (1, or more when split % 32 == 0)
   int32_t out_bf16;
   int32_t write_new_k;    // store the new key's transformed row back into the cache slot
+  const int32_t* block_table;  // paged caches: [B][max_blocks] page of each block of rows (null: contiguous)
+  int32_t block_log2;     // paged: log2(rows per page)
+  int32_t max_blocks;     // paged: row length of block_table
   float eps;
   float scale_log2;       // softmax scale * log2(e): scores live in the log2 domain
   double rope_theta;      // <= 0: RoPE off

@@ -133,26 +133,63 @@ __device__ __forceinline__ constexpr int vkey_t(int t) { return t < 4 ? t : 12 +
 // Addressing of one (b, KV head) slab: a uniform 64-bit base plus 32-bit byte
 // offsets (the host guarantees the slab spans less than 4 GiB).  The per-lane
 // parts of the offsets are fixed for the whole sweep.
+// K / V rows of one (sequence, KV head).  Contiguous: row j at kb + j * kss.
+// Paged: logical row j at kb + block_table[j >> log2bs] * kpage + (j % bs) * kss;
+// steps start at multiples of 32 keys and pages hold a power of two >= 32
+// rows, so the 32 rows of a step always share one page.
+template <bool PAGED>
 struct Slab {
   const uint8_t* kb;
   const uint8_t* vb;
   uint32_t kss, vss;     // row strides in bytes
   uint32_t klane, vlane; // per-lane byte offsets
+  const int32_t* bt;     // paged: this sequence's row of the block table
+  int log2bs;            // paged: log2(rows per page)
+  int64_t kpage, vpage;  // paged: page strides in bytes
+
+  // The page holding key (paged; 0 otherwise).  key is clamped below kend,
+  // so the table entry read is one of the sequence's own blocks.  The sweep
+  // requests it one step ahead of the loads that use it.
+  __device__ __forceinline__ int page_of(int key, int kend) const {
+    if constexpr (PAGED) return bt[min(key, kend - 1) >> log2bs];
+    else return 0;
+  }
+  // base pointers of `page` (the one holding key0) and key0's row index in it
+  __device__ __forceinline__ const uint8_t* kbase(int key0, int page, int& rel) const {
+    if constexpr (PAGED) {
+      rel = key0 & ((1 << log2bs) - 1);
+      return kb + (int64_t)page * kpage;
+    } else {
+      rel = key0;
+      return kb;
+    }
+  }
+  __device__ __forceinline__ const uint8_t* vbase(int key0, int page, int& rel) const {
+    if constexpr (PAGED) {
+      rel = key0 & ((1 << log2bs) - 1);
+      return vb + (int64_t)page * vpage;
+    } else {
+      rel = key0;
+      return vb;
+    }
+  }
 };
 
 // Loads of one step.  FULL: every row of the step is below kend, no
 // predication.  !FULL (the last step of a chunk): rows at or past kend are
 // replaced by row kend-1 (always valid) and the loaded values are zeroed, so
 // rows past the sequence are never read and the code stays branch-free.
-template <bool FULL>
-__device__ __forceinline__ void load_k(StepBF16& st, const Slab& sl, int key0, int kend, int n16, int q4) {
+template <bool FULL, class SL>
+__device__ __forceinline__ void load_k(StepBF16& st, const SL& sl, int key0, int kend, int n16, int q4, int page) {
+  int rel;
+  const uint8_t* kb = sl.kbase(key0, page, rel);
 #pragma unroll
   for (int gi = 0; gi < 2; ++gi) {
     const int key = key0 + 16 * gi + n16;
     const bool ok = FULL || key < kend;
-    const uint32_t off = FULL ? (uint32_t)(key0 + 16 * gi) * sl.kss + sl.klane
-                              : (uint32_t)(ok ? key : kend - 1) * sl.kss + 64u * q4;
-    const u32x4* src = (const u32x4*)(sl.kb + off);
+    const uint32_t off = FULL ? (uint32_t)(rel + 16 * gi) * sl.kss + sl.klane
+                              : (uint32_t)((ok ? key : kend - 1) - key0 + rel) * sl.kss + 64u * q4;
+    const u32x4* src = (const u32x4*)(kb + off);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const u32x4 x = src[j];
@@ -161,28 +198,32 @@ __device__ __forceinline__ void load_k(StepBF16& st, const Slab& sl, int key0, i
   }
 }
 
-template <bool FULL>
-__device__ __forceinline__ void load_v(StepBF16& st, const Slab& sl, int key0, int kend, int n16, int q4) {
+template <bool FULL, class SL>
+__device__ __forceinline__ void load_v(StepBF16& st, const SL& sl, int key0, int kend, int n16, int q4, int page) {
+  int rel;
+  const uint8_t* vb = sl.vbase(key0, page, rel);
 #pragma unroll
   for (int t = 0; t < 8; ++t) {
     const int key = key0 + 4 * q4 + vkey_t(t);
     const bool ok = FULL || key < kend;
-    const uint32_t off = FULL ? (uint32_t)(key0 + vkey_t(t)) * sl.vss + sl.vlane
-                              : (uint32_t)(ok ? key : kend - 1) * sl.vss + 16u * n16;
-    const u32x4 x = *(const u32x4*)(sl.vb + off);
+    const uint32_t off = FULL ? (uint32_t)(rel + vkey_t(t)) * sl.vss + sl.vlane
+                              : (uint32_t)((ok ? key : kend - 1) - key0 + rel) * sl.vss + 16u * n16;
+    const u32x4 x = *(const u32x4*)(vb + off);
     st.v[t] = ok ? x : u32x4{0, 0, 0, 0};
   }
 }
 
-template <bool FULL>
-__device__ __forceinline__ void load_k(StepF32& st, const Slab& sl, int key0, int kend, int n16, int q4) {
+template <bool FULL, class SL>
+__device__ __forceinline__ void load_k(StepF32& st, const SL& sl, int key0, int kend, int n16, int q4, int page) {
+  int rel;
+  const uint8_t* kb = sl.kbase(key0, page, rel);
 #pragma unroll
   for (int gi = 0; gi < 2; ++gi) {
     const int key = key0 + 16 * gi + n16;
     const bool ok = FULL || key < kend;
-    const uint32_t off = FULL ? (uint32_t)(key0 + 16 * gi) * sl.kss + sl.klane
-                              : (uint32_t)(ok ? key : kend - 1) * sl.kss + 128u * q4;
-    const f32x4* src = (const f32x4*)(sl.kb + off);
+    const uint32_t off = FULL ? (uint32_t)(rel + 16 * gi) * sl.kss + sl.klane
+                              : (uint32_t)((ok ? key : kend - 1) - key0 + rel) * sl.kss + 128u * q4;
+    const f32x4* src = (const f32x4*)(kb + off);
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       const f32x4 x = src[j];
@@ -191,37 +232,39 @@ __device__ __forceinline__ void load_k(StepF32& st, const Slab& sl, int key0, in
   }
 }
 
-template <bool FULL>
-__device__ __forceinline__ void load_v(StepF32& st, const Slab& sl, int key0, int kend, int n16, int q4) {
+template <bool FULL, class SL>
+__device__ __forceinline__ void load_v(StepF32& st, const SL& sl, int key0, int kend, int n16, int q4, int page) {
+  int rel;
+  const uint8_t* vb = sl.vbase(key0, page, rel);
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
     const int key = key0 + 16 * (e >> 2) + 4 * q4 + (e & 3);
     const bool ok = FULL || key < kend;
-    const uint32_t off = FULL ? (uint32_t)(key0 + 16 * (e >> 2) + (e & 3)) * sl.vss + sl.vlane
-                              : (uint32_t)(ok ? key : kend - 1) * sl.vss + 32u * n16;
-    const f32x4* src = (const f32x4*)(sl.vb + off);
+    const uint32_t off = FULL ? (uint32_t)(rel + 16 * (e >> 2) + (e & 3)) * sl.vss + sl.vlane
+                              : (uint32_t)((ok ? key : kend - 1) - key0 + rel) * sl.vss + 32u * n16;
+    const f32x4* src = (const f32x4*)(vb + off);
     const f32x4 x0 = src[0], x1 = src[1];
     st.v[e][0] = ok ? x0 : f32x4{0.f, 0.f, 0.f, 0.f};
     st.v[e][1] = ok ? x1 : f32x4{0.f, 0.f, 0.f, 0.f};
   }
 }
 
-template <class Step>
-__device__ __forceinline__ void load_k_any(Step& st, const Slab& sl, int key0, int kend, int n16, int q4) {
-  if (key0 + kStep <= kend) load_k<true>(st, sl, key0, kend, n16, q4);
-  else load_k<false>(st, sl, key0, kend, n16, q4);
+template <class Step, class SL>
+__device__ __forceinline__ void load_k_any(Step& st, const SL& sl, int key0, int kend, int n16, int q4, int page) {
+  if (key0 + kStep <= kend) load_k<true>(st, sl, key0, kend, n16, q4, page);
+  else load_k<false>(st, sl, key0, kend, n16, q4, page);
 }
 
-template <class Step>
-__device__ __forceinline__ void load_v_any(Step& st, const Slab& sl, int key0, int kend, int n16, int q4) {
-  if (key0 + kStep <= kend) load_v<true>(st, sl, key0, kend, n16, q4);
-  else load_v<false>(st, sl, key0, kend, n16, q4);
+template <class Step, class SL>
+__device__ __forceinline__ void load_v_any(Step& st, const SL& sl, int key0, int kend, int n16, int q4, int page) {
+  if (key0 + kStep <= kend) load_v<true>(st, sl, key0, kend, n16, q4, page);
+  else load_v<false>(st, sl, key0, kend, n16, q4, page);
 }
 
-template <class Step>
-__device__ __forceinline__ void load_step(Step& st, const Slab& sl, int key0, int kend, int n16, int q4) {
-  load_k_any(st, sl, key0, kend, n16, q4);
-  load_v_any(st, sl, key0, kend, n16, q4);
+template <class Step, class SL>
+__device__ __forceinline__ void load_step(Step& st, const SL& sl, int key0, int kend, int n16, int q4, int page) {
+  load_k_any(st, sl, key0, kend, n16, q4, page);
+  load_v_any(st, sl, key0, kend, n16, q4, page);
 }
 
 // ----------------------------------------------------------------- query operand and running state
@@ -323,15 +366,17 @@ __device__ __forceinline__ void accumulate_pv(const StepF32& st, const float (&p
 // next_key0 (if next_key0 < kend): its K half right after the QK^T MFMAs
 // have consumed st.k, its V half right after P V has consumed st.v.
 // kn >= 0: the score of key kn (the new key) is replaced by snew[lane % 16].
-template <class Step, class QFrag>
+// page: the page of next_key0 (paged caches), requested a step earlier; on
+// return it holds the page of the step after next_key0.
+template <class Step, class QFrag, class SL>
 __device__ __forceinline__ void sweep_step(Step& st, const QFrag& qf, const float* snew, int kn, RunState& rs,
-                                           float scale_log2, int key0, int kend, int next_key0, const Slab& sl,
-                                           int n16, int q4) {
+                                           float scale_log2, int key0, int kend, int next_key0, const SL& sl,
+                                           int n16, int q4, int& page) {
   const bool full = key0 + kStep <= kend;
   float s[8];
   scores(st, qf, scale_log2, s);
   const bool more = next_key0 < kend;
-  if (more) load_k_any(st, sl, next_key0, kend, n16, q4);
+  if (more) load_k_any(st, sl, next_key0, kend, n16, q4, page);
   if (kn >= key0 && kn < key0 + kStep) {   // wave-uniform: this step holds the new key
     const float sn = snew[n16];
 #pragma unroll
@@ -363,7 +408,10 @@ __device__ __forceinline__ void sweep_step(Step& st, const QFrag& qf, const floa
 #pragma unroll
   for (int T = 0; T < 8; ++T) rs.o[T] *= corr;
   accumulate_pv(st, p, rs);
-  if (more) load_v_any(st, sl, next_key0, kend, n16, q4);
+  if (more) {
+    load_v_any(st, sl, next_key0, kend, n16, q4, page);
+    page = sl.page_of(next_key0 + kStreamWaves * kStep, kend);
+  }
 }
 
 // ----------------------------------------------------------------- the prologue wave
@@ -381,8 +429,8 @@ struct PrologueRegs {
 
 // Branch-free: every lane fetches valid rows, so no fetch is waited on here.
 template <bool BF16>
-__device__ __forceinline__ void prologue_issue(const DecodeParams& p, int b, int h, int lane, int kn,
-                                               PrologueRegs<BF16>& pr) {
+__device__ __forceinline__ void prologue_issue(const DecodeParams& p, int b, int h, int lane,
+                                               const uint8_t* krow, PrologueRegs<BF16>& pr) {
   constexpr int kElem = BF16 ? 2 : 4;
   const int r4 = lane >> 4, c16 = lane & 15;
   const int G = p.group;
@@ -394,8 +442,7 @@ __device__ __forceinline__ void prologue_issue(const DecodeParams& p, int b, int
   }
   pr.gq = fetch_half_row<BF16>(p.q_norm_w != nullptr ? p.q_norm_w : p.q, c16);
   pr.gk = fetch_half_row<BF16>(p.k_norm_w != nullptr ? p.k_norm_w : p.q, c16);
-  const uint8_t* row = (const uint8_t*)p.k + ((int64_t)b * p.k_sb + (int64_t)h * p.k_sh + (int64_t)max(kn, 0) * p.k_ss) * kElem;
-  pr.y = fetch_half_row<BF16>(row, c16);
+  pr.y = fetch_half_row<BF16>(krow, c16);
 }
 
 template <bool BF16>
@@ -536,7 +583,20 @@ __device__ __forceinline__ void merge_chunk(const DecodeParams& p, const DecodeS
 // Two waves per SIMD at most (one workgroup of 5 waves per compute unit): no
 // register spills, which matters most for long sweeps (a spill reload would
 // queue behind the wave's in-flight K/V loads).
-template <bool BF16>
+// Row j of the (sequence b, KV head h) K cache: contiguous, or through the
+// block table (page stride k_sb).
+template <bool PAGED>
+__device__ __forceinline__ const uint8_t* k_row(const DecodeParams& p, int b, int h, int j, int elem) {
+  if constexpr (PAGED) {
+    const int page = p.block_table[(int64_t)b * p.max_blocks + (j >> p.block_log2)];
+    return (const uint8_t*)p.k +
+           ((int64_t)page * p.k_sb + (int64_t)h * p.k_sh + (int64_t)(j & ((1 << p.block_log2) - 1)) * p.k_ss) * elem;
+  } else {
+    return (const uint8_t*)p.k + ((int64_t)b * p.k_sb + (int64_t)h * p.k_sh + (int64_t)j * p.k_ss) * elem;
+  }
+}
+
+template <bool BF16, bool PAGED>
 __global__ __launch_bounds__(kThreads, BF16 ? 2 : 1) void decode_partition_kernel(const DecodeParams p) {
   using Step = typename std::conditional<BF16, StepBF16, StepF32>::type;
   using QFrag = typename std::conditional<BF16, QFragBF16, QFragF32>::type;
@@ -567,9 +627,18 @@ __global__ __launch_bounds__(kThreads, BF16 ? 2 : 1) void decode_partition_kerne
   const int c0 = cf * p.split;
   const int cap = min(min(cf + p.cpw, p.n_split) * p.split, p.max_seq);   // static end of the range
 
-  Slab sl;
-  sl.kb = (const uint8_t*)p.k + ((int64_t)b * p.k_sb + (int64_t)h * p.k_sh) * kElem;
-  sl.vb = (const uint8_t*)p.v + ((int64_t)b * p.v_sb + (int64_t)h * p.v_sh) * kElem;
+  Slab<PAGED> sl;
+  if constexpr (PAGED) {   // head h inside every page; pages through this sequence's block-table row
+    sl.kb = (const uint8_t*)p.k + (int64_t)h * p.k_sh * kElem;
+    sl.vb = (const uint8_t*)p.v + (int64_t)h * p.v_sh * kElem;
+    sl.bt = p.block_table + (int64_t)b * p.max_blocks;
+    sl.log2bs = p.block_log2;
+    sl.kpage = p.k_sb * kElem;
+    sl.vpage = p.v_sb * kElem;
+  } else {
+    sl.kb = (const uint8_t*)p.k + ((int64_t)b * p.k_sb + (int64_t)h * p.k_sh) * kElem;
+    sl.vb = (const uint8_t*)p.v + ((int64_t)b * p.v_sb + (int64_t)h * p.v_sh) * kElem;
+  }
   sl.kss = (uint32_t)(p.k_ss * kElem);
   sl.vss = (uint32_t)(p.v_ss * kElem);
   if constexpr (BF16) {
@@ -591,7 +660,7 @@ __global__ __launch_bounds__(kThreads, BF16 ? 2 : 1) void decode_partition_kerne
   const bool has_new = (rope || p.k_norm_w != nullptr) && c0 < L && c1 == L;   // range holds slot L-1
   const int kn = has_new ? L - 1 : -1;
   PrologueRegs<BF16> pr;
-  if (wave == kPrologueWave && c0 < L) prologue_issue<BF16>(p, b, h, lane, kn, pr);
+  if (wave == kPrologueWave && c0 < L) prologue_issue<BF16>(p, b, h, lane, k_row<PAGED>(p, b, h, max(kn, 0), kElem), pr);
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");   // keeps the loads above on this side
   __builtin_amdgcn_s_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
@@ -605,7 +674,11 @@ __global__ __launch_bounds__(kThreads, BF16 ? 2 : 1) void decode_partition_kerne
   const int spc = nchunks == 1 ? nsteps : p.split / kStep;      // steps per chunk
   int s = wave;
   Step A;
-  if (stream && s < nsteps) load_step(A, sl, c0 + s * kStep, c1, n16, q4);
+  int page = 0;   // paged: the page of this wave's next step
+  if (stream && s < nsteps) {
+    load_step(A, sl, c0 + s * kStep, c1, n16, q4, sl.page_of(c0 + s * kStep, c1));
+    page = sl.page_of(c0 + (s + kStreamWaves) * kStep, c1);
+  }
   if (wave == kPrologueWave) prologue_finish<BF16>(p, sm, pos, lane, rope, has_new, pr);
   __syncthreads();   // q', the new-key score and the tables are in LDS
 
@@ -623,7 +696,7 @@ __global__ __launch_bounds__(kThreads, BF16 ? 2 : 1) void decode_partition_kerne
       const int s_end = min(nsteps, (j + 1) * spc);
       while (s < s_end) {
         sweep_step(A, qf, sm.snew, kn, rs, p.scale_log2, c0 + s * kStep, c1, c0 + (s + kStreamWaves) * kStep, sl,
-                   n16, q4);
+                   n16, q4, page);
         s += kStreamWaves;
       }
       // ---- this wave's state of chunk j into LDS buffer j % 2
@@ -653,7 +726,7 @@ __global__ __launch_bounds__(kThreads, BF16 ? 2 : 1) void decode_partition_kerne
   //      every read of that row (the prologue's and the streaming waves' step
   //      holding it) is complete, and no other workgroup reads it
   if (p.write_new_k && has_new && wave == kPrologueWave && lane < 32) {
-    uint8_t* row = (uint8_t*)p.k + ((int64_t)b * p.k_sb + (int64_t)h * p.k_sh + (int64_t)kn * p.k_ss) * kElem;
+    uint8_t* row = (uint8_t*)k_row<PAGED>(p, b, h, kn, kElem);
     const f32x4 y = *(const f32x4*)&sm.kn[4 * lane];
     if (BF16) *(u32x2*)(row + 8 * lane) = u32x2{pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3])};
     else *(f32x4*)(row + 16 * lane) = y;
@@ -765,7 +838,8 @@ template <bool BF16>
 void launch_partition(const DecodeParams& p, hipStream_t stream) {
   const int wpg = (p.n_split + p.cpw - 1) / p.cpw;
   const dim3 grid(wpg * p.num_kv_heads * p.batch);
-  hipLaunchKernelGGL((decode_partition_kernel<BF16>), grid, dim3(kThreads), 0, stream, p);
+  if (p.block_table != nullptr) hipLaunchKernelGGL((decode_partition_kernel<BF16, true>), grid, dim3(kThreads), 0, stream, p);
+  else hipLaunchKernelGGL((decode_partition_kernel<BF16, false>), grid, dim3(kThreads), 0, stream, p);
 }
 
 }  // namespace

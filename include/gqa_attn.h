@@ -96,6 +96,9 @@ typedef struct gqa_decode_desc {
   float eps;               /* RMSNorm epsilon (e.g. 1e-6)                          */
   float scale;             /* softmax scale; <= 0 selects 1/sqrt(head_dim)         */
   int32_t write_new_k;     /* 1: store K'_{L-1} into k_cache[b, kv, L-1] (below)   */
+  int32_t block_size;      /* 0: contiguous caches; > 0: rows per page of a paged
+                              cache (gqa_attn_decode_paged only), a power of two
+                              >= 32 dividing max_seq                               */
 } gqa_decode_desc;
 
 /* Prefill: self-attention over seq_lens[b] tokens per sequence (T_q = S_kv). */
@@ -205,6 +208,27 @@ gqa_status gqa_attn_decode_partition(const gqa_decode_desc* desc, const void* q,
 
 gqa_status gqa_attn_decode_merge(const gqa_decode_desc* desc, const int32_t* seq_lens, void* out, void* workspace,
                                  size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * Decode over a paged KV cache (block table; the layout a serving engine's
+ * fused attention consumes).  Same computation and outputs as gqa_attn_decode
+ * (including write_new_k), with logical cache row j of sequence b at
+ *   k_pages[block_table[b * (max_seq / bs) + j / bs], kv, j % bs, :]
+ * (bs = desc->block_size; likewise v_pages), where the element strides are
+ * k_stride_b = between pages, k_stride_h = between heads inside a page,
+ * k_stride_s = between rows (same for v).  block_table: [B][max_seq / bs]
+ * int32 page indices (device); entries for blocks at or past
+ * ceil(seq_lens[b] / bs) are not read.  The split-KV chunk length is rounded
+ * up to a multiple of 32 keys, so no 32-key step crosses a page.
+ * Errors: as gqa_attn_decode; GQA_ERR_NULL for a missing block_table,
+ * GQA_ERR_SHAPE for block_size == 0 here, or != 0 with the contiguous entry
+ * points, or not a power of two >= 32 dividing max_seq.
+ */
+gqa_status gqa_attn_decode_paged(const gqa_decode_desc* desc, const void* q, const void* k_pages,
+                                 const void* v_pages, const int32_t* block_table, const int32_t* seq_lens,
+                                 const int32_t* positions, const void* q_norm_w, const void* k_norm_w,
+                                 float rope_theta, void* out, void* workspace, size_t workspace_bytes,
+                                 hipStream_t stream);
 
 /*
  * Bytes of the optional prefill workspace (host only, no HIP call):

@@ -282,3 +282,23 @@ def test_prefill_chunk_errors():
     assert call_chunk(d, past=FAKE + 2, wsb=need) == G.GQA_ERR_ALIGN
     assert call_chunk(pdesc(max_chunk=64, head_dim=64), wsb=need) == G.GQA_ERR_UNSUPPORTED
     assert call_chunk(pdesc(max_chunk=64, in_dtype=G.GQA_F32), wsb=need) == G.GQA_ERR_UNSUPPORTED
+
+
+def call_paged(d, bt=FAKE, ws=FAKE, wsb=1 << 40):
+    return G.gqa_attn_decode_paged(d, FAKE, FAKE, FAKE, bt, FAKE, FAKE, NULL, NULL, 1e6, FAKE, ws, wsb, None)
+
+
+def test_decode_paged_errors_and_plan():
+    d = ddesc(block_size=64)
+    assert call_paged(d, bt=NULL) == G.GQA_ERR_NULL
+    assert call_paged(d, bt=FAKE + 2) == G.GQA_ERR_ALIGN
+    assert call_paged(ddesc()) == G.GQA_ERR_SHAPE                  # contiguous descriptor
+    assert call_decode(d) == G.GQA_ERR_SHAPE                        # paged descriptor, contiguous entry point
+    for bad in (16, 48, 96, 3):
+        assert call_paged(ddesc(block_size=bad)) == G.GQA_ERR_SHAPE
+    assert call_paged(ddesc(block_size=64, max_seq=4096 + 32)) == G.GQA_ERR_SHAPE   # pages do not divide max_seq
+    # the chunk length rounds up to a multiple of 32 keys so no step crosses a page
+    st, T, n = G.gqa_attn_decode_plan(ddesc(block_size=32, kv_split_tokens=100))
+    assert st == G.GQA_OK and T == 128 and n == -(-4096 // 128)
+    st, T, n = G.gqa_attn_decode_plan(ddesc(kv_split_tokens=100))
+    assert st == G.GQA_OK and T == 100
