@@ -217,9 +217,10 @@ def prefill_case(torch, G, synth, np, two_phase=True):
     return pw, pin, t, call
 
 
-def prefill_chunk_case(torch, G, synth, np, past=3072, chunk=1024):
+def prefill_chunk_case(torch, G, synth, np, past=3072, chunk=1024, bs=0):
     """The last `chunk` tokens of the Qwen3-14B prefill prompt as one chunk after
-    `past` cached tokens (a cache of past + chunk rows; seeded synthetic rows)."""
+    `past` cached tokens (a cache of past + chunk rows; seeded synthetic rows).
+    bs > 0: the same cache as a shuffled pool of bs-row pages."""
     pw = synth.QWEN3_PREFILL
     rng = np.random.Generator(np.random.PCG64(pw.seed + 100))
     bf = torch.bfloat16
@@ -232,14 +233,35 @@ def prefill_chunk_case(torch, G, synth, np, past=3072, chunk=1024):
              pos=torch.tensor([0], dtype=torch.int32, device="cuda"))
     t["out"] = torch.empty(t["q"].shape, dtype=torch.float32, device="cuda")
     desc = G.prefill_chunk_desc(t["q"], t["k"], t["v"], t["out"], True, pw.eps)
+    if bs:
+        nb = S // bs
+        perm = torch.from_numpy(rng.permutation(nb)).cuda()
+        pages = lambda x: x[0].reshape(pw.num_kv_heads, nb, bs, 128).transpose(0, 1)   # [nb, Hkv, bs, 128]
+        t["kp"] = torch.empty_like(pages(t["k"])).contiguous()
+        t["vp"] = torch.empty_like(t["kp"])
+        t["kp"][perm] = pages(t["k"])
+        t["vp"][perm] = pages(t["v"])
+        t["table"] = perm.to(torch.int32).reshape(1, nb).contiguous()
+        kp, vp = t["kp"], t["vp"]
+        desc.k_stride_b, desc.k_stride_h, desc.k_stride_s = kp.stride(0), kp.stride(1), kp.stride(2)
+        desc.v_stride_b, desc.v_stride_h, desc.v_stride_s = vp.stride(0), vp.stride(1), vp.stride(2)
+        desc.block_size = bs
+        del t["k"], t["v"]
     t["ws"] = G.prefill_workspace(desc, "cuda")
     flops = 4 * 128 * pw.num_q_heads * sum(past + i + 1 for i in range(chunk))
 
     def call(i, stream):
-        st = G.gqa_attn_prefill_chunk(desc, t["q"].data_ptr(), t["k"].data_ptr(), t["v"].data_ptr(),
-                                      t["past"].data_ptr(), t["cl"].data_ptr(), t["pos"].data_ptr(),
-                                      t["qw"].data_ptr(), t["kw"].data_ptr(), pw.rope_theta, t["out"].data_ptr(),
-                                      t["ws"].data_ptr(), t["ws"].numel(), stream)
+        if bs:
+            st = G.gqa_attn_prefill_chunk_paged(desc, t["q"].data_ptr(), t["kp"].data_ptr(), t["vp"].data_ptr(),
+                                                t["table"].data_ptr(), t["past"].data_ptr(), t["cl"].data_ptr(),
+                                                t["pos"].data_ptr(), t["qw"].data_ptr(), t["kw"].data_ptr(),
+                                                pw.rope_theta, t["out"].data_ptr(), t["ws"].data_ptr(),
+                                                t["ws"].numel(), stream)
+        else:
+            st = G.gqa_attn_prefill_chunk(desc, t["q"].data_ptr(), t["k"].data_ptr(), t["v"].data_ptr(),
+                                          t["past"].data_ptr(), t["cl"].data_ptr(), t["pos"].data_ptr(),
+                                          t["qw"].data_ptr(), t["kw"].data_ptr(), pw.rope_theta, t["out"].data_ptr(),
+                                          t["ws"].data_ptr(), t["ws"].numel(), stream)
         assert st == G.GQA_OK
     return t, call, flops
 
@@ -407,6 +429,17 @@ def main():
                                   "tflops": round(tf_c, 2), "frac_of_bf16_peak": round(tf_c / BF16_PEAK_TFLOPS, 4),
                                   "algorithmic_flops": cflops}
         log(f"[bench] prefill chunk (3072 cached + 1024 new) {us_c:.1f} us -> {tf_c:.1f} TFLOP/s")
+        del ct, ccall
+        torch.cuda.empty_cache()
+
+        ct, ccall, cflops = prefill_chunk_case(torch, G, synth, np, bs=64)
+        pt = graph_time_ms(torch, ccall, pk_steps, max(2, W // 10))
+        us_c = 1000.0 * pt / pk_steps
+        tf_c = cflops / (us_c * 1e-6) / 1e12
+        extra["prefill_chunk_paged"] = {"workload": "qwen3_14b_prefill_chunk_3072_cached_1024_new", "block_size": 64,
+                                        "us_per_call": round(us_c, 2), "tflops": round(tf_c, 2),
+                                        "frac_of_bf16_peak": round(tf_c / BF16_PEAK_TFLOPS, 4)}
+        log(f"[bench] prefill chunk over 64-row pages {us_c:.1f} us -> {tf_c:.1f} TFLOP/s")
         del ct, ccall
         torch.cuda.empty_cache()
 

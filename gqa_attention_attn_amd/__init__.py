@@ -42,6 +42,7 @@ EXPORTS = (
     "gqa_attn_prefill_workspace_size",
     "gqa_attn_prefill",
     "gqa_attn_prefill_chunk",
+    "gqa_attn_prefill_chunk_paged",
 )
 
 
@@ -75,6 +76,7 @@ class GqaPrefillDesc(ctypes.Structure):
         ("v_stride_b", ctypes.c_int64), ("v_stride_h", ctypes.c_int64), ("v_stride_s", ctypes.c_int64),
         ("out_stride_b", ctypes.c_int64), ("out_stride_h", ctypes.c_int64), ("out_stride_s", ctypes.c_int64),
         ("eps", ctypes.c_float), ("scale", ctypes.c_float), ("max_chunk", ctypes.c_int32),
+        ("block_size", ctypes.c_int32),
     ]
 
 
@@ -116,6 +118,9 @@ def lib() -> ctypes.CDLL:
         L.gqa_attn_prefill_chunk.argtypes = [ctypes.POINTER(GqaPrefillDesc), vp, vp, vp, vp, vp, vp, vp, vp,
                                              ctypes.c_float, vp, vp, ctypes.c_size_t, vp]
         L.gqa_attn_prefill_chunk.restype = ctypes.c_int
+        L.gqa_attn_prefill_chunk_paged.argtypes = [ctypes.POINTER(GqaPrefillDesc), vp, vp, vp, vp, vp, vp, vp, vp,
+                                                   vp, ctypes.c_float, vp, vp, ctypes.c_size_t, vp]
+        L.gqa_attn_prefill_chunk_paged.restype = ctypes.c_int
         _lib = L
     return _lib
 
@@ -190,6 +195,14 @@ def gqa_attn_prefill_chunk(desc, q, k_cache, v_cache, past_lens, chunk_lens, pos
     return int(lib().gqa_attn_prefill_chunk(ctypes.byref(desc) if desc is not None else None, q, k_cache, v_cache,
                                             past_lens, chunk_lens, positions, q_norm_w, k_norm_w, float(rope_theta),
                                             out, workspace, int(workspace_bytes), stream))
+
+
+def gqa_attn_prefill_chunk_paged(desc, q, k_pages, v_pages, block_table, past_lens, chunk_lens, positions,
+                                 q_norm_w, k_norm_w, rope_theta, out, workspace, workspace_bytes, stream) -> int:
+    return int(lib().gqa_attn_prefill_chunk_paged(ctypes.byref(desc) if desc is not None else None, q, k_pages,
+                                                  v_pages, block_table, past_lens, chunk_lens, positions, q_norm_w,
+                                                  k_norm_w, float(rope_theta), out, workspace, int(workspace_bytes),
+                                                  stream))
 
 
 # ----------------------------------------------------------------- torch conveniences
@@ -364,4 +377,34 @@ def decode_paged(q, k_pages, v_pages, block_table, seq_lens, positions, q_norm_w
                                _ptr(workspace), ws_bytes, _stream_ptr(stream))
     if st != GQA_OK:
         raise GqaError(st, "gqa_attn_decode_paged")
+    return out
+
+
+def prefill_chunk_paged(q, k_pages, v_pages, block_table, past_lens, chunk_lens, positions, q_norm_w=None,
+                        k_norm_w=None, rope_theta: float = 0.0, out=None, causal: bool = True, eps: float = 1e-6,
+                        scale: float = 0.0, out_dtype=None, workspace=None, stream=None):
+    """gqa_attn_prefill_chunk_paged on torch tensors: k_pages / v_pages [num_pages, Hkv, bs, 128],
+    block_table [B, max_blocks] int32 (cache capacity max_blocks * bs); returns out."""
+    import torch
+    if out is None:
+        out = torch.empty(q.shape, dtype=out_dtype or torch.float32, device=q.device)
+    B, Hq, T, d = q.shape
+    _, Hkv, bs, _ = k_pages.shape
+    desc = GqaPrefillDesc(
+        batch=B, num_q_heads=Hq, num_kv_heads=Hkv, head_dim=d, max_seq=block_table.shape[1] * bs,
+        in_dtype=_dtype_code(q), out_dtype=_dtype_code(out), causal=1 if causal else 0,
+        q_stride_b=q.stride(0), q_stride_h=q.stride(1), q_stride_s=q.stride(2),
+        k_stride_b=k_pages.stride(0), k_stride_h=k_pages.stride(1), k_stride_s=k_pages.stride(2),
+        v_stride_b=v_pages.stride(0), v_stride_h=v_pages.stride(1), v_stride_s=v_pages.stride(2),
+        out_stride_b=out.stride(0), out_stride_h=out.stride(1), out_stride_s=out.stride(2),
+        eps=float(eps), scale=float(scale), max_chunk=T, block_size=bs)
+    if workspace is None:
+        workspace = prefill_workspace(desc, q.device)
+    ws_bytes = workspace.numel() * workspace.element_size()
+    st = gqa_attn_prefill_chunk_paged(desc, _ptr(q), _ptr(k_pages), _ptr(v_pages), _ptr(block_table),
+                                      _ptr(past_lens), _ptr(chunk_lens), _ptr(positions), _ptr(q_norm_w),
+                                      _ptr(k_norm_w), rope_theta, _ptr(out), _ptr(workspace), ws_bytes,
+                                      _stream_ptr(stream))
+    if st != GQA_OK:
+        raise GqaError(st, "gqa_attn_prefill_chunk_paged")
     return out

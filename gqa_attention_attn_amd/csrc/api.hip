@@ -120,6 +120,10 @@ gqa_status check_prefill_desc(const gqa_prefill_desc* d) {
   if (d->head_dim != GQA_ATTN_HEAD_DIM) return GQA_ERR_UNSUPPORTED;
   if (d->in_dtype != GQA_BF16 || !dtype_ok(d->out_dtype)) return GQA_ERR_UNSUPPORTED;
   if (d->causal != 0 && d->causal != 1) return GQA_ERR_SHAPE;
+  if (d->block_size != 0) {   // paged: a power of two >= 16 rows per page, whole pages
+    if (d->block_size < 16 || (d->block_size & (d->block_size - 1)) != 0 || d->max_seq % d->block_size != 0)
+      return GQA_ERR_SHAPE;
+  }
   // prefill addresses one (b, KV head) K / V slab with 32-bit byte offsets
   if ((int64_t)d->max_seq * d->k_stride_s * 2 + 512 > ((int64_t)1 << 32) ||
       (int64_t)d->max_seq * d->v_stride_s * 2 + 512 > ((int64_t)1 << 32))
@@ -321,9 +325,12 @@ namespace {
 gqa_status prepare_prefill(const gqa_prefill_desc* d, const void* q, const void* k, const void* v,
                            const int32_t* lens, const int32_t* past_lens, const int32_t* positions,
                            const void* q_norm_w, const void* k_norm_w, float rope_theta, void* out, void* workspace,
-                           size_t workspace_bytes, gqa::PrefillParams* pp) {
+                           size_t workspace_bytes, gqa::PrefillParams* pp, const int32_t* block_table = nullptr) {
   gqa_status st = check_prefill_desc(d);
   if (st != GQA_OK) return st;
+  // a paged descriptor (block_size > 0) goes with gqa_attn_prefill_chunk_paged only
+  if ((d->block_size != 0) != (block_table != nullptr)) return GQA_ERR_SHAPE;
+  if ((uintptr_t)block_table & 3u) return GQA_ERR_ALIGN;
   if (q == nullptr || k == nullptr || v == nullptr || lens == nullptr || positions == nullptr || out == nullptr)
     return GQA_ERR_NULL;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) || !aligned16(q_norm_w) ||
@@ -340,6 +347,11 @@ gqa_status prepare_prefill(const gqa_prefill_desc* d, const void* q, const void*
   p.v = v;
   p.seq_lens = lens;
   p.past_lens = past_lens;
+  if (block_table != nullptr) {
+    p.block_table = block_table;
+    p.block_log2 = __builtin_ctz((unsigned)d->block_size);
+    p.max_blocks = d->max_seq / d->block_size;
+  }
   p.positions = positions;
   p.q_norm_w = q_norm_w;
   p.k_norm_w = k_norm_w;
@@ -404,6 +416,24 @@ gqa_status gqa_attn_prefill_chunk(const gqa_prefill_desc* d, const void* q, cons
   gqa::PrefillParams p;
   const gqa_status st = prepare_prefill(d, q, k_cache, v_cache, chunk_lens, past_lens, positions, q_norm_w, k_norm_w,
                                         rope_theta, out, workspace, workspace_bytes, &p);
+  if (st != GQA_OK) return st;
+  return gqa::launch_prefill_phased(p, workspace, stream) == hipSuccess ? GQA_OK : GQA_ERR_HIP;
+}
+
+gqa_status gqa_attn_prefill_chunk_paged(const gqa_prefill_desc* d, const void* q, const void* k_pages,
+                                        const void* v_pages, const int32_t* block_table, const int32_t* past_lens,
+                                        const int32_t* chunk_lens, const int32_t* positions, const void* q_norm_w,
+                                        const void* k_norm_w, float rope_theta, void* out, void* workspace,
+                                        size_t workspace_bytes, hipStream_t stream) {
+  if (d == nullptr) return GQA_ERR_NULL;
+  if (d->max_chunk < 0 || d->block_size == 0) return GQA_ERR_SHAPE;
+  const int64_t tmax = d->max_chunk > 0 ? d->max_chunk : d->max_seq;
+  if ((int64_t)d->batch * d->num_q_heads * ((tmax + 31) / 32) > INT32_MAX) return GQA_ERR_SHAPE;
+  if (past_lens == nullptr || block_table == nullptr) return GQA_ERR_NULL;
+  if (workspace == nullptr) return GQA_ERR_WORKSPACE;
+  gqa::PrefillParams p;
+  const gqa_status st = prepare_prefill(d, q, k_pages, v_pages, chunk_lens, past_lens, positions, q_norm_w,
+                                        k_norm_w, rope_theta, out, workspace, workspace_bytes, &p, block_table);
   if (st != GQA_OK) return st;
   return gqa::launch_prefill_phased(p, workspace, stream) == hipSuccess ? GQA_OK : GQA_ERR_HIP;
 }

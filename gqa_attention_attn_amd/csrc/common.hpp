@@ -58,6 +58,9 @@ struct PrefillParams {
   int32_t causal;
   int32_t out_bf16;
   const int32_t* past_lens;  // chunked prefill: keys already in the cache per sequence (null: none)
+  const int32_t* block_table;  // paged caches: [B][max_blocks] page of each block of rows (null: contiguous)
+  int32_t block_log2;     // paged: log2(rows per page)
+  int32_t max_blocks;     // paged: row length of block_table
   int32_t max_chunk;      // query / output rows per sequence (max_seq for a plain prefill)
   int32_t heads_per_wg;   // HC: query heads of one KV head batched in a workgroup
   int32_t block_q;        // BQ: query tokens per workgroup (multiple of 32)
@@ -82,6 +85,8 @@ constexpr int kPrefillMaxWaves = 10;
 
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
 typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
+typedef __attribute__((ext_vector_type(8))) _Float16 f16x8;
+typedef __attribute__((ext_vector_type(2))) _Float16 f16x2;
 typedef __attribute__((ext_vector_type(4))) float f32x4;
 typedef __attribute__((ext_vector_type(16))) float f32x16;
 typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
@@ -101,6 +106,14 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
 
 // Element e (0..7) of 8 packed bf16 held in 4 dwords, as float.
+// Two f32 to packed fp16 (round to nearest even; beyond +-65504 -> +-inf).
+__device__ __forceinline__ uint32_t pack_f16x2(float lo, float hi) {
+  const f16x2 v = {(_Float16)lo, (_Float16)hi};
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+__device__ __forceinline__ f16x8 as_f16x8(u32x4 v) { return __builtin_bit_cast(f16x8, v); }
+
 __device__ __forceinline__ float bf16_elem(const u32x4& v, int e) {
   uint32_t w = v[e >> 1];
   return (e & 1) ? bf16hi(w) : bf16lo(w);

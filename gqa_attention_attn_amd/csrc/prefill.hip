@@ -18,11 +18,11 @@
 //    5 heads x 64 tokens).  Every key tile, and its key prologue, is shared by
 //    all of them.
 //  * per 32-key tile: the raw K and V rows are fetched into registers one tile
-//    ahead; K rows go through the key prologue (f32) and are stored as bf16 K'
+//    ahead; K rows go through the key prologue (f32) and are stored as fp16 K'
 //    in LDS (16-byte chunks XOR-swizzled by key), V rows are stored transposed
 //    (V^T, key pairs packed per dword); both double-buffered, so one barrier
 //    per tile suffices.  S^T = K' Q'^T and O^T = V^T P^T run on
-//    v_mfma_f32_32x32x16_bf16 with f32 accumulation; in the S^T orientation a
+//    v_mfma_f32_32x32x16_f16 with f32 accumulation; in the S^T orientation a
 //    lane owns one query row, so the row max needs one cross-lane step.
 //  * scores live in the log2 domain (scale * log2 e folded into the exp2 FMA);
 //    the running output is rescaled only when a row maximum grows by more
@@ -38,13 +38,13 @@ constexpr int kMaxWaves = kPrefillMaxWaves;
 constexpr int kMaxThreads = 64 * kMaxWaves;
 constexpr int BN = 32;                 // keys per tile
 constexpr int kXcds = 8;               // MI355X: 8 XCDs, each with its own L2
-constexpr int kVtRow = 40;             // V^T row stride in bf16 (32 keys + 8): conflict-free 16-byte reads
+constexpr int kVtRow = 40;             // V^T row stride in fp16 (32 keys + 8): conflict-free 16-byte reads
 constexpr float kLazyRescale = 8.0f;   // rescale O only when a row max grows by more than 2^8
 constexpr int kKUnits = 256;           // K staging units per tile (32 keys x 8 dim chunks)
 constexpr int kUnits = 512;            // + 256 V staging units (16 key pairs x 16 dim chunks)
 
 struct __attribute__((aligned(16))) PrefillSmem {
-  uint32_t kt[2][BN][kHeadDim / 2];   // K' tiles, bf16 pairs, 16-byte chunks swizzled by key & 15
+  uint32_t kt[2][BN][kHeadDim / 2];   // K' tiles, fp16 pairs, 16-byte chunks swizzled by key & 15
   uint16_t vt[2][kHeadDim][kVtRow];   // V^T tiles: vt[buf][dim][vpos(key)]
   double inv_rev[kHeadDim / 2];       // theta^(-2i/128) / (2 pi)
   float gk[kHeadDim];                 // key RMSNorm weight (f32)
@@ -136,18 +136,19 @@ __device__ __forceinline__ void stage_unit(PrefillSmem& sm, const Raw& r, const 
     }
     uint32_t* krow = sm.kt[buf][lkey];
     const int sw = kswz(lkey);
-    *(u32x4*)(krow + 4 * (c ^ sw)) = u32x4{pack_bf16x2(xl[0], xl[1]), pack_bf16x2(xl[2], xl[3]),
-                                          pack_bf16x2(xl[4], xl[5]), pack_bf16x2(xl[6], xl[7])};
-    *(u32x4*)(krow + 4 * ((8 + c) ^ sw)) = u32x4{pack_bf16x2(xh[0], xh[1]), pack_bf16x2(xh[2], xh[3]),
-                                                pack_bf16x2(xh[4], xh[5]), pack_bf16x2(xh[6], xh[7])};
+    *(u32x4*)(krow + 4 * (c ^ sw)) = u32x4{pack_f16x2(xl[0], xl[1]), pack_f16x2(xl[2], xl[3]),
+                                          pack_f16x2(xl[4], xl[5]), pack_f16x2(xl[6], xl[7])};
+    *(u32x4*)(krow + 4 * ((8 + c) ^ sw)) = u32x4{pack_f16x2(xh[0], xh[1]), pack_f16x2(xh[2], xh[3]),
+                                                pack_f16x2(xh[4], xh[5]), pack_f16x2(xh[6], xh[7])};
   } else {
     const int v = u - kKUnits;
     const int kp = v & 15, dc = v >> 4;
     const int pos = vpos(2 * kp);   // keys 2kp, 2kp+1 stay adjacent
 #pragma unroll
     for (int j = 0; j < 4; ++j) {   // dims 8dc + 2j (lo halves) and 8dc + 2j + 1 (hi halves)
-      *(uint32_t*)&sm.vt[buf][8 * dc + 2 * j][pos] = pair_lo(r.a[j], r.b[j]);
-      *(uint32_t*)&sm.vt[buf][8 * dc + 2 * j + 1][pos] = pair_hi(r.a[j], r.b[j]);
+      const uint32_t a = r.a[j], c = r.b[j];
+      *(uint32_t*)&sm.vt[buf][8 * dc + 2 * j][pos] = pack_f16x2(bf16lo(a), bf16lo(c));
+      *(uint32_t*)&sm.vt[buf][8 * dc + 2 * j + 1][pos] = pack_f16x2(bf16hi(a), bf16hi(c));
     }
   }
 }
@@ -217,7 +218,7 @@ __global__ __launch_bounds__(kMaxThreads) void prefill_kernel(const PrefillParam
   if (has1) fetch_unit(r1, st, 0, u1);
 
   // query prologue: lane (n32, hf) owns row qrow of head hq, dims [32hf, 32hf+32) and [64+32hf, 64+32hf+32)
-  bf16x8 qf[8];
+  f16x8 qf[8];
   {
     // raw row halves kept packed (16 registers each), unpacked chunk by chunk
     u32x4 qlo[4], qhi[4];
@@ -275,10 +276,10 @@ __global__ __launch_bounds__(kMaxThreads) void prefill_kernel(const PrefillParam
           xh[e] = hi * c + lo * s;
         }
       }
-      qf[j] = as_bf16x8(u32x4{pack_bf16x2(xl[0], xl[1]), pack_bf16x2(xl[2], xl[3]), pack_bf16x2(xl[4], xl[5]),
-                              pack_bf16x2(xl[6], xl[7])});
-      qf[4 + j] = as_bf16x8(u32x4{pack_bf16x2(xh[0], xh[1]), pack_bf16x2(xh[2], xh[3]), pack_bf16x2(xh[4], xh[5]),
-                                  pack_bf16x2(xh[6], xh[7])});
+      qf[j] = as_f16x8(u32x4{pack_f16x2(xl[0], xl[1]), pack_f16x2(xl[2], xl[3]), pack_f16x2(xl[4], xl[5]),
+                              pack_f16x2(xl[6], xl[7])});
+      qf[4 + j] = as_f16x8(u32x4{pack_f16x2(xh[0], xh[1]), pack_f16x2(xh[2], xh[3]), pack_f16x2(xh[4], xh[5]),
+                                  pack_f16x2(xh[6], xh[7])});
     }
   }
   if (has0) stage_unit(sm, r0, p, rope, pos0, 0, u0, 0);
@@ -312,7 +313,7 @@ __global__ __launch_bounds__(kMaxThreads) void prefill_kernel(const PrefillParam
 #pragma unroll
         for (int kk = 0; kk < 8; ++kk) {
           const u32x4 a = *(const u32x4*)(kr + 4 * (qk_chunk(kk, hf) ^ sw));
-          sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), qf[kk], sacc, 0, 0, 0);
+          sacc = __builtin_amdgcn_mfma_f32_32x32x16_f16(as_f16x8(a), qf[kk], sacc, 0, 0, 0);
         }
       }
       if ((p.causal && ks + BN - 1 > wq0) || ks + BN > n) {   // wave-uniform: diagonal or ragged tile
@@ -347,12 +348,12 @@ __global__ __launch_bounds__(kMaxThreads) void prefill_kernel(const PrefillParam
       // stored contiguously at V^T positions 16e + 8hf .. 16e + 8hf + 7
 #pragma unroll
       for (int e = 0; e < 2; ++e) {
-        const u32x4 pf = {pack_bf16x2(sacc[8 * e + 0], sacc[8 * e + 1]), pack_bf16x2(sacc[8 * e + 2], sacc[8 * e + 3]),
-                          pack_bf16x2(sacc[8 * e + 4], sacc[8 * e + 5]), pack_bf16x2(sacc[8 * e + 6], sacc[8 * e + 7])};
+        const u32x4 pf = {pack_f16x2(sacc[8 * e + 0], sacc[8 * e + 1]), pack_f16x2(sacc[8 * e + 2], sacc[8 * e + 3]),
+                          pack_f16x2(sacc[8 * e + 4], sacc[8 * e + 5]), pack_f16x2(sacc[8 * e + 6], sacc[8 * e + 7])};
 #pragma unroll
         for (int T = 0; T < 4; ++T) {
           const u32x4 a = *(const u32x4*)&sm.vt[buf][32 * T + n32][16 * e + 8 * hf];
-          o[T] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), as_bf16x8(pf), o[T], 0, 0, 0);
+          o[T] = __builtin_amdgcn_mfma_f32_32x32x16_f16(as_f16x8(a), as_f16x8(pf), o[T], 0, 0, 0);
         }
       }
     }

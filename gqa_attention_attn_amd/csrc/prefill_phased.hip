@@ -6,9 +6,9 @@
 // separated by an in-kernel grid-wide barrier.  On the GPU the grid-wide
 // barrier is the boundary between two dispatches on one stream:
 //  * phase 1 (key_prologue_kernel): every key row of every (sequence, KV head)
-//    goes through RMSNorm + RoPE once and is stored as bf16 K' in a workspace,
-//    beside a copy of its V row, both already in the padded row layout the
-//    attention tiles have in LDS;
+//    goes through RMSNorm + RoPE once and is stored as fp16 K' in a workspace,
+//    beside its V row converted to fp16, both already in the padded row
+//    layout the attention tiles have in LDS;
 //  * phase 2 (attention_kernel): tiled online softmax ("ADR-0060: AHBM GQA
 //    Fused Attention Kernel (Llama3-70B)", sections 3 and 5.4) over K' and V,
 //    with each query row's prologue applied when the query tile is loaded.
@@ -21,7 +21,9 @@
 // unit).  32-key tiles are filled by linear direct-to-LDS copies (no register
 // staging) from the padded workspace; V is read back transposed by
 // ds_read_b64_tr_b16 as the V^T operand.  S^T = K' Q'^T and O^T = V^T P^T run
-// on v_mfma_f32_32x32x16_bf16.  Software pipeline of a wave, per tile t: the
+// on v_mfma_f32_32x32x16_f16 (the bf16 rate, with 11 significand bits for
+// the rounded q', k' and P instead of 8; bf16 V converts to fp16 exactly for
+// magnitudes in [2^-14, 65504]).  Software pipeline of a wave, per tile t: the
 // scores of tile t+1 are computed beside the exponentials of tile t, then P V
 // of tile t, then the row maxima of tile t+1; K' is loaded two tiles ahead
 // and V one tile ahead, so one barrier per tile suffices.  A 1-D grid ordered
@@ -78,6 +80,12 @@ __device__ __forceinline__ SeqExtent seq_extent(const PrefillParams& p, int b) {
 
 // ----------------------------------------------------------------- phase 1: key prologue
 
+// Eight bf16 (packed) to eight fp16 (packed), round to nearest even.
+__device__ __forceinline__ u32x4 bf16x8_to_f16x8(const u32x4 x) {
+  return u32x4{pack_f16x2(bf16lo(x[0]), bf16hi(x[0])), pack_f16x2(bf16lo(x[1]), bf16hi(x[1])),
+               pack_f16x2(bf16lo(x[2]), bf16hi(x[2])), pack_f16x2(bf16lo(x[3]), bf16hi(x[3]))};
+}
+
 // 16 key rows per workgroup; a row is held by 16 lanes (dims 4c..4c+3 and
 // 64+4c..64+4c+3), so RMSNorm reduces over 16 lanes and RoPE pairs (i, i+64)
 // stay in one lane.  The same lanes copy the row's V (16 bytes each).  Rows
@@ -102,12 +110,20 @@ __global__ __launch_bounds__(256) void key_prologue_kernel(const PrefillParams p
     }
     return;
   }
-  *(u32x4*)(vd + 16 * c) =
-      *(const u32x4*)((const uint8_t*)p.v + ((int64_t)b * p.v_sb + (int64_t)h * p.v_sh + (int64_t)key * p.v_ss) * 2 +
-                      16 * c);
-  const uint16_t* src = (const uint16_t*)p.k + ((int64_t)b * p.k_sb + (int64_t)h * p.k_sh + (int64_t)key * p.k_ss);
+  int64_t kro, vro;   // element offsets of cache row `key`: contiguous, or page / row through the block table
+  if (p.block_table) {
+    const int64_t page = p.block_table[(int64_t)b * p.max_blocks + (key >> p.block_log2)];
+    const int64_t row = key & ((1 << p.block_log2) - 1);
+    kro = page * p.k_sb + (int64_t)h * p.k_sh + row * p.k_ss;
+    vro = page * p.v_sb + (int64_t)h * p.v_sh + row * p.v_ss;
+  } else {
+    kro = (int64_t)b * p.k_sb + (int64_t)h * p.k_sh + (int64_t)key * p.k_ss;
+    vro = (int64_t)b * p.v_sb + (int64_t)h * p.v_sh + (int64_t)key * p.v_ss;
+  }
+  *(u32x4*)(vd + 16 * c) = bf16x8_to_f16x8(*(const u32x4*)((const uint8_t*)p.v + vro * 2 + 16 * c));
+  const uint16_t* src = (const uint16_t*)p.k + kro;
   if (key < ext.past) {   // cached key: already transformed
-    *(u32x4*)(kd + 16 * c) = *(const u32x4*)((const uint8_t*)src + 16 * c);
+    *(u32x4*)(kd + 16 * c) = bf16x8_to_f16x8(*(const u32x4*)((const uint8_t*)src + 16 * c));
     return;
   }
   const u32x2 lo = *(const u32x2*)(src + 4 * c);
@@ -138,8 +154,8 @@ __global__ __launch_bounds__(256) void key_prologue_kernel(const PrefillParams p
       x[4 + j] = bb * cs + a * sn;
     }
   }
-  *(u32x2*)(kd + 8 * c) = u32x2{pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3])};
-  *(u32x2*)(kd + 128 + 8 * c) = u32x2{pack_bf16x2(x[4], x[5]), pack_bf16x2(x[6], x[7])};
+  *(u32x2*)(kd + 8 * c) = u32x2{pack_f16x2(x[0], x[1]), pack_f16x2(x[2], x[3])};
+  *(u32x2*)(kd + 128 + 8 * c) = u32x2{pack_f16x2(x[4], x[5]), pack_f16x2(x[6], x[7])};
 }
 
 // ----------------------------------------------------------------- phase 2: attention
@@ -178,7 +194,7 @@ __device__ __forceinline__ void dma_tile(uint32_t lds, const uint8_t* src, uint3
 // S^T for the 32 keys of a K' tile and the wave's two 32-row blocks:
 // s[rb][i] = S[key 8(i/4) + 4hf + i%4][query 32rb + n32] (raw dot products).
 // Each K' fragment read from LDS feeds both blocks.
-__device__ __forceinline__ void qk_tile(f32x16 (&s)[kRB], const LDS_AS uint8_t* kt, const bf16x8 (&qf)[kRB][8], int n32,
+__device__ __forceinline__ void qk_tile(f32x16 (&s)[kRB], const LDS_AS uint8_t* kt, const f16x8 (&qf)[kRB][8], int n32,
                                         int hf) {
   const LDS_AS uint8_t* base = kt + kKPitch * n32 + 64 * hf;
 #pragma unroll
@@ -190,7 +206,7 @@ __device__ __forceinline__ void qk_tile(f32x16 (&s)[kRB], const LDS_AS uint8_t* 
     const u32x4 a = *(const LDS_AS u32x4*)(base + 16 * ((kk & 3) + 8 * (kk >> 2)));
 #pragma unroll
     for (int rb = 0; rb < kRB; ++rb)
-      s[rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), qf[rb][kk], s[rb], 0, 0, 0);
+      s[rb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(as_f16x8(a), qf[rb][kk], s[rb], 0, 0, 0);
   }
 }
 
@@ -223,28 +239,28 @@ __device__ __forceinline__ void row_max(const f32x16 (&s)[kRB], float (&mx)[kRB]
   for (int rb = 0; rb < kRB; ++rb) mx[rb] = max_xor32(row_max16(s[rb])) * scale_log2;
 }
 
-// P = exp2(S scale log2(e) - m) as bf16 MFMA operands pf[rb][e] (keys 16e +
-// {4hf+t, 8+4hf+t}, t < 4).  The row sum l is taken over the bf16-rounded P
+// P = exp2(S scale log2(e) - m) as fp16 MFMA operands pf[rb][e] (keys 16e +
+// {4hf+t, 8+4hf+t}, t < 4).  The row sum l is taken over the fp16-rounded P
 // that the P V products use (v_dot2 of each packed pair with (1, 1)), so
 // numerator and denominator see the same weights.
 __device__ __forceinline__ void softmax_exp(f32x16 (&s)[kRB], const float (&m)[kRB], float (&l)[kRB], u32x4 (&pf)[kRB][2],
                                             float scale_log2) {
-  const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
+  const f16x2 one = {(_Float16)1.0f, (_Float16)1.0f};
 #pragma unroll
   for (int rb = 0; rb < kRB; ++rb) {
 #pragma unroll
     for (int i = 0; i < 16; ++i) s[rb][i] = fast_exp2(fmaf(s[rb][i], scale_log2, -m[rb]));
 #pragma unroll
     for (int e = 0; e < 2; ++e)
-      pf[rb][e] = u32x4{pack_bf16x2(s[rb][8 * e + 0], s[rb][8 * e + 1]), pack_bf16x2(s[rb][8 * e + 2], s[rb][8 * e + 3]),
-                        pack_bf16x2(s[rb][8 * e + 4], s[rb][8 * e + 5]), pack_bf16x2(s[rb][8 * e + 6], s[rb][8 * e + 7])};
+      pf[rb][e] = u32x4{pack_f16x2(s[rb][8 * e + 0], s[rb][8 * e + 1]), pack_f16x2(s[rb][8 * e + 2], s[rb][8 * e + 3]),
+                        pack_f16x2(s[rb][8 * e + 4], s[rb][8 * e + 5]), pack_f16x2(s[rb][8 * e + 6], s[rb][8 * e + 7])};
     float ps[2] = {0.f, 0.f};
 #pragma unroll
     for (int e = 0; e < 2; ++e)
 #pragma unroll
       for (int w = 0; w < 4; ++w)   // the (uint32_t) copy matters: hipcc bit-casts element 0 of a vector lvalue
-        ps[w & 1] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, (uint32_t)pf[rb][e][w]), one,
-                                                    ps[w & 1], false);
+        ps[w & 1] = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, (uint32_t)pf[rb][e][w]), one, ps[w & 1],
+                                           false);
     l[rb] += ps[0] + ps[1];
   }
 }
@@ -253,7 +269,9 @@ __device__ __forceinline__ void softmax_exp(f32x16 (&s)[kRB], const float (&m)[k
 // transposing reads of natural V rows: lane group g (16 lanes) covers dims
 // 32T + 16(g%2) .. +15 and keys R = 16e + 8a + 4(g/2) .. R+3 for a = 0, 1
 // (slots 4a .. 4a+3); source lane j of the group points at key R + j/4,
-// dims + 4(j%4) .. +3.  Each V^T fragment feeds both row blocks.
+// dims + 4(j%4) .. +3.  Each V^T fragment feeds both row blocks.  The
+// transposing read moves 16-bit elements as they are: the words are fp16,
+// the builtin's bf16 vector type only fixes their width.
 typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 bf16x4_v;
 
 __device__ __forceinline__ void pv_tile(f32x16 (&o)[kRB][4], const LDS_AS uint8_t* vt, const u32x4 (&pf)[kRB][2],
@@ -268,10 +286,10 @@ __device__ __forceinline__ void pv_tile(f32x16 (&o)[kRB][4], const LDS_AS uint8_
           __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LDS_AS bf16x4_v*)(base + kVPitch * (16 * e) + 64 * T));
       const bf16x4_v x1 =
           __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LDS_AS bf16x4_v*)(base + kVPitch * (16 * e + 8) + 64 * T));
-      const bf16x8 a = __builtin_shufflevector(x0, x1, 0, 1, 2, 3, 4, 5, 6, 7);
+      const f16x8 a = __builtin_bit_cast(f16x8, __builtin_shufflevector(x0, x1, 0, 1, 2, 3, 4, 5, 6, 7));
 #pragma unroll
       for (int rb = 0; rb < kRB; ++rb)
-        o[rb][T] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, as_bf16x8(pf[rb][e]), o[rb][T], 0, 0, 0);
+        o[rb][T] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, as_f16x8(pf[rb][e]), o[rb][T], 0, 0, 0);
     }
 }
 
@@ -308,7 +326,7 @@ struct WaveCtx {
 // l follow, after the P V products that used the old m.
 __device__ __forceinline__ void wave_tile(int t, f32x16 (&s_cur)[kRB], f32x16 (&s_next)[kRB],
                                           const LDS_AS uint8_t* kt_next, const LDS_AS uint8_t* vt,
-                                          const bf16x8 (&qf)[kRB][8], WaveState& ws, const WaveCtx& w, int lane) {
+                                          const f16x8 (&qf)[kRB][8], WaveState& ws, const WaveCtx& w, int lane) {
   const int n32 = lane & 31, hf = lane >> 5;
   u32x4 pf[kRB][2];
   qk_tile(s_next, kt_next, qf, n32, hf);
@@ -413,7 +431,7 @@ __global__ __launch_bounds__(kAttnThreads, kWavesPerSimd) void attention_kernel(
 
   // ---- query prologue: lane (n32, hf) owns rows wq0 + n32 and wq0 + 32 + n32
   //      of head hq, dims [32hf, 32hf+32) and [64+32hf, 64+32hf+32)
-  bf16x8 qf[kRB][8];
+  f16x8 qf[kRB][8];
   {
     u32x4 qlo[kRB][4], qhi[kRB][4];
 #pragma unroll
@@ -477,10 +495,10 @@ __global__ __launch_bounds__(kAttnThreads, kWavesPerSimd) void attention_kernel(
             xh[e] = hi * c + lo * s;
           }
         }
-        qf[rb][j] = as_bf16x8(u32x4{pack_bf16x2(xl[0], xl[1]), pack_bf16x2(xl[2], xl[3]),
-                                    pack_bf16x2(xl[4], xl[5]), pack_bf16x2(xl[6], xl[7])});
-        qf[rb][4 + j] = as_bf16x8(u32x4{pack_bf16x2(xh[0], xh[1]), pack_bf16x2(xh[2], xh[3]),
-                                        pack_bf16x2(xh[4], xh[5]), pack_bf16x2(xh[6], xh[7])});
+        qf[rb][j] = as_f16x8(u32x4{pack_f16x2(xl[0], xl[1]), pack_f16x2(xl[2], xl[3]),
+                                   pack_f16x2(xl[4], xl[5]), pack_f16x2(xl[6], xl[7])});
+        qf[rb][4 + j] = as_f16x8(u32x4{pack_f16x2(xh[0], xh[1]), pack_f16x2(xh[2], xh[3]),
+                                       pack_f16x2(xh[4], xh[5]), pack_f16x2(xh[6], xh[7])});
       }
     }
   }

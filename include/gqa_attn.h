@@ -108,7 +108,7 @@ typedef struct gqa_prefill_desc {
   int32_t num_kv_heads;    /* Hkv, Hq % Hkv == 0                                   */
   int32_t head_dim;        /* must be 128                                          */
   int32_t max_seq;         /* S: token rows per sequence in q / k / v / out        */
-  int32_t in_dtype;        /* must be GQA_BF16 (bf16 MFMA path)                    */
+  int32_t in_dtype;        /* must be GQA_BF16 (products on fp16 MFMA)             */
   int32_t out_dtype;       /* GQA_F32 or GQA_BF16                                  */
   int32_t causal;          /* 1: query i sees keys j <= i; 0: all keys < S_b       */
   int64_t q_stride_b, q_stride_h, q_stride_s;
@@ -119,6 +119,9 @@ typedef struct gqa_prefill_desc {
   float scale;             /* <= 0 selects 1/sqrt(head_dim)                        */
   int32_t max_chunk;       /* gqa_attn_prefill_chunk only: query / output rows per
                               sequence (T_max); 0 means max_seq                   */
+  int32_t block_size;      /* 0: contiguous caches; > 0: rows per page of a paged
+                              cache (gqa_attn_prefill_chunk_paged only), a power
+                              of two >= 16 dividing max_seq                        */
 } gqa_prefill_desc;
 
 /* Human-readable name of a status code (static storage; never NULL). */
@@ -250,8 +253,14 @@ gqa_status gqa_attn_prefill_workspace_size(const gqa_prefill_desc* desc, size_t*
  * Rows s >= n of out are not written; rows s >= n of q / k / v are not read.
  *
  * q: [B, Hq, max_seq, 128]; k, v: [B, Hkv, max_seq, 128]; out: [B, Hq,
- * max_seq, 128].  in_dtype must be GQA_BF16 (QK^T and P V run on bf16 MFMA
- * with f32 accumulation; q', k' and P are rounded to bf16 before the MFMA).
+ * max_seq, 128].  in_dtype must be GQA_BF16.  QK^T and P V run on fp16 MFMA
+ * with f32 accumulation: q', k' and P are rounded to fp16 (round to nearest
+ * even) and v converted to fp16 before the products.  The conversion of a
+ * bf16 input is exact for magnitudes in [2^-14, 65504] and loses at most
+ * 2^-25 absolute below; a v element, or a q' or k' element after the
+ * prologue, of magnitude 65520 or more becomes infinite and the output rows
+ * that read it are undefined (with the RMSNorm on, |q'|, |k'| are at most
+ * sqrt(128) max|gamma|).
  *
  * workspace: optional.  With a device buffer of at least
  * gqa_attn_prefill_workspace_size bytes (256-byte aligned; contents on entry
@@ -302,6 +311,24 @@ gqa_status gqa_attn_prefill_chunk(const gqa_prefill_desc* desc, const void* q, c
                                   const int32_t* positions, const void* q_norm_w, const void* k_norm_w,
                                   float rope_theta, void* out, void* workspace, size_t workspace_bytes,
                                   hipStream_t stream);
+
+/*
+ * gqa_attn_prefill_chunk over a paged KV cache: cache row j of sequence b is
+ *   k_pages[block_table[b * (max_seq / bs) + j / bs], kv, j % bs, :]
+ * (bs = desc->block_size; likewise v_pages), with element strides k_stride_b =
+ * between pages, k_stride_h = between heads inside a page, k_stride_s =
+ * between rows.  block_table: [B][max_seq / bs] int32 page indices (device);
+ * entries for blocks at or past ceil((past_lens[b] + T) / bs) are not read.
+ * Everything else is as gqa_attn_prefill_chunk.
+ * Errors: as gqa_attn_prefill_chunk; GQA_ERR_NULL for a missing block_table;
+ * GQA_ERR_SHAPE for block_size == 0 here, or != 0 with the contiguous entry
+ * points, or not a power of two >= 16 dividing max_seq.
+ */
+gqa_status gqa_attn_prefill_chunk_paged(const gqa_prefill_desc* desc, const void* q, const void* k_pages,
+                                        const void* v_pages, const int32_t* block_table, const int32_t* past_lens,
+                                        const int32_t* chunk_lens, const int32_t* positions, const void* q_norm_w,
+                                        const void* k_norm_w, float rope_theta, void* out, void* workspace,
+                                        size_t workspace_bytes, hipStream_t stream);
 
 #ifdef __cplusplus
 }

@@ -302,3 +302,18 @@ def test_decode_paged_errors_and_plan():
     assert st == G.GQA_OK and T == 128 and n == -(-4096 // 128)
     st, T, n = G.gqa_attn_decode_plan(ddesc(kv_split_tokens=100))
     assert st == G.GQA_OK and T == 100
+
+
+def test_prefill_chunk_paged_errors():
+    d = pdesc(max_chunk=64, block_size=64)
+    call = lambda dd, bt=FAKE, past=FAKE, ws=FAKE, wsb=1 << 40: G.gqa_attn_prefill_chunk_paged(
+        dd, FAKE, FAKE, FAKE, bt, past, FAKE, FAKE, NULL, NULL, 1e6, FAKE, ws, wsb, None)
+    assert call(d, bt=NULL) == G.GQA_ERR_NULL
+    assert call(d, past=NULL) == G.GQA_ERR_NULL
+    assert call(d, ws=NULL) == G.GQA_ERR_WORKSPACE
+    assert call(d, bt=FAKE + 2) == G.GQA_ERR_ALIGN
+    assert call(pdesc(max_chunk=64)) == G.GQA_ERR_SHAPE                    # contiguous descriptor
+    assert call_chunk(d) == G.GQA_ERR_SHAPE                                 # paged descriptor, contiguous entry
+    assert call_prefill(pdesc(block_size=64)) == G.GQA_ERR_SHAPE
+    for bad in (8, 24, 96):
+        assert call(pdesc(max_chunk=64, block_size=bad)) == G.GQA_ERR_SHAPE

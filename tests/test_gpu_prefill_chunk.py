@@ -1,6 +1,6 @@
 """GPU parity of gqa_attn_prefill_chunk (through the C ABI) against the fp64
-chunked-prefill oracle.  bf16 inputs, f32 accumulation and output:
-max |err| <= 1e-2.  Cached rows j < P hold the oracle's own post-prologue
+chunked-prefill oracle.  bf16 inputs, fp16 MFMA operands, f32 accumulation
+and output: max |err| <= 1e-2.  Cached rows j < P hold the oracle's own post-prologue
 keys rounded to bf16; the chunk's rows are raw; rows past P + T of the caches
 and rows past T of q are NaN, so a read of them shows up in the output.
 """
@@ -121,3 +121,34 @@ def test_qwen3_chunk_3072_plus_1024_sampled():
     r = ref(c, heads=heads, rows=rows)
     compare(out[0][heads][:, rows], r[0][heads][:, rows], ATOL, "qwen3 chunk sampled")
     assert np.all(np.isfinite(out))
+
+
+@pytest.mark.parametrize("bs", [16, 64, 256])
+def test_paged_chunk_equals_contiguous_bitwise(bs):
+    torch = require_gpu()
+    S = 512
+    c = make(B=2, Hq=10, Hkv=2, S=S, Tmax=128, past=[300, 0], chunk=[128, 77], seed=67)
+    log(f"case paged chunked prefill bs={bs}")
+    # the same logical cache as shuffled pages; blocks past the sequence are unmapped (-1)
+    rng = np.random.default_rng(bs)
+    nb = S // bs
+    perm = rng.permutation(2 * nb + 2)
+    table = perm[:2 * nb].reshape(2, nb).astype(np.int32)
+    kp = np.full((2 * nb + 2, 2, bs, 128), np.nan, dtype=np.float32)
+    vp = np.full_like(kp, np.nan)
+    for b in range(2):
+        used = -(-int(c["past"][b] + c["chunk"][b]) // bs)
+        for i in range(nb):
+            kp[table[b, i]] = c["k"][b][:, i * bs:(i + 1) * bs]
+            vp[table[b, i]] = c["v"][b][:, i * bs:(i + 1) * bs]
+        table[b, used:] = -1
+    bfd = torch.bfloat16
+    paged = G.prefill_chunk_paged(dev(c["q"], bfd), dev(kp, bfd), dev(vp, bfd), ints(table), ints(c["past"]),
+                                  ints(c["chunk"]), ints(c["pos"]), dev(c["gq"], bfd), dev(c["gk"], bfd), c["theta"])
+    torch.cuda.synchronize()
+    cont = run(c)
+    assert np.array_equal(valid(paged.cpu().numpy(), c), valid(cont, c))
+    K = O.paged_gather(kp, table, c["past"] + c["chunk"], bs, S)
+    V = O.paged_gather(vp, table, c["past"] + c["chunk"], bs, S)
+    want = O.prefill_chunk_ref(c["q"], K, V, c["past"], c["chunk"], c["pos"], c["gq"], c["gk"], c["theta"])
+    compare(valid(paged.cpu().numpy(), c), want, ATOL, f"paged chunk bs={bs}")
