@@ -92,10 +92,17 @@ int32_t decode_chunks_per_workgroup(const gqa_decode_desc* d, int32_t T, int32_t
   return cpw < 1 ? 1 : (int32_t)cpw;
 }
 
-// Decode workspace: [partial O: B * Hq * n * 128 f32] [partial (m, l): B * Hq * n * 2 f32].
-size_t decode_ws_bytes(const gqa_decode_desc* d, int32_t n) {
+// Decode workspace, with w = ceil(n / cpw) partition workgroups per (b, KV
+// head), each writing one partial per query head of its group:
+// [partial O: B * Hq * w * 128 f32] [partial (m, l): B * Hq * w * 2 f32].
+int32_t decode_workgroups_per_group(const gqa_decode_desc* d, int32_t T, int32_t n) {
+  const int32_t cpw = decode_chunks_per_workgroup(d, T, n);
+  return (n + cpw - 1) / cpw;
+}
+
+size_t decode_ws_bytes(const gqa_decode_desc* d, int32_t T, int32_t n) {
   if (n <= 1) return 0;
-  const size_t slots = (size_t)d->batch * (size_t)d->num_q_heads * (size_t)n;
+  const size_t slots = (size_t)d->batch * (size_t)d->num_q_heads * (size_t)decode_workgroups_per_group(d, T, n);
   return slots * (GQA_ATTN_HEAD_DIM + 2) * sizeof(float);
 }
 
@@ -176,7 +183,7 @@ gqa_status gqa_attn_decode_workspace_size(const gqa_decode_desc* desc, size_t* b
   if (st != GQA_OK) return st;
   int32_t T, n;
   decode_plan(desc, &T, &n);
-  *bytes = decode_ws_bytes(desc, n);
+  *bytes = decode_ws_bytes(desc, T, n);
   return GQA_OK;
 }
 
@@ -207,7 +214,7 @@ gqa_status prepare_decode(const gqa_decode_desc* d, const void* q, const void* k
   decode_plan(d, &T, &n);
   const int64_t wgs = (int64_t)n * d->batch * d->num_kv_heads;
   if (wgs > INT32_MAX) return GQA_ERR_SHAPE;
-  const size_t need = decode_ws_bytes(d, n);
+  const size_t need = decode_ws_bytes(d, T, n);
   if (need > 0) {
     if (workspace == nullptr || workspace_bytes < need) return GQA_ERR_WORKSPACE;
     if (((uintptr_t)workspace & 255u) != 0) return GQA_ERR_ALIGN;
@@ -221,9 +228,10 @@ gqa_status prepare_decode(const gqa_decode_desc* d, const void* q, const void* k
   p->q_norm_w = q_norm_w;
   p->k_norm_w = k_norm_w;
   p->out = out;
+  const int32_t wpg = decode_workgroups_per_group(d, T, n);
   if (need > 0) {
     p->ws_o = (float*)workspace;
-    p->ws_ml = p->ws_o + (size_t)d->batch * d->num_q_heads * n * GQA_ATTN_HEAD_DIM;
+    p->ws_ml = p->ws_o + (size_t)d->batch * d->num_q_heads * wpg * GQA_ATTN_HEAD_DIM;
   }
   p->q_sb = d->q_stride_b;
   p->q_sh = d->q_stride_h;
@@ -243,6 +251,7 @@ gqa_status prepare_decode(const gqa_decode_desc* d, const void* q, const void* k
   p->split = T;
   p->n_split = n;
   p->cpw = decode_chunks_per_workgroup(d, T, n);
+  p->wpg = wpg;
   p->out_bf16 = d->out_dtype == GQA_BF16;
   p->write_new_k = d->write_new_k != 0;
   if (block_table != nullptr) {

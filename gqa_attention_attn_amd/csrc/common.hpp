@@ -21,8 +21,8 @@ struct DecodeParams {
   const void* q_norm_w;   // may be null: no RMSNorm on q
   const void* k_norm_w;   // may be null: no RMSNorm on the new key row
   void* out;
-  float* ws_o;            // [B][Hq][n_split][128] unnormalised partial O
-  float* ws_ml;           // [B][Hq][n_split][2]   (m in log2 units, l)
+  float* ws_o;            // [B][Hq][wpg][128] unnormalised partial O, one per partition workgroup
+  float* ws_ml;           // [B][Hq][wpg][2]   (m in log2 units, l)
   int64_t q_sb, q_sh;     // element strides
   int64_t k_sb, k_sh, k_ss;
   int64_t v_sb, v_sh, v_ss;
@@ -30,6 +30,7 @@ struct DecodeParams {
   int32_t batch, num_q_heads, num_kv_heads, group, max_seq;
   int32_t split, n_split;
   int32_t cpw;            // chunks swept by one partition workgroup (1, or more when split % 32 == 0)
+  int32_t wpg;            // partition workgroups (= partial slots) per (b, KV head): ceil(n_split / cpw)
   int32_t out_bf16;
   int32_t write_new_k;    // store the new key's transformed row back into the cache slot
   const int32_t* block_table;  // paged caches: [B][max_blocks] page of each block of rows (null: contiguous)
@@ -105,7 +106,6 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
 
-// Element e (0..7) of 8 packed bf16 held in 4 dwords, as float.
 // Two f32 to packed fp16 (round to nearest even; beyond +-65504 -> +-inf).
 __device__ __forceinline__ uint32_t pack_f16x2(float lo, float hi) {
   const f16x2 v = {(_Float16)lo, (_Float16)hi};
@@ -114,6 +114,7 @@ __device__ __forceinline__ uint32_t pack_f16x2(float lo, float hi) {
 
 __device__ __forceinline__ f16x8 as_f16x8(u32x4 v) { return __builtin_bit_cast(f16x8, v); }
 
+// Element e (0..7) of 8 packed bf16 held in 4 dwords, as float.
 __device__ __forceinline__ float bf16_elem(const u32x4& v, int e) {
   uint32_t w = v[e >> 1];
   return (e & 1) ? bf16hi(w) : bf16lo(w);

@@ -529,27 +529,50 @@ __device__ __forceinline__ void write_zero_rows(const DecodeParams& p, int b, in
   }
 }
 
-// Merge of the 4 wave states of one chunk held in LDS buffer `buf` (ADR-0060
-// section 4, in-workgroup level) by `nthr` threads: thread t takes head
-// t/16 (+ nthr/16, ...) and dims 8 (t%16) .. +7; the result is the chunk's
-// partial (or, with a single chunk, the normalised output row).
-__device__ __forceinline__ void merge_chunk(const DecodeParams& p, const DecodeSmem& sm, int buf, int b, int h, int c,
+// The 4 wave states of one chunk held in LDS buffer `buf`, combined (ADR-0060
+// section 4, in-workgroup level) for head g, dims d8 .. d8+7: the chunk's
+// maximum M, sum l and unnormalised O.  The chunk holds at least one key, so
+// M is finite.
+__device__ __forceinline__ void chunk_state(const DecodeSmem& sm, int buf, int g, int d8, float& M, float& lt,
+                                            float (&acc)[8]) {
+  M = sm.mm[buf][0][g];
+#pragma unroll
+  for (int w = 1; w < kStreamWaves; ++w) M = fmaxf(M, sm.mm[buf][w][g]);
+  lt = 0.f;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) acc[j] = 0.f;
+#pragma unroll
+  for (int w = 0; w < kStreamWaves; ++w) {
+    const float sc = fast_exp2(sm.mm[buf][w][g] - M);   // 0 for a wave that saw no key
+    lt += sc * sm.ml[buf][w][g];
+    const float* src = &sm.mo[buf][w][g][d8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc[j] += sc * src[j];
+  }
+}
+
+__device__ __forceinline__ void store_partial(const DecodeParams& p, int b, int hq, int wc, int d8, bool ml, float M,
+                                              float lt, const float (&acc)[8]) {
+  const int64_t slot = ((int64_t)b * p.num_q_heads + hq) * p.wpg + wc;
+  float* wo = p.ws_o + slot * kHeadDim + d8;
+  *(f32x4*)wo = f32x4{acc[0], acc[1], acc[2], acc[3]};
+  *(f32x4*)(wo + 4) = f32x4{acc[4], acc[5], acc[6], acc[7]};
+  if (ml) {
+    p.ws_ml[2 * slot] = M;
+    p.ws_ml[2 * slot + 1] = lt;
+  }
+}
+
+// Merge of the 4 wave states of the workgroup's only chunk by `nthr` threads:
+// thread t takes head t/16 (+ nthr/16, ...) and dims 8 (t%16) .. +7; the
+// result is the workgroup's partial in slot wc (or, with a single chunk in
+// the plan, the normalised output row).
+__device__ __forceinline__ void merge_chunk(const DecodeParams& p, const DecodeSmem& sm, int buf, int b, int h, int wc,
                                             int t, int nthr) {
   const int G = p.group, d8 = (t & 15) * 8;
   for (int g = t >> 4; g < G; g += nthr >> 4) {
-    float M = sm.mm[buf][0][g];
-#pragma unroll
-    for (int w = 1; w < kStreamWaves; ++w) M = fmaxf(M, sm.mm[buf][w][g]);
-    float lt = 0.f;
-    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int w = 0; w < kStreamWaves; ++w) {
-      const float sc = fast_exp2(sm.mm[buf][w][g] - M);   // 0 for a wave that saw no key
-      lt += sc * sm.ml[buf][w][g];
-      const float* src = &sm.mo[buf][w][g][d8];
-#pragma unroll
-      for (int j = 0; j < 8; ++j) acc[j] += sc * src[j];
-    }
+    float M, lt, acc[8];
+    chunk_state(sm, buf, g, d8, M, lt, acc);
     const int hq = h * G + g;
     if (p.n_split == 1) {
       const float inv = 1.0f / lt;
@@ -562,24 +585,53 @@ __device__ __forceinline__ void merge_chunk(const DecodeParams& p, const DecodeS
         *(f32x4*)(o + 4 * d8 + 16) = f32x4{acc[4] * inv, acc[5] * inv, acc[6] * inv, acc[7] * inv};
       }
     } else {
-      const int64_t slot = ((int64_t)b * p.num_q_heads + hq) * p.n_split + c;
-      float* wo = p.ws_o + slot * kHeadDim + d8;
-      *(f32x4*)wo = f32x4{acc[0], acc[1], acc[2], acc[3]};
-      *(f32x4*)(wo + 4) = f32x4{acc[4], acc[5], acc[6], acc[7]};
-      if ((t & 15) == 0) {
-        p.ws_ml[2 * slot] = M;
-        p.ws_ml[2 * slot + 1] = lt;
-      }
+      store_partial(p, b, hq, wc, d8, (t & 15) == 0, M, lt, acc);
     }
   }
 }
 
+// Running log-sum-exp merge of the chunks a workgroup sweeps, kept by the 64
+// lanes of the prologue wave: lane t holds heads t/16 + 4k (k < 4) at dims
+// 8 (t%16) .. +7.  Seeded (-inf, 0, 0).
+struct RunMerge {
+  float m[4], l[4];
+  float o[4][8];
+};
+
+__device__ __forceinline__ void fold_chunk(const DecodeParams& p, const DecodeSmem& sm, int buf, int lane,
+                                           RunMerge& r) {
+  const int d8 = (lane & 15) * 8;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int g = (lane >> 4) + 4 * k;
+    if (g < p.group) {
+      float M, lt, acc[8];
+      chunk_state(sm, buf, g, d8, M, lt, acc);
+      const float mn = fmaxf(r.m[k], M);
+      const float a = fast_exp2(r.m[k] - mn), c = fast_exp2(M - mn);   // a = 0 on the first chunk
+      r.l[k] = a * r.l[k] + c * lt;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) r.o[k][j] = a * r.o[k][j] + c * acc[j];
+      r.m[k] = mn;
+    }
+  }
+}
+
+__device__ __forceinline__ void store_run(const DecodeParams& p, const RunMerge& r, int b, int h, int wc, int lane) {
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int g = (lane >> 4) + 4 * k;
+    if (g < p.group) store_partial(p, b, h * p.group + g, wc, (lane & 15) * 8, (lane & 15) == 0, r.m[k], r.l[k], r.o[k]);
+  }
+}
+
 // A workgroup sweeps `cpw` consecutive chunks of one (b, KV head) group and
-// writes one partial per chunk.  The streaming waves load continuously across
-// chunk boundaries; at the end of each chunk they leave their states in one
-// of two LDS buffers and meet the prologue wave at a barrier, after which the
-// prologue wave merges that chunk while they sweep the next one.  (Chunks are
-// multiples of 32 keys whenever cpw > 1, so no step spans two chunks.)
+// writes one partial: the log-sum-exp merge of its chunks.  The streaming
+// waves load continuously across chunk boundaries; at the end of each chunk
+// they leave their states in one of two LDS buffers and meet the prologue
+// wave at a barrier, after which the prologue wave folds that chunk into its
+// running merge while they sweep the next one.  (Chunks are multiples of 32
+// keys whenever cpw > 1, so no step spans two chunks.)
 // Two waves per SIMD at most (one workgroup of 5 waves per compute unit): no
 // register spills, which matters most for long sweeps (a spill reload would
 // queue behind the wave's in-flight K/V loads).
@@ -665,7 +717,7 @@ __global__ __launch_bounds__(kThreads, BF16 ? 2 : 1) void decode_partition_kerne
   __builtin_amdgcn_s_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 
-  if (c0 >= L) {     // no keys in this range
+  if (c0 >= L) {     // no keys in this range: no partial, no arrival
     if (cf == 0 && direct) write_zero_rows(p, b, h, tid);   // L == 0: all-zero output rows
     return;
   }
@@ -715,12 +767,25 @@ __global__ __launch_bounds__(kThreads, BF16 ? 2 : 1) void decode_partition_kerne
       __syncthreads();
     }
   } else {
-    // the prologue wave merges chunk j while the streaming waves sweep chunk j+1
+    // the prologue wave folds chunk j while the streaming waves sweep chunk j+1,
+    // then the last chunk, and stores the workgroup's partial
+    RunMerge run;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      run.m[k] = -INFINITY;
+      run.l[k] = 0.f;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) run.o[k][j] = 0.f;
+    }
     for (int j = 0; j + 1 < nchunks; ++j) {
       __syncthreads();
-      merge_chunk(p, sm, j & 1, b, h, cf + j, lane, 64);
+      fold_chunk(p, sm, j & 1, lane, run);
     }
     __syncthreads();
+    if (nchunks > 1) {
+      fold_chunk(p, sm, (nchunks - 1) & 1, lane, run);
+      store_run(p, run, b, h, wc, lane);
+    }
   }
   // ---- the new key's transformed row replaces the raw one in its cache slot:
   //      every read of that row (the prologue's and the streaming waves' step
@@ -731,13 +796,14 @@ __global__ __launch_bounds__(kThreads, BF16 ? 2 : 1) void decode_partition_kerne
     if (BF16) *(u32x2*)(row + 8 * lane) = u32x2{pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3])};
     else *(f32x4*)(row + 16 * lane) = y;
   }
-  // ---- the last chunk: every thread of the workgroup merges
-  merge_chunk(p, sm, (nchunks - 1) & 1, b, h, cf + nchunks - 1, tid, kThreads);
+  // ---- a single chunk: every thread of the workgroup merges its wave states
+  if (nchunks == 1) merge_chunk(p, sm, 0, b, h, wc, tid, kThreads);
 }
 
 // ----------------------------------------------------------------- merge kernel
 // One workgroup per (q head, sequence): out = sum_c 2^(m_c - M) O_c / sum_c 2^(m_c - M) l_c
-// over the n = ceil(L / T) chunks that hold keys (ADR-0060 section 4).  Thread
+// over the partials of the n = ceil(L / (cpw T)) partition workgroups that
+// hold keys (ADR-0060 section 4).  Thread
 // (group sg, dims 4*d4 .. 4*d4+3) folds chunks sg, sg + 16, ... with a running
 // maximum, kMergeUnroll chunks per batch of loads; the 16 group states are then
 // merged through LDS.
@@ -766,7 +832,8 @@ __global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(const Decod
   }
   int L = p.seq_lens[b];
   L = L < 0 ? 0 : (L > p.max_seq ? p.max_seq : L);
-  const int n = (L + p.split - 1) / p.split;
+  const int64_t span = (int64_t)p.cpw * p.split;
+  const int n = (int)((L + span - 1) / span);   // partition workgroups that wrote a partial
   uint8_t* o = (uint8_t*)p.out + ((int64_t)b * p.o_sb + (int64_t)hq * p.o_sh) * (p.out_bf16 ? 2 : 4);
   if (n == 0) {
     if (tid < 32) {
@@ -775,7 +842,7 @@ __global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(const Decod
     }
     return;
   }
-  const int64_t slot0 = ((int64_t)b * p.num_q_heads + hq) * p.n_split;
+  const int64_t slot0 = ((int64_t)b * p.num_q_heads + hq) * p.wpg;
   const int d4 = tid & 31, sg = tid >> 5;
   float M = -INFINITY, ls = 0.f;
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};

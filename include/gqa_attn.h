@@ -141,7 +141,10 @@ gqa_status gqa_attn_decode_plan(const gqa_decode_desc* desc, int32_t* split_toke
 /*
  * Bytes of device workspace gqa_attn_decode needs for `desc` (host only, no
  * HIP call).  0 when the plan has a single chunk.  The workspace holds one
- * unnormalised partial (m, l, O[128]) in f32 per (b, q head, chunk).
+ * unnormalised partial (m, l, O[128]) in f32 per (b, q head, partition
+ * workgroup); a partition workgroup sweeps c >= 1 consecutive chunks (c > 1
+ * only with few (b, KV head) groups and many chunks, to keep the grid near
+ * one workgroup per compute unit), so there are ceil(n / c) per (b, q head).
  */
 gqa_status gqa_attn_decode_workspace_size(const gqa_decode_desc* desc, size_t* bytes);
 
@@ -191,15 +194,16 @@ gqa_status gqa_attn_decode(const gqa_decode_desc* desc, const void* q, const voi
  * the same stream.
  *
  * gqa_attn_decode_partition: the split-KV partition step (ADR-0060 sections
- * 3 and 5.2 with the fused prologue).  Each (b, KV head, chunk) writes one
- * unnormalised partial (m, l, O) per query head of its group to `workspace`
- * (m in log2 units: scores are scaled by log2(e)).  When the plan has a
- * single chunk it writes the normalised result to `out` instead and needs no
- * workspace.
+ * 3 and 5.2 with the fused prologue).  Each partition workgroup (b, KV head,
+ * a run of c consecutive chunks) writes one unnormalised partial (m, l, O)
+ * per query head of its group to `workspace`: the log-sum-exp merge of its
+ * chunks' partials (m in log2 units: scores are scaled by log2(e)).  When the
+ * plan has a single chunk it writes the normalised result to `out` instead
+ * and needs no workspace.
  *
  * gqa_attn_decode_merge: the log-sum-exp merge step (ADR-0060 section 4):
- * out[b, h, :] = sum_c 2^(m_c - M) O_c / sum_c 2^(m_c - M) l_c over the
- * ceil(L / T) chunks that hold keys; L = 0 writes zeros.  Reads only
+ * out[b, h, :] = sum_w 2^(m_w - M) O_w / sum_w 2^(m_w - M) l_w over the
+ * ceil(L / (c T)) partition workgroups that hold keys; L = 0 writes zeros.  Reads only
  * `workspace` and seq_lens; a no-op returning GQA_OK when the plan has a
  * single chunk.
  * Errors: as gqa_attn_decode.
@@ -235,8 +239,8 @@ gqa_status gqa_attn_decode_paged(const gqa_decode_desc* desc, const void* q, con
 
 /*
  * Bytes of the optional prefill workspace (host only, no HIP call):
- * B * Hkv * ceil(max_seq / 32) * 9216 * 2: per 32-key tile, the bf16 K'
- * rows (norm + RoPE applied) and a copy of the V rows, in the padded row
+ * B * Hkv * ceil(max_seq / 32) * 9216 * 2: per 32-key tile, the K' rows
+ * (norm + RoPE applied) and the V rows, both in fp16, in the padded row
  * layout the attention tiles have in on-chip memory.
  */
 gqa_status gqa_attn_prefill_workspace_size(const gqa_prefill_desc* desc, size_t* bytes);

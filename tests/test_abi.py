@@ -111,12 +111,15 @@ def pdesc(**kw):
 
 
 def test_decode_plan_and_workspace_arithmetic():
-    # explicit chunk 512 over 131072 keys: 256 chunks; workspace = B*Hq*n*(128+2)*4
+    # explicit chunk 512 over 131072 keys: 256 chunks per (b, KV head); with 8
+    # groups a partition workgroup sweeps 8 chunks (256 * 8 / 256 target
+    # workgroups), so 32 workgroups per group write one partial each:
+    # workspace = B*Hq*32*(128+2)*4
     d = ddesc(batch=1, num_q_heads=64, max_seq=131072, kv_split_tokens=512,
               k_stride_b=8 * 131072 * 128, k_stride_h=131072 * 128, v_stride_b=8 * 131072 * 128,
               v_stride_h=131072 * 128, q_stride_b=64 * 128, out_stride_b=64 * 128)
     assert G.gqa_attn_decode_plan(d) == (G.GQA_OK, 512, 256)
-    assert G.gqa_attn_decode_workspace_size(d) == (G.GQA_OK, 1 * 64 * 256 * 130 * 4)
+    assert G.gqa_attn_decode_workspace_size(d) == (G.GQA_OK, 1 * 64 * 32 * 130 * 4)
     # no split: chunk >= max_seq -> one chunk, no workspace
     d2 = ddesc(kv_split_tokens=4096)
     assert G.gqa_attn_decode_plan(d2) == (G.GQA_OK, 4096, 1)
@@ -190,6 +193,7 @@ def test_decode_pointer_errors():
 def test_decode_workspace_errors():
     d = ddesc(kv_split_tokens=512)
     st, need = G.gqa_attn_decode_workspace_size(d)
+    # 8 chunks of 512, one per workgroup (16 groups): 8 partials per (b, q head)
     assert st == G.GQA_OK and need == 2 * 40 * 8 * 130 * 4
     assert call_decode(d, ws=NULL, wsb=need) == G.GQA_ERR_WORKSPACE
     assert call_decode(d, ws=FAKE, wsb=need - 1) == G.GQA_ERR_WORKSPACE
