@@ -90,6 +90,12 @@ def lib() -> ctypes.CDLL:
         if not os.path.exists(LIB_PATH):
             raise RuntimeError(f"{LIB_PATH} is not built (python -m gqa_attention_attn_amd.build); "
                                "there is no fallback implementation")
+        # The library needs the HIP runtime by its soname (libamdhip64.so.7),
+        # as does the copy torch ships.  Loaded after torch, the library binds
+        # to torch's runtime, so torch's device memory and streams are valid
+        # for it; loaded first, it would bring in the system runtime and torch
+        # a second one, and the library's launches would fail.
+        import torch  # noqa: F401
         L = ctypes.CDLL(LIB_PATH)
         vp, i32p, szp = ctypes.c_void_p, ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_size_t)
         L.gqa_attn_status_string.argtypes = [ctypes.c_int]

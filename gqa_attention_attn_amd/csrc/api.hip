@@ -321,7 +321,8 @@ gqa_status gqa_attn_prefill_workspace_size(const gqa_prefill_desc* desc, size_t*
   if (bytes == nullptr) return GQA_ERR_NULL;
   const gqa_status st = check_prefill_desc(desc);
   if (st != GQA_OK) return st;
-  *bytes = gqa::prefill_workspace_bytes(desc->batch, desc->num_kv_heads, desc->max_seq);
+  *bytes = gqa::prefill_workspace_bytes(desc->batch, desc->num_q_heads, desc->num_kv_heads, desc->max_seq,
+                                        desc->max_chunk > 0 ? desc->max_chunk : desc->max_seq, desc->causal != 0);
   return GQA_OK;
 }
 
@@ -346,7 +347,9 @@ gqa_status prepare_prefill(const gqa_prefill_desc* d, const void* q, const void*
       !aligned16(k_norm_w) || ((uintptr_t)lens & 3u) || ((uintptr_t)positions & 3u) || ((uintptr_t)past_lens & 3u))
     return GQA_ERR_ALIGN;
   if (workspace != nullptr) {
-    if (workspace_bytes < gqa::prefill_workspace_bytes(d->batch, d->num_kv_heads, d->max_seq)) return GQA_ERR_WORKSPACE;
+    if (workspace_bytes < gqa::prefill_workspace_bytes(d->batch, d->num_q_heads, d->num_kv_heads, d->max_seq,
+                                                       d->max_chunk > 0 ? d->max_chunk : d->max_seq, d->causal != 0))
+      return GQA_ERR_WORKSPACE;
     if (((uintptr_t)workspace & 255u) != 0) return GQA_ERR_ALIGN;
   }
   gqa::PrefillParams& p = *pp;

@@ -63,6 +63,11 @@ struct PrefillParams {
   int32_t block_log2;     // paged: log2(rows per page)
   int32_t max_blocks;     // paged: row length of block_table
   int32_t max_chunk;      // query / output rows per sequence (max_seq for a plain prefill)
+  int32_t span_tiles;     // two-phase: at most this many 32-key tiles per attention workgroup
+  int32_t n_spans;        // two-phase: key spans per query block in the grid (1: no split)
+  uint32_t* counters;     // two-phase, n_spans > 1: arrivals per (b, q head, query block)
+  int32_t n_counters;
+  float* partials;        // two-phase, n_spans > 1: (m, l, O) of each (b, q head, query block, span)
   int32_t heads_per_wg;   // HC: query heads of one KV head batched in a workgroup
   int32_t block_q;        // BQ: query tokens per workgroup (multiple of 32)
   int32_t n_qblocks;      // ceil(max_seq / BQ)
@@ -72,12 +77,23 @@ struct PrefillParams {
   double rope_log2_theta;
 };
 
-// Launchers (return the hipGetLastError() of their launches).
+// Launch of `kernel` with its arguments; returns the status of this launch
+// (hipLaunchKernel), not a sticky error an earlier HIP call of the process
+// may have left behind.
+template <typename... Args>
+inline hipError_t launch_kernel(void (*kernel)(Args...), dim3 grid, dim3 block, hipStream_t stream, Args... args) {
+  void* ptrs[] = {(void*)&args...};
+  return hipLaunchKernel((const void*)kernel, grid, block, ptrs, 0, stream);
+}
+
+// Launchers (return the status of their launches).
 hipError_t launch_decode_partition(const DecodeParams& p, bool in_bf16, hipStream_t stream);
 hipError_t launch_decode_merge(const DecodeParams& p, hipStream_t stream);
 hipError_t launch_prefill_fused(const PrefillParams& p, hipStream_t stream);
 hipError_t launch_prefill_phased(const PrefillParams& p, void* workspace, hipStream_t stream);
-size_t prefill_workspace_bytes(int batch, int num_kv_heads, int max_seq);
+// Bytes of the two-phase prefill workspace, for a plain prefill (max_chunk =
+// max_seq) and a chunked one (max_chunk <= max_seq) alike.
+size_t prefill_workspace_bytes(int batch, int num_q_heads, int num_kv_heads, int max_seq, int max_chunk, bool causal);
 
 // Prefill workgroups hold HC * BQ / 32 waves of 32 query rows, at most this many.
 constexpr int kPrefillMaxWaves = 10;

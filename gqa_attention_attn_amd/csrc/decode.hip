@@ -902,25 +902,22 @@ __global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(const Decod
 }
 
 template <bool BF16>
-void launch_partition(const DecodeParams& p, hipStream_t stream) {
+hipError_t launch_partition(const DecodeParams& p, hipStream_t stream) {
   const int wpg = (p.n_split + p.cpw - 1) / p.cpw;
   const dim3 grid(wpg * p.num_kv_heads * p.batch);
-  if (p.block_table != nullptr) hipLaunchKernelGGL((decode_partition_kernel<BF16, true>), grid, dim3(kThreads), 0, stream, p);
-  else hipLaunchKernelGGL((decode_partition_kernel<BF16, false>), grid, dim3(kThreads), 0, stream, p);
+  if (p.block_table != nullptr) return launch_kernel(decode_partition_kernel<BF16, true>, grid, dim3(kThreads), stream, p);
+  return launch_kernel(decode_partition_kernel<BF16, false>, grid, dim3(kThreads), stream, p);
 }
 
 }  // namespace
 
 hipError_t launch_decode_partition(const DecodeParams& p, bool in_bf16, hipStream_t stream) {
-  if (in_bf16) launch_partition<true>(p, stream);
-  else launch_partition<false>(p, stream);
-  return hipGetLastError();
+  return in_bf16 ? launch_partition<true>(p, stream) : launch_partition<false>(p, stream);
 }
 
 hipError_t launch_decode_merge(const DecodeParams& p, hipStream_t stream) {
   if (p.n_split == 1) return hipSuccess;
-  hipLaunchKernelGGL(decode_merge_kernel, dim3(p.num_q_heads * p.batch), dim3(kMergeThreads), 0, stream, p);
-  return hipGetLastError();
+  return launch_kernel(decode_merge_kernel, dim3(p.num_q_heads * p.batch), dim3(kMergeThreads), stream, p);
 }
 
 }  // namespace gqa

@@ -394,9 +394,8 @@ __global__ __launch_bounds__(kMaxThreads) void prefill_kernel(const PrefillParam
 hipError_t launch_prefill_fused(const PrefillParams& p, hipStream_t stream) {
   const int waves = p.heads_per_wg * p.block_q / 32;
   const dim3 grid(p.n_qblocks * (p.group / p.heads_per_wg) * p.num_kv_heads * p.batch);
-  if (64 * waves >= kUnits) hipLaunchKernelGGL(prefill_kernel<1>, grid, dim3(64 * waves), 0, stream, p);
-  else hipLaunchKernelGGL(prefill_kernel<2>, grid, dim3(64 * waves), 0, stream, p);
-  return hipGetLastError();
+  if (64 * waves >= kUnits) return launch_kernel(prefill_kernel<1>, grid, dim3(64 * waves), stream, p);
+  return launch_kernel(prefill_kernel<2>, grid, dim3(64 * waves), stream, p);
 }
 
 }  // namespace gqa

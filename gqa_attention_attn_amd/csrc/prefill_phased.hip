@@ -16,9 +16,9 @@
 // tile) pair, each key row is transformed once (about 32x less VALU work for
 // a 4096-token causal prefill) at the cost of writing and re-reading K' and V.
 //
-// Attention mapping: a workgroup = (sequence, query head, 128-query block) of
-// 4 waves x 32 query rows, two waves per SIMD (two workgroups per compute
-// unit).  32-key tiles are filled by linear direct-to-LDS copies (no register
+// Attention mapping: a workgroup = (sequence, query head, 128-query block,
+// key span) of 4 waves x 32 query rows, three waves per SIMD (three
+// workgroups per compute unit).  32-key tiles are filled by linear direct-to-LDS copies (no register
 // staging) from the padded workspace; V is read back transposed by
 // ds_read_b64_tr_b16 as the V^T operand.  S^T = K' Q'^T and O^T = V^T P^T run
 // on v_mfma_f32_32x32x16_f16 (the bf16 rate, with 11 significand bits for
@@ -27,8 +27,13 @@
 // scores of tile t+1 are computed beside the exponentials of tile t, then P V
 // of tile t, then the row maxima of tile t+1; K' is loaded two tiles ahead
 // and V one tile ahead, so one barrier per tile suffices.  A 1-D grid ordered
-// so a (sequence, KV head) group's workgroups share one XCD's L2, heaviest
-// block first.
+// so a (sequence, KV head) group's workgroups share one XCD's L2, largest
+// item first; when the grid is short, the key range of a long query block is
+// split over several workgroups whose states are merged by the last of them.
+#include <algorithm>
+#include <utility>
+#include <vector>
+
 #include "common.hpp"
 
 namespace gqa {
@@ -39,11 +44,11 @@ constexpr int kBM = 128;                 // query rows per workgroup
 // 32-row MFMA blocks per wave.  Two blocks per wave would share every K' and
 // V operand read from LDS (half the LDS traffic per product), but their
 // registers leave one wave per SIMD, whose in-order issue serialises the
-// matrix and vector work; one block per wave with two waves per SIMD is
+// matrix and vector work; one block per wave with three waves per SIMD is
 // faster.
 constexpr int kRB = 1;
 constexpr int kWaves = kBM / (32 * kRB);  // waves per workgroup
-constexpr int kWavesPerSimd = 2;
+constexpr int kWavesPerSimd = 3;   // 168 VGPRs; the tile loop holds no spill (the span merge does)
 constexpr int kAttnThreads = 64 * kWaves;
 constexpr int kBN = 32;                  // keys per tile
 constexpr float kLazyRescale = 8.0f;     // rescale O only when a row max grows by more than 2^8
@@ -94,6 +99,9 @@ __global__ __launch_bounds__(256) void key_prologue_kernel(const PrefillParams p
   __shared__ double inv_rev[kHeadDim / 2];
   const int b = blockIdx.z, h = blockIdx.y;
   const int tid = threadIdx.x, r = tid >> 4, c = tid & 15;
+  // the attention kernel's arrival counters start every call at zero
+  if (p.counters != nullptr && b == 0 && h == 0)
+    for (int i = blockIdx.x * 256 + tid; i < p.n_counters; i += gridDim.x * 256) p.counters[i] = 0;
   const bool rope = p.rope_theta > 0.0;
   if (tid < 64 && rope) inv_rev[tid] = rope_inv_freq(tid, p.rope_log2_theta) * 0.15915494309189535;
   __syncthreads();
@@ -298,6 +306,90 @@ struct WaveState {
   float m[kRB], l[kRB];
 };
 
+// ---- split key ranges ("ADR-0060: AHBM GQA Fused Attention Kernel
+// (Llama3-70B)" section 4: partials (m, l, O) of disjoint key ranges combine
+// by the log-sum-exp merge).  A query block whose visible keys span more
+// than span_tiles tiles is cut into ns = ceil(tiles / span_tiles) nearly
+// equal key spans, one workgroup each, so that no workgroup carries the whole
+// causal row of the last blocks.  Each span writes its unnormalised state in
+// the lanes' own register layout, then arrives at the block's counter; the
+// last to arrive merges the other spans' states into its registers and
+// writes out.  Partial stores and loads are device-coherent (they bypass the
+// non-coherent per-XCD L2s); a workgroup's stores have completed before its
+// arrival.  No workgroup waits for another.
+static_assert(kRB == 1, "partial layout: one 32-row block per wave");
+constexpr int kPartO = kWaves * 16 * 64 * 4;           // floats of O: [wave][j][lane][4]
+constexpr int kPartFloats = kPartO + kWaves * 64 * 2;  // + (m, l) per lane
+constexpr int kMaxOrder = 1024;
+
+// Workgroup order of the (query block, span) items of one (sequence, head):
+// rank -> qb * n_spans + span, largest estimated item first; n == 0 means
+// query blocks in descending order, spans in order.
+struct AttnOrder {
+  uint16_t item[kMaxOrder];
+  int32_t n;
+};
+
+// Device-scope (sc1) buffer accesses to one partial slot: written through to,
+// and read from, the device coherence point, past the per-XCD L2s.  The
+// resource spans the slot only (accesses beyond it would be dropped).
+constexpr int kDeviceScope = 16;   // cache-policy bit sc1
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t slot_rsrc(const float* slot) {
+  return __builtin_amdgcn_make_buffer_rsrc((void*)slot, 0, kPartFloats * 4, 0x00020000);
+}
+
+__device__ __forceinline__ void store_partial(const float* slot, const WaveState& ws, int wave, int lane) {
+  const __amdgpu_buffer_rsrc_t r = slot_rsrc(slot);
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    const f32x4 v = {ws.o[0][j >> 2][4 * (j & 3)], ws.o[0][j >> 2][4 * (j & 3) + 1], ws.o[0][j >> 2][4 * (j & 3) + 2],
+                     ws.o[0][j >> 2][4 * (j & 3) + 3]};
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), r, ((wave * 16 + j) * 64 + lane) * 16, 0,
+                                           kDeviceScope);
+  }
+  __builtin_amdgcn_raw_buffer_store_b64(u32x2{__float_as_uint(ws.m[0]), __float_as_uint(ws.l[0])}, r,
+                                        (kPartO + (wave * 64 + lane) * 2) * 4, 0, kDeviceScope);
+}
+
+__device__ __forceinline__ f32x4 load_o4(__amdgpu_buffer_rsrc_t r, int wave, int j, int lane) {
+  return __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, ((wave * 16 + j) * 64 + lane) * 16, 0,
+                                                                          kDeviceScope));
+}
+
+__device__ __forceinline__ void load_ml(__amdgpu_buffer_rsrc_t r, int wave, int lane, float& m, float& l) {
+  const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(r, (kPartO + (wave * 64 + lane) * 2) * 4, 0, kDeviceScope);
+  m = __uint_as_float(v[0]);
+  l = __uint_as_float(v[1]);
+}
+
+__device__ __forceinline__ void load_partial(WaveState& ws, const float* slot, int wave, int lane) {
+  const __amdgpu_buffer_rsrc_t r = slot_rsrc(slot);
+  load_ml(r, wave, lane, ws.m[0], ws.l[0]);
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    const f32x4 x = load_o4(r, wave, j, lane);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) ws.o[0][j >> 2][4 * (j & 3) + i] = x[i];
+  }
+}
+
+// ws <- merge(ws, the partial in slot): M = max(m, m'), scale each side by 2^(m - M).
+__device__ __forceinline__ void merge_partial(WaveState& ws, const float* slot, int wave, int lane) {
+  const __amdgpu_buffer_rsrc_t r = slot_rsrc(slot);
+  float mk, lk;
+  load_ml(r, wave, lane, mk, lk);
+  const float M = __builtin_elementwise_maximum(ws.m[0], mk);   // both finite: every row sees each span
+  const float a = fast_exp2(ws.m[0] - M), c = fast_exp2(mk - M);
+  ws.l[0] = a * ws.l[0] + c * lk;
+  ws.m[0] = M;
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    const f32x4 x = load_o4(r, wave, j, lane);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) ws.o[0][j >> 2][4 * (j & 3) + i] = a * ws.o[0][j >> 2][4 * (j & 3) + i] + c * x[i];
+  }
+}
+
 struct WaveCtx {
   int wq0;          // first query row of the wave (of the T new tokens)
   int qrow[kRB];    // this lane's query row in each block
@@ -356,16 +448,41 @@ __device__ __forceinline__ void wave_tile(int t, f32x16 (&s_cur)[kRB], f32x16 (&
   }
 }
 
+// out rows of this lane: O / l (l summed over the two lane halves).
+__device__ __forceinline__ void write_rows(const PrefillParams& p, const WaveState& ws, const WaveCtx& wc, int b, int hq,
+                                           int T, int hf) {
+#pragma unroll
+  for (int rb = 0; rb < kRB; ++rb) {
+    const float l = sum_xor32(ws.l[rb]);
+    if (wc.qrow[rb] >= T) continue;
+    const float inv = 1.0f / l;
+    uint8_t* orow = (uint8_t*)p.out +
+                    ((int64_t)b * p.o_sb + (int64_t)hq * p.o_sh + (int64_t)wc.qrow[rb] * p.o_ss) * (p.out_bf16 ? 2 : 4);
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+#pragma unroll
+      for (int a = 0; a < 4; ++a) {
+        const int d0 = 32 * t + 8 * a + 4 * hf;
+        const float v0 = ws.o[rb][t][4 * a] * inv, v1 = ws.o[rb][t][4 * a + 1] * inv;
+        const float v2 = ws.o[rb][t][4 * a + 2] * inv, v3 = ws.o[rb][t][4 * a + 3] * inv;
+        if (p.out_bf16) *(u32x2*)(orow + 2 * d0) = u32x2{pack_bf16x2(v0, v1), pack_bf16x2(v2, v3)};
+        else *(f32x4*)(orow + 4 * d0) = f32x4{v0, v1, v2, v3};
+      }
+    }
+  }
+}
+
 // Pipeline per tile t (one barrier): at the start of step t the copies of
 // K'_{t+2} (into the buffer of K'_t, whose scores were computed in step t-1)
 // and of V_{t+1} (into the buffer of V_{t-1}) are issued; step t computes the
 // scores of tile t+1 and the softmax and P V of tile t; the copies are waited
 // for before the closing barrier.
 __global__ __launch_bounds__(kAttnThreads, kWavesPerSimd) void attention_kernel(const PrefillParams p, const uint8_t* kws,
-                                                                     const uint8_t* vws) {
+                                                                     const uint8_t* vws, const AttnOrder ord) {
   __shared__ __attribute__((aligned(16))) uint8_t kt0[kTileBytes], kt1[kTileBytes];
   __shared__ __attribute__((aligned(16))) uint8_t vt0[kTileBytes], vt1[kTileBytes];
   __shared__ double inv_rev[kHeadDim / 2];   // query RoPE: theta^(-2i/128) / (2 pi)
+  __shared__ int last_span;                   // this workgroup merges its query block's spans
   LDS_AS uint8_t* const K0 = (LDS_AS uint8_t*)kt0;
   LDS_AS uint8_t* const K1 = (LDS_AS uint8_t*)kt1;
   LDS_AS uint8_t* const V0 = (LDS_AS uint8_t*)vt0;
@@ -378,9 +495,9 @@ __global__ __launch_bounds__(kAttnThreads, kWavesPerSimd) void attention_kernel(
   const int n32 = lane & 31, hf = lane >> 5;
   const int G = p.group;
 
-  // ---- workgroup -> (sequence, KV head group, query head, 128-query block)
+  // ---- workgroup -> (sequence, KV head group, query head, 128-query block, key span)
   const int nqb = p.n_qblocks;
-  const int per_group = nqb * G;
+  const int per_group = nqb * p.n_spans * G;
   const int groups = p.batch * p.num_kv_heads;
   const int bid = blockIdx.x;
   int grp, wi;
@@ -393,8 +510,17 @@ __global__ __launch_bounds__(kAttnThreads, kWavesPerSimd) void attention_kernel(
     wi = bid % per_group;
   }
   const int b = grp / p.num_kv_heads, h = grp % p.num_kv_heads;
-  const int qb = nqb - 1 - wi / G;   // heaviest block first
+  const int rank = wi / G;   // largest item first
   const int hq = h * G + wi % G;
+  int qb, span;
+  if (ord.n > 0) {
+    const int it = ord.item[rank];
+    qb = it / p.n_spans;
+    span = it % p.n_spans;
+  } else {
+    qb = nqb - 1 - rank / p.n_spans;
+    span = rank % p.n_spans;
+  }
 
   const SeqExtent ext = seq_extent(p, b);
   const int n = ext.n, T = ext.T;
@@ -402,7 +528,10 @@ __global__ __launch_bounds__(kAttnThreads, kWavesPerSimd) void attention_kernel(
   if (q0 >= T) return;
   const int qe = min(q0 + kBM, T);
   const int kend = p.causal ? ext.past + qe : n;
-  const int ntiles = (kend + kBN - 1) / kBN;
+  const int ntb = (kend + kBN - 1) / kBN;                            // tiles of the query block
+  const int ns = p.n_spans > 1 ? (ntb + p.span_tiles - 1) / p.span_tiles : 1;   // its spans
+  if (span >= ns) return;
+  const int ta = (int)((int64_t)span * ntb / ns), tb = (int)((int64_t)(span + 1) * ntb / ns);   // tiles [ta, tb)
   const bool rope = p.rope_theta > 0.0;
   const double pos0 = (double)p.positions[b];
 
@@ -416,7 +545,7 @@ __global__ __launch_bounds__(kAttnThreads, kWavesPerSimd) void attention_kernel(
   wc.scale_log2 = p.scale_log2;
   const bool wave_live = wc.wq0 < T;
   const int wkend = !wave_live ? 0 : (wc.causal ? min(n, ext.past + wc.wq0 + 32 * kRB) : n);
-  wc.wtiles = (wkend + kBN - 1) / kBN;
+  wc.wtiles = min((wkend + kBN - 1) / kBN, tb);   // end of this wave's tiles in the span
 
   const int64_t slab = ((int64_t)b * p.num_kv_heads + h) * ws_tiles(p.max_seq) * kTileBytes;
   const uint8_t* kslab = kws + slab;
@@ -424,9 +553,9 @@ __global__ __launch_bounds__(kAttnThreads, kWavesPerSimd) void attention_kernel(
   const uint32_t lane_off = 16u * lane;
 
   // ---- first tiles requested before the query prologue
-  dma_tile<kTileBytes / 1024>(k0a, kslab, lane_off, wave);
-  dma_tile<kTileBytes / 1024>(v0a, vslab, lane_off, wave);
-  if (ntiles > 1) dma_tile<kTileBytes / 1024>(k1a, kslab + kTileBytes, lane_off, wave);
+  dma_tile<kTileBytes / 1024>(k0a, kslab + ta * kTileBytes, lane_off, wave);
+  dma_tile<kTileBytes / 1024>(v0a, vslab + ta * kTileBytes, lane_off, wave);
+  if (tb - ta > 1) dma_tile<kTileBytes / 1024>(k1a, kslab + (ta + 1) * kTileBytes, lane_off, wave);
   if (tid < 64 && rope) inv_rev[tid] = rope_inv_freq(tid, p.rope_log2_theta) * 0.15915494309189535;
 
   // ---- query prologue: lane (n32, hf) owns rows wq0 + n32 and wq0 + 32 + n32
@@ -514,73 +643,158 @@ __global__ __launch_bounds__(kAttnThreads, kWavesPerSimd) void attention_kernel(
   }
 
   f32x16 sa[kRB], sb[kRB];
-  if (wc.wtiles > 0) {   // scores and row maxima of tile 0 (every row sees key 0, so m is finite)
+  if (wc.wtiles > ta) {   // scores and row maxima of tile ta (every row sees the span's first key: m is finite)
     qk_tile(sa, K0, qf, n32, hf);
-    if (wc.needs_mask(0)) {
+    if (wc.needs_mask(ta * kBN)) {
       int lim[kRB];
-      wc.limits(0, hf, lim);
+      wc.limits(ta * kBN, hf, lim);
       apply_mask(sa, lim);
     }
     row_max(sa, ws.m, wc.scale_log2);
   }
-  __syncthreads();   // every read of K'_0 done: its buffer takes K'_2
+  __syncthreads();   // every read of K'_ta done: its buffer takes K'_ta+2
 
   // two tiles per trip: buffers and score registers have fixed roles in each half
-  for (int t = 0; t < ntiles; t += 2) {
-    if (t + 2 < ntiles) dma_tile<kTileBytes / 1024>(k0a, kslab + (t + 2) * kTileBytes, lane_off, wave);
-    if (t + 1 < ntiles) dma_tile<kTileBytes / 1024>(v1a, vslab + (t + 1) * kTileBytes, lane_off, wave);
+  for (int t = ta; t < tb; t += 2) {
+    if (t + 2 < tb) dma_tile<kTileBytes / 1024>(k0a, kslab + (t + 2) * kTileBytes, lane_off, wave);
+    if (t + 1 < tb) dma_tile<kTileBytes / 1024>(v1a, vslab + (t + 1) * kTileBytes, lane_off, wave);
     if (t < wc.wtiles) wave_tile(t, sa, sb, K1, V0, qf, ws, wc, lane);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     const int t1 = t + 1;
-    if (t1 >= ntiles) break;
-    if (t1 + 2 < ntiles) dma_tile<kTileBytes / 1024>(k1a, kslab + (t1 + 2) * kTileBytes, lane_off, wave);
-    if (t1 + 1 < ntiles) dma_tile<kTileBytes / 1024>(v0a, vslab + (t1 + 1) * kTileBytes, lane_off, wave);
+    if (t1 >= tb) break;
+    if (t1 + 2 < tb) dma_tile<kTileBytes / 1024>(k1a, kslab + (t1 + 2) * kTileBytes, lane_off, wave);
+    if (t1 + 1 < tb) dma_tile<kTileBytes / 1024>(v0a, vslab + (t1 + 1) * kTileBytes, lane_off, wave);
     if (t1 < wc.wtiles) wave_tile(t1, sb, sa, K0, V1, qf, ws, wc, lane);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
   }
+  // ---- a split block: store this span's state, arrive; the last span merges
+  if (ns > 1) {
+    const int64_t blk = ((int64_t)b * p.num_q_heads + hq) * nqb + qb;
+    const float* part = p.partials + blk * p.n_spans * kPartFloats;
+    if (wave_live) store_partial(p.partials + (blk * p.n_spans + span) * kPartFloats, ws, wave, lane);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // this thread's partial stores have completed
+    __syncthreads();
+    if (tid == 0) {
+      const uint32_t prev = __hip_atomic_fetch_add(p.counters + blk, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      last_span = prev + 1 == (uint32_t)ns;
+    }
+    __syncthreads();
+    if (!last_span) return;
+    if (!wave_live) return;
+    // every span's state (this one's too) from memory: the tile loop's registers are dead here
+    WaveState mg;
+    load_partial(mg, part, wave, lane);
+    for (int k = 1; k < ns; ++k) merge_partial(mg, part + k * kPartFloats, wave, lane);
+    write_rows(p, mg, wc, b, hq, T, hf);
+    return;
+  }
   // ---- epilogue: O / l for this lane's query rows
   if (!wave_live) return;
-#pragma unroll
-  for (int rb = 0; rb < kRB; ++rb) {
-    const float l = sum_xor32(ws.l[rb]);
-    if (wc.qrow[rb] >= T) continue;
-    const float inv = 1.0f / l;
-    uint8_t* orow = (uint8_t*)p.out +
-                    ((int64_t)b * p.o_sb + (int64_t)hq * p.o_sh + (int64_t)wc.qrow[rb] * p.o_ss) * (p.out_bf16 ? 2 : 4);
-#pragma unroll
-    for (int T = 0; T < 4; ++T) {
-#pragma unroll
-      for (int a = 0; a < 4; ++a) {
-        const int d0 = 32 * T + 8 * a + 4 * hf;
-        const float v0 = ws.o[rb][T][4 * a] * inv, v1 = ws.o[rb][T][4 * a + 1] * inv;
-        const float v2 = ws.o[rb][T][4 * a + 2] * inv, v3 = ws.o[rb][T][4 * a + 3] * inv;
-        if (p.out_bf16) *(u32x2*)(orow + 2 * d0) = u32x2{pack_bf16x2(v0, v1), pack_bf16x2(v2, v3)};
-        else *(f32x4*)(orow + 4 * d0) = f32x4{v0, v1, v2, v3};
-      }
+  write_rows(p, ws, wc, b, hq, T, hf);
+}
+
+// Split plan of the attention grid (host).  The work of a query block is
+// estimated from the extent of the largest sequence the descriptor admits:
+// T = max_chunk new tokens after max_seq - max_chunk cached ones.  Key spans
+// are used only when the grid has fewer than 384 workgroups (1.5 per compute
+// unit), where it cannot fill the GPU: a chunk after a long cached prefix,
+// or one sequence with few heads.  Spans are then sized for about 640 items
+// (2.5 workgroups per compute unit), at least 32 tiles and at most 16 per
+// block.  Measured on Qwen3-14B shapes: a 1024-token chunk after 3072
+// cached tokens takes 134 us unsplit, 119 us in 2 spans, 134 us in 3; a
+// 96-token chunk after 4000, 104 us unsplit, 66 in 2 spans, 45 in 4; the
+// 4096-token prefill (1280 workgroups) is not split, splitting its longest
+// blocks made it 8 % slower.
+struct SplitPlan {
+  int n_qblocks, n_spans, span_tiles;
+};
+
+int est_block_tiles(int max_seq, int max_chunk, bool causal, int qb) {
+  const int64_t past = (int64_t)max_seq - max_chunk;
+  const int64_t qe = std::min<int64_t>((int64_t)(qb + 1) * kBM, max_chunk);
+  const int64_t kend = causal ? past + qe : past + max_chunk;
+  return (int)((kend + kBN - 1) / kBN);
+}
+
+SplitPlan split_plan(int batch, int num_q_heads, int max_seq, int max_chunk, bool causal) {
+  SplitPlan sp{(max_chunk + kBM - 1) / kBM, 1, 0};
+  const int tiles = (int)ws_tiles(max_seq);
+  int longest = 0;
+  for (int qb = 0; qb < sp.n_qblocks; ++qb) longest = std::max(longest, est_block_tiles(max_seq, max_chunk, causal, qb));
+  const int64_t items = (int64_t)batch * num_q_heads * sp.n_qblocks;
+  sp.span_tiles = (int)std::max<int64_t>({32, ((int64_t)longest * items + 639) / 640, (tiles + 15) / 16});
+  if (items < 384 && longest > sp.span_tiles) sp.n_spans = (tiles + sp.span_tiles - 1) / sp.span_tiles;
+  return sp;
+}
+
+// Items (query block, span) of one head sorted by estimated tiles, largest
+// first (ties: later block first); n = 0 when they do not fit the table.
+void fill_order(const SplitPlan& sp, int max_seq, int max_chunk, bool causal, AttnOrder& ord) {
+  const int items = sp.n_qblocks * sp.n_spans;
+  ord.n = 0;
+  if (sp.n_spans == 1 || items > kMaxOrder) return;
+  std::vector<std::pair<int, int>> key(items);   // (-estimated tiles, -item)
+  for (int qb = 0; qb < sp.n_qblocks; ++qb) {
+    const int t = est_block_tiles(max_seq, max_chunk, causal, qb);
+    const int ns = (t + sp.span_tiles - 1) / sp.span_tiles;
+    for (int sidx = 0; sidx < sp.n_spans; ++sidx) {
+      const int size = sidx < ns ? (int)((int64_t)(sidx + 1) * t / ns - (int64_t)sidx * t / ns) : 0;
+      key[qb * sp.n_spans + sidx] = {-size, -(qb * sp.n_spans + sidx)};
     }
   }
+  std::sort(key.begin(), key.end());
+  for (int r = 0; r < items; ++r) ord.item[r] = (uint16_t)(-key[r].second);
+  ord.n = items;
+}
+
+// Workspace: [K' tiles][V tiles], then, for a split plan, [counters: B * Hq *
+// n_qblocks u32, to 256 bytes][partials: B * Hq * n_qblocks * n_spans *
+// kPartFloats f32].
+size_t kv_bytes(int batch, int num_kv_heads, int max_seq) {
+  return (size_t)batch * num_kv_heads * ws_tiles(max_seq) * kTileBytes * 2;
+}
+
+size_t split_bytes(int batch, int num_q_heads, const SplitPlan& sp) {
+  if (sp.n_spans == 1) return 0;
+  const size_t blocks = (size_t)batch * num_q_heads * sp.n_qblocks;
+  return (blocks * 4 + 255) / 256 * 256 + blocks * sp.n_spans * kPartFloats * sizeof(float);
 }
 
 }  // namespace
 
-size_t prefill_workspace_bytes(int batch, int num_kv_heads, int max_seq) {
-  return (size_t)batch * num_kv_heads * ws_tiles(max_seq) * kTileBytes * 2;
+size_t prefill_workspace_bytes(int batch, int num_q_heads, int num_kv_heads, int max_seq, int max_chunk, bool causal) {
+  const size_t plain = split_bytes(batch, num_q_heads, split_plan(batch, num_q_heads, max_seq, max_seq, causal));
+  const size_t chunk = split_bytes(batch, num_q_heads, split_plan(batch, num_q_heads, max_seq, max_chunk, causal));
+  return kv_bytes(batch, num_kv_heads, max_seq) + std::max(plain, chunk);
 }
 
 hipError_t launch_prefill_phased(const PrefillParams& p, void* workspace, hipStream_t stream) {
   uint8_t* kws = (uint8_t*)workspace;
   uint8_t* vws = kws + (size_t)p.batch * p.num_kv_heads * ws_tiles(p.max_seq) * kTileBytes;
-  hipLaunchKernelGGL(key_prologue_kernel, dim3((unsigned)(ws_tiles(p.max_seq) * kBN / 16), p.num_kv_heads, p.batch), dim3(256),
-                     0, stream, p, kws, vws);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  const SplitPlan sp = split_plan(p.batch, p.num_q_heads, p.max_seq, p.max_chunk, p.causal != 0);
   PrefillParams q = p;
-  q.n_qblocks = (p.max_chunk + kBM - 1) / kBM;
-  hipLaunchKernelGGL(attention_kernel, dim3(q.n_qblocks * p.num_q_heads * p.batch), dim3(kAttnThreads), 0, stream, q,
-                     (const uint8_t*)kws, (const uint8_t*)vws);
-  return hipGetLastError();
+  q.n_qblocks = sp.n_qblocks;
+  q.n_spans = sp.n_spans;
+  q.span_tiles = sp.span_tiles;
+  q.counters = nullptr;
+  q.n_counters = 0;
+  q.partials = nullptr;
+  if (sp.n_spans > 1) {
+    uint8_t* extra = kws + kv_bytes(p.batch, p.num_kv_heads, p.max_seq);
+    const size_t blocks = (size_t)p.batch * p.num_q_heads * sp.n_qblocks;
+    q.counters = (uint32_t*)extra;
+    q.n_counters = (int32_t)blocks;
+    q.partials = (float*)(extra + (blocks * 4 + 255) / 256 * 256);
+  }
+  AttnOrder ord;
+  fill_order(sp, p.max_seq, p.max_chunk, p.causal != 0, ord);
+  const hipError_t e = launch_kernel(key_prologue_kernel, dim3((unsigned)(ws_tiles(p.max_seq) * kBN / 16), p.num_kv_heads, p.batch),
+                                     dim3(256), stream, q, kws, vws);
+  if (e != hipSuccess) return e;
+  return launch_kernel(attention_kernel, dim3(q.n_qblocks * q.n_spans * p.num_q_heads * p.batch), dim3(kAttnThreads),
+                       stream, q, (const uint8_t*)kws, (const uint8_t*)vws, ord);
 }
 
 }  // namespace gqa

@@ -70,7 +70,7 @@ typedef enum gqa_status {
                               decode cache slab of one (b, head) >= 4 GiB        */
   GQA_ERR_ALIGN = 4,       /* base pointer or stride not 16-byte aligned          */
   GQA_ERR_WORKSPACE = 5,   /* workspace NULL or smaller than required             */
-  GQA_ERR_HIP = 6          /* a kernel launch failed (hipGetLastError)            */
+  GQA_ERR_HIP = 6          /* a kernel launch failed (its hipLaunchKernel status) */
 } gqa_status;
 
 typedef enum gqa_dtype {
@@ -238,10 +238,16 @@ gqa_status gqa_attn_decode_paged(const gqa_decode_desc* desc, const void* q, con
                                  hipStream_t stream);
 
 /*
- * Bytes of the optional prefill workspace (host only, no HIP call):
- * B * Hkv * ceil(max_seq / 32) * 9216 * 2: per 32-key tile, the K' rows
- * (norm + RoPE applied) and the V rows, both in fp16, in the padded row
- * layout the attention tiles have in on-chip memory.
+ * Bytes of the optional prefill workspace (host only, no HIP call), for
+ * gqa_attn_prefill and the chunked forms alike:
+ * B * Hkv * ceil(max_seq / 32) * 9216 * 2 for the key tiles (per 32-key
+ * tile, the K' rows (norm + RoPE applied) and the V rows, both in fp16, in
+ * the padded row layout the attention tiles have in on-chip memory), plus,
+ * when the attention grid would have fewer than 384 workgroups (B * Hq *
+ * ceil(T_max / 128)), room to split long key ranges over several
+ * workgroups: one counter per (b, q head, 128-query block) and one partial
+ * (m, l, O) of 66 KiB per (b, q head, 128-query block, key span), with at
+ * most 16 spans of at least 32 key tiles each.
  */
 gqa_status gqa_attn_prefill_workspace_size(const gqa_prefill_desc* desc, size_t* bytes);
 
