@@ -279,7 +279,9 @@ gqa_status gqa_attn_prefill_workspace_size(const gqa_prefill_desc* desc, size_t*
  * every key row's prologue is computed once into the workspace, then the
  * attention kernel applies the query prologue as it loads query tiles.  With
  * workspace == NULL a single kernel recomputes the key prologue for every
- * (query block, key tile) pair (no workspace, more arithmetic).
+ * (query block, key tile) pair (no workspace, more arithmetic).  Calls that
+ * share a workspace must not run concurrently (the key tiles, and the split
+ * counters the call resets, are per call).
  * Errors: as gqa_attn_decode.
  */
 gqa_status gqa_attn_prefill(const gqa_prefill_desc* desc, const void* q, const void* k, const void* v,
