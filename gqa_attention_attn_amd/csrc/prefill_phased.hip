@@ -308,13 +308,14 @@ struct WaveState {
 
 // ---- split key ranges ("ADR-0060: AHBM GQA Fused Attention Kernel
 // (Llama3-70B)" section 4: partials (m, l, O) of disjoint key ranges combine
-// by the log-sum-exp merge).  A query block whose visible keys span more
-// than span_tiles tiles is cut into ns = ceil(tiles / span_tiles) nearly
-// equal key spans, one workgroup each, so that no workgroup carries the whole
-// causal row of the last blocks.  Each span writes its unnormalised state in
-// the lanes' own register layout, then arrives at the block's counter; the
-// last to arrive merges the other spans' states into its registers and
-// writes out.  Partial stores and loads are device-coherent (they bypass the
+// by the log-sum-exp merge).  When the grid is short (few query blocks), a
+// query block whose visible keys span more than span_tiles tiles is cut
+// into ns = ceil(tiles / span_tiles) nearly equal key spans, one workgroup
+// each, so that more of the GPU works on it.  Each span writes its
+// unnormalised state in the lanes' own register layout, then arrives at the
+// block's counter; the last to arrive reads every span's state back (its own
+// too: the tile loop's registers are dead by then), merges and writes out.
+// Partial stores and loads are device-coherent (they bypass the
 // non-coherent per-XCD L2s); a workgroup's stores have completed before its
 // arrival.  No workgroup waits for another.
 static_assert(kRB == 1, "partial layout: one 32-row block per wave");
