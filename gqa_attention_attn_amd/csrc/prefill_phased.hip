@@ -199,16 +199,19 @@ __device__ __forceinline__ void dma_tile(uint32_t lds, const uint8_t* src, uint3
 // pair (i, i+64) stays in one lane; the K' operand of slot kk is read from the
 // same dims of the lane's key row.
 
-// S^T for the 32 keys of a K' tile and the wave's two 32-row blocks:
-// s[rb][i] = S[key 8(i/4) + 4hf + i%4][query 32rb + n32] (raw dot products).
-// Each K' fragment read from LDS feeds both blocks.
+// S^T for the 32 keys of a K' tile and the wave's 32-row blocks:
+// s[rb][i] = init[rb] + S[key 8(i/4) + 4hf + i%4][query 32rb + n32].  The
+// query fragments carry the softmax scale times log2(e), so S is already in
+// log2 units, and init = -m (the row's running maximum) leaves exp2(s) to the
+// softmax: the subtraction rides in the accumulator's initial value.  Each K'
+// fragment read from LDS feeds every block.
 __device__ __forceinline__ void qk_tile(f32x16 (&s)[kRB], const LDS_AS uint8_t* kt, const f16x8 (&qf)[kRB][8], int n32,
-                                        int hf) {
+                                        int hf, const float (&init)[kRB]) {
   const LDS_AS uint8_t* base = kt + kKPitch * n32 + 64 * hf;
 #pragma unroll
   for (int rb = 0; rb < kRB; ++rb)
 #pragma unroll
-    for (int i = 0; i < 16; ++i) s[rb][i] = 0.f;
+    for (int i = 0; i < 16; ++i) s[rb][i] = init[rb];
 #pragma unroll
   for (int kk = 0; kk < 8; ++kk) {
     const u32x4 a = *(const LDS_AS u32x4*)(base + 16 * ((kk & 3) + 8 * (kk >> 2)));
@@ -234,7 +237,7 @@ __device__ __forceinline__ float row_max16(const f32x16& s) {
 
 // Online softmax in log2 units with a lazy rescale.  Keys at tile offsets at
 // or past lim[rb] (per lane half) are invisible; row_max is the row maximum
-// of each block times scale * log2(e).
+// of each block (relative to m once the scores carry -m).
 __device__ __forceinline__ void apply_mask(f32x16 (&s)[kRB], const int (&lim)[kRB]) {
 #pragma unroll
   for (int rb = 0; rb < kRB; ++rb)
@@ -242,22 +245,21 @@ __device__ __forceinline__ void apply_mask(f32x16 (&s)[kRB], const int (&lim)[kR
     for (int i = 0; i < 16; ++i) s[rb][i] = (8 * (i >> 2) + (i & 3) < lim[rb]) ? s[rb][i] : -INFINITY;
 }
 
-__device__ __forceinline__ void row_max(const f32x16 (&s)[kRB], float (&mx)[kRB], float scale_log2) {
+__device__ __forceinline__ void row_max(const f32x16 (&s)[kRB], float (&mx)[kRB]) {
 #pragma unroll
-  for (int rb = 0; rb < kRB; ++rb) mx[rb] = max_xor32(row_max16(s[rb])) * scale_log2;
+  for (int rb = 0; rb < kRB; ++rb) mx[rb] = max_xor32(row_max16(s[rb]));
 }
 
-// P = exp2(S scale log2(e) - m) as fp16 MFMA operands pf[rb][e] (keys 16e +
+// P = exp2(s) = exp2(S scale log2(e) - m) as fp16 MFMA operands pf[rb][e] (keys 16e +
 // {4hf+t, 8+4hf+t}, t < 4).  The row sum l is taken over the fp16-rounded P
 // that the P V products use (v_dot2 of each packed pair with (1, 1)), so
 // numerator and denominator see the same weights.
-__device__ __forceinline__ void softmax_exp(f32x16 (&s)[kRB], const float (&m)[kRB], float (&l)[kRB], u32x4 (&pf)[kRB][2],
-                                            float scale_log2) {
+__device__ __forceinline__ void softmax_exp(f32x16 (&s)[kRB], float (&l)[kRB], u32x4 (&pf)[kRB][2]) {
   const f16x2 one = {(_Float16)1.0f, (_Float16)1.0f};
 #pragma unroll
   for (int rb = 0; rb < kRB; ++rb) {
 #pragma unroll
-    for (int i = 0; i < 16; ++i) s[rb][i] = fast_exp2(fmaf(s[rb][i], scale_log2, -m[rb]));
+    for (int i = 0; i < 16; ++i) s[rb][i] = fast_exp2(s[rb][i]);
 #pragma unroll
     for (int e = 0; e < 2; ++e)
       pf[rb][e] = u32x4{pack_f16x2(s[rb][8 * e + 0], s[rb][8 * e + 1]), pack_f16x2(s[rb][8 * e + 2], s[rb][8 * e + 3]),
@@ -398,7 +400,6 @@ struct WaveCtx {
   int n;            // keys: P + T
   int wtiles;       // tiles holding keys this wave sees
   bool causal;
-  float scale_log2;
   // tile offsets at or past lim are invisible to this lane (per block)
   __device__ __forceinline__ void limits(int ks, int hf, int (&lim)[kRB]) const {
 #pragma unroll
@@ -414,16 +415,21 @@ struct WaveCtx {
 // tile t (V_t in vt) beside the row maxima of tile t+1.  On the wave's last
 // tile the scores and maxima are computed from whatever kt_next holds and
 // discarded, which keeps the loop body one basic block apart from the masking
-// of the diagonal tiles and the (rare) rescale.  m grows to the new maxima
-// when any of them exceeds m by more than 2^8 (wave-uniform decision); O and
-// l follow, after the P V products that used the old m.
+// of the diagonal tiles and the (rare) rescale.  The scores of tile t+1 are
+// formed relative to the m of tile t; m grows to the new maxima when any of
+// them exceeds m by more than 2^8 (wave-uniform decision); O and l follow,
+// after the P V products that used the old m, and the fresh scores drop the
+// increase.
 __device__ __forceinline__ void wave_tile(int t, f32x16 (&s_cur)[kRB], f32x16 (&s_next)[kRB],
                                           const LDS_AS uint8_t* kt_next, const LDS_AS uint8_t* vt,
                                           const f16x8 (&qf)[kRB][8], WaveState& ws, const WaveCtx& w, int lane) {
   const int n32 = lane & 31, hf = lane >> 5;
   u32x4 pf[kRB][2];
-  qk_tile(s_next, kt_next, qf, n32, hf);
-  softmax_exp(s_cur, ws.m, ws.l, pf, w.scale_log2);
+  float neg_m[kRB];
+#pragma unroll
+  for (int rb = 0; rb < kRB; ++rb) neg_m[rb] = -ws.m[rb];
+  qk_tile(s_next, kt_next, qf, n32, hf, neg_m);
+  softmax_exp(s_cur, ws.l, pf);
   pv_tile(ws.o, vt, pf, lane);
   const int ks = (t + 1) * kBN;
   if (w.needs_mask(ks)) {
@@ -431,20 +437,22 @@ __device__ __forceinline__ void wave_tile(int t, f32x16 (&s_cur)[kRB], f32x16 (&
     w.limits(ks, hf, lim);
     apply_mask(s_next, lim);
   }
-  float mx[kRB];
-  row_max(s_next, mx, w.scale_log2);
+  float mx[kRB];   // row maxima of tile t+1 less m
+  row_max(s_next, mx);
   bool grow = false;
 #pragma unroll
-  for (int rb = 0; rb < kRB; ++rb) grow = grow || mx[rb] > ws.m[rb] + kLazyRescale;
+  for (int rb = 0; rb < kRB; ++rb) grow = grow || mx[rb] > kLazyRescale;
   if (t + 1 < w.wtiles && __any(grow)) {
 #pragma unroll
     for (int rb = 0; rb < kRB; ++rb) {
-      const float m_new = __builtin_elementwise_maximum(ws.m[rb], mx[rb]);
-      const float corr = fast_exp2(ws.m[rb] - m_new);
+      const float inc = __builtin_elementwise_maximum(mx[rb], 0.0f);
+      const float corr = fast_exp2(-inc);
       ws.l[rb] *= corr;
 #pragma unroll
       for (int T = 0; T < 4; ++T) ws.o[rb][T] *= corr;
-      ws.m[rb] = m_new;
+      ws.m[rb] += inc;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) s_next[rb][i] -= inc;
     }
   }
 }
@@ -543,7 +551,6 @@ __global__ __launch_bounds__(kAttnThreads, kWavesPerSimd) void attention_kernel(
   wc.past = ext.past;
   wc.n = n;
   wc.causal = p.causal != 0;
-  wc.scale_log2 = p.scale_log2;
   const bool wave_live = wc.wq0 < T;
   const int wkend = !wave_live ? 0 : (wc.causal ? min(n, ext.past + wc.wq0 + 32 * kRB) : n);
   wc.wtiles = min((wkend + kBN - 1) / kBN, tb);   // end of this wave's tiles in the span
@@ -597,6 +604,7 @@ __global__ __launch_bounds__(kAttnThreads, kWavesPerSimd) void attention_kernel(
         ss = sum_xor32(ss);
         r = rsqrtf(ss * (1.0f / kHeadDim) + p.eps);
       }
+      r *= p.scale_log2;   // q' carries the softmax scale times log2(e) (RoPE is linear)
       const double qpos = pos0 + (double)(ext.past + wc.qrow[rb]);
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
@@ -613,6 +621,12 @@ __global__ __launch_bounds__(kAttnThreads, kWavesPerSimd) void attention_kernel(
           for (int e = 0; e < 8; ++e) {
             xl[e] *= r * bf16_elem(glo, e);
             xh[e] *= r * bf16_elem(ghi, e);
+          }
+        } else {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            xl[e] *= r;
+            xh[e] *= r;
           }
         }
         if (rope) {
@@ -645,13 +659,18 @@ __global__ __launch_bounds__(kAttnThreads, kWavesPerSimd) void attention_kernel(
 
   f32x16 sa[kRB], sb[kRB];
   if (wc.wtiles > ta) {   // scores and row maxima of tile ta (every row sees the span's first key: m is finite)
-    qk_tile(sa, K0, qf, n32, hf);
+    const float zero[kRB] = {};
+    qk_tile(sa, K0, qf, n32, hf, zero);
     if (wc.needs_mask(ta * kBN)) {
       int lim[kRB];
       wc.limits(ta * kBN, hf, lim);
       apply_mask(sa, lim);
     }
-    row_max(sa, ws.m, wc.scale_log2);
+    row_max(sa, ws.m);
+#pragma unroll
+    for (int rb = 0; rb < kRB; ++rb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) sa[rb][i] -= ws.m[rb];
   }
   __syncthreads();   // every read of K'_ta done: its buffer takes K'_ta+2
 
