@@ -8,7 +8,9 @@ decode call (partition + merge).  `value` is the achieved HBM bandwidth in
 algorithmic bytes (valid K/V rows + q + out) per second.  Inputs are resident
 in HBM; K/V rotate over enough distinct buffer sets (>= 1 GiB) that the
 256 MB Infinity Cache cannot serve them.  The K timed steps are replayed
-from a HIP graph.
+from a HIP graph: a graph of the W warmup steps is replayed for at least
+50 ms of GPU time first (the shader clock settles), then the median of five
+timed replays of the K steps is taken.
 
 Also reported in the same line: per-launch kernel durations (HIP events on the
 launch stream) and the roofline of the dominant kernel, the oracle timed on
@@ -21,6 +23,7 @@ Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-extra] [--no-cp
 import argparse
 import json
 import math
+import statistics
 import os
 import sys
 import time
@@ -135,9 +138,12 @@ def measured_traffic(kernel):
     return rec.get("traffic_bytes_per_launch")
 
 
-def graph_time_ms(torch, fn, steps, warmup):
-    """Capture `steps` calls of fn(i, stream) in a HIP graph, replay it after a
-    warmup graph, and return the elapsed GPU time of the timed replay (ms)."""
+def graph_time_ms(torch, fn, steps, warmup, trials=5, settle_ms=50.0):
+    """Capture `steps` calls of fn(i, stream) in a HIP graph and return the GPU
+    time of one replay (ms): the median of `trials` timed replays, taken after a
+    warmup graph of `warmup` calls has been replayed for at least `settle_ms`
+    of GPU time (the shader clock ramps up over the first tens of ms of
+    sustained work; timing before it settles measures the ramp)."""
     s = torch.cuda.Stream()
     torch.cuda.synchronize()
     with torch.cuda.stream(s):
@@ -152,15 +158,26 @@ def graph_time_ms(torch, fn, steps, warmup):
         for i in range(steps):
             fn(i, s.cuda_stream)
     torch.cuda.synchronize()
-    gw.replay()
-    torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    with torch.cuda.stream(s):
-        e0.record(s)
-        gt.replay()
-        e1.record(s)
-    torch.cuda.synchronize()
-    return e0.elapsed_time(e1)
+    settled = 0.0
+    while True:
+        with torch.cuda.stream(s):
+            e0.record(s)
+            gw.replay()
+            e1.record(s)
+        torch.cuda.synchronize()
+        settled += e0.elapsed_time(e1)
+        if settled >= settle_ms:
+            break
+    times = []
+    for _ in range(max(trials, 1)):
+        with torch.cuda.stream(s):
+            e0.record(s)
+            gt.replay()
+            e1.record(s)
+        torch.cuda.synchronize()
+        times.append(e0.elapsed_time(e1))
+    return statistics.median(times)
 
 
 def launch_time_us(torch, fn, steps, warmup):
