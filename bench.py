@@ -21,6 +21,7 @@ Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-extra] [--no-cp
 """
 
 import argparse
+import dataclasses
 import json
 import math
 import statistics
@@ -333,6 +334,8 @@ def profile_calls(args, torch, G, synth, np):
         _, _, _, call = prefill_case(torch, G, synth, np, two_phase=args.only == "prefill")
     else:
         w = {"decode": synth.QWEN3_DECODE, "long": synth.LLAMA70B_LONG, "ragged": synth.QWEN3_RAGGED}[args.only or "decode"]
+        if args.group:   # the same shape with G query heads per KV head (K/V bytes do not depend on G)
+            w = dataclasses.replace(w, name=f"{w.name}_g{args.group}", num_q_heads=w.num_kv_heads * args.group)
         call = DecodeCase(w, 1, torch, G, synth, exact_first=(w is synth.QWEN3_DECODE)).call
     if args.copy_probe_mib:
         src = torch.ones(args.copy_probe_mib << 18, dtype=torch.float32, device="cuda")
@@ -358,6 +361,8 @@ def main():
                     help="with --eager-calls: the workload to run")
     ap.add_argument("--eager-calls", type=int, default=0,
                     help="profiling mode: run this many plain calls of --only's workload (no timing, no JSON)")
+    ap.add_argument("--group", type=int, default=0,
+                    help="profiling mode, decode workloads: G query heads per KV head instead of the workload's")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="profiling mode: first copy a device buffer of this many MiB (counter calibration)")
     args = ap.parse_args()
@@ -489,6 +494,18 @@ def main():
                 f"(partition {tp:.1f} us, merge {tm:.1f} us)")
             del c
             torch.cuda.empty_cache()
+
+        # what a plain device copy reaches on this machine (torch copy_ of 1 GiB: 1 GiB read + 1 GiB written)
+        src = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        t = graph_time_ms(torch, lambda i, stream: dst.copy_(src), 10, 2)
+        probe = 2.0 * src.numel() * 4 * 10 / (t * 1e-3) / 1e9
+        extra["hbm_copy_probe"] = {"kernel": "torch copy_ of 1 GiB (read + write)", "gbs": round(probe, 1),
+                                   "frac_of_hbm_peak": round(probe / HBM_PEAK_GBS, 4),
+                                   "decode_partition_frac_of_probe": round(ach / probe, 4)}
+        log(f"[bench] copy probe {probe:.0f} GB/s")
+        del src, dst
+        torch.cuda.empty_cache()
         result["extra"] = extra
 
     if not args.no_cpu_baseline:
