@@ -33,14 +33,39 @@ def ints(x, device="cuda"):
     return torch.from_numpy(np.ascontiguousarray(np.asarray(x, dtype=np.int32))).to(device)
 
 
+# The pages' own device-vs-golden diagnostics ("Qwen3-14B Optimization",
+# validation of the fused attention stage): cosine similarity as a sanity
+# check and the fraction of elements within 3e-3.  Reported beside the bound
+# that decides the test; the cosine must exceed 0.999.
+PASS_RATE_ATOL = 3e-3
+MIN_COSINE = 0.999
+
+
+def diagnostics(got, ref):
+    """(max relative error, cosine similarity, pass rate at PASS_RATE_ATOL)."""
+    g = got.ravel()
+    r = ref.ravel()
+    if g.size == 0:
+        return 0.0, 1.0, 1.0
+    rel = float(np.max(np.abs(g - r) / np.maximum(np.abs(r), 1e-6)))
+    ng, nr = float(np.linalg.norm(g)), float(np.linalg.norm(r))
+    cos = float(np.dot(g, r) / (ng * nr)) if ng > 0 and nr > 0 else (1.0 if ng == nr else 0.0)
+    rate = float(np.mean(np.abs(g - r) <= PASS_RATE_ATOL))
+    return rel, cos, rate
+
+
 def compare(got, ref, atol, what=""):
-    """Element-wise |got - ref| <= atol; returns the max error (logged)."""
+    """Element-wise |got - ref| <= atol and cosine > 0.999; returns the max
+    error (logged with the max relative error, cosine and pass rate)."""
     got = np.asarray(got, dtype=np.float64)
     ref = np.asarray(ref, dtype=np.float64)
     assert got.shape == ref.shape, (got.shape, ref.shape)
     assert np.all(np.isfinite(got)), f"{what}: non-finite output"
     err = np.abs(got - ref)
     mx = float(err.max()) if err.size else 0.0
-    log(f"  {what}: max|err| = {mx:.3e} (atol {atol:g}, n = {err.size})")
+    rel, cos, rate = diagnostics(got, ref)
+    log(f"  {what}: max|err| = {mx:.3e} (atol {atol:g}, n = {err.size}); max rel {rel:.2e}, "
+        f"cosine {cos:.8f}, within {PASS_RATE_ATOL:g}: {100 * rate:.3f} %")
     assert mx <= atol, f"{what}: max abs error {mx} > {atol}"
+    assert cos > MIN_COSINE, f"{what}: cosine {cos} <= {MIN_COSINE}"
     return mx
