@@ -163,12 +163,24 @@ def partial_state(q, K, V, scale: float):
 
 
 def merge(a, b):
-    """ADR-0060 §4 log-sum-exp merge of two flash states (m, l, O)."""
-    m_a, l_a, O_a = a
-    m_b, l_b, O_b = b
-    m = np.maximum(m_a, m_b)
-    sa, sb = np.exp(m_a - m), np.exp(m_b - m)
-    return m, l_a * sa + l_b * sb, O_a * sa[..., None] + O_b * sb[..., None]
+    """Union of two flash states over disjoint key sets (ADR-0060 §4 reduction).
+
+    A state (m, l, O) stands for keys whose softmax mass is Z = l * e^m and
+    whose normalised output is O / l.  The union has log-mass
+    lse = log(e^lse_a + e^lse_b) with lse_i = m_i + log l_i, and its output is
+    each side's normalised output weighted by that side's share of the mass,
+    e^(lse_i - lse).  The result is returned in the same (m, l, O) form with
+    m = lse and l = 1, so merges chain and ``finalize`` applies unchanged.
+    """
+    m_a, l_a, O_a = (_f64(x) for x in a)
+    m_b, l_b, O_b = (_f64(x) for x in b)
+    lse_a = m_a + np.log(l_a)
+    lse_b = m_b + np.log(l_b)
+    lse = np.logaddexp(lse_a, lse_b)
+    share_a = np.exp(lse_a - lse)
+    share_b = np.exp(lse_b - lse)
+    out = (share_a / l_a)[..., None] * O_a + (share_b / l_b)[..., None] * O_b
+    return lse, np.ones_like(lse), out
 
 
 def finalize(state):
