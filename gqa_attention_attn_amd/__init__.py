@@ -28,7 +28,7 @@ GQA_F32 = 0
 GQA_BF16 = 1
 GQA_ATTN_HEAD_DIM = 128
 GQA_ATTN_MAX_GROUP = 16
-GQA_ATTN_VERSION = 2
+GQA_ATTN_VERSION = 3
 
 EXPORTS = (
     "gqa_attn_status_string",
@@ -41,6 +41,8 @@ EXPORTS = (
     "gqa_attn_decode_paged",
     "gqa_attn_prefill_workspace_size",
     "gqa_attn_prefill",
+    "gqa_attn_prefill_keys",
+    "gqa_attn_prefill_attend",
     "gqa_attn_prefill_chunk",
     "gqa_attn_prefill_chunk_paged",
 )
@@ -76,7 +78,7 @@ class GqaPrefillDesc(ctypes.Structure):
         ("v_stride_b", ctypes.c_int64), ("v_stride_h", ctypes.c_int64), ("v_stride_s", ctypes.c_int64),
         ("out_stride_b", ctypes.c_int64), ("out_stride_h", ctypes.c_int64), ("out_stride_s", ctypes.c_int64),
         ("eps", ctypes.c_float), ("scale", ctypes.c_float), ("max_chunk", ctypes.c_int32),
-        ("block_size", ctypes.c_int32),
+        ("block_size", ctypes.c_int32), ("write_k_cache", ctypes.c_int32),
     ]
 
 
@@ -121,6 +123,9 @@ def lib() -> ctypes.CDLL:
         L.gqa_attn_prefill.argtypes = [ctypes.POINTER(GqaPrefillDesc), vp, vp, vp, vp, vp, vp, vp, ctypes.c_float,
                                        vp, vp, ctypes.c_size_t, vp]
         L.gqa_attn_prefill.restype = ctypes.c_int
+        for name in ("gqa_attn_prefill_keys", "gqa_attn_prefill_attend"):
+            getattr(L, name).argtypes = L.gqa_attn_prefill.argtypes
+            getattr(L, name).restype = ctypes.c_int
         L.gqa_attn_prefill_chunk.argtypes = [ctypes.POINTER(GqaPrefillDesc), vp, vp, vp, vp, vp, vp, vp, vp,
                                              ctypes.c_float, vp, vp, ctypes.c_size_t, vp]
         L.gqa_attn_prefill_chunk.restype = ctypes.c_int
@@ -196,6 +201,20 @@ def gqa_attn_prefill(desc, q, k, v, seq_lens, positions, q_norm_w, k_norm_w, rop
                                       stream))
 
 
+def gqa_attn_prefill_keys(desc, q, k, v, seq_lens, positions, q_norm_w, k_norm_w, rope_theta, out, workspace,
+                          workspace_bytes, stream) -> int:
+    return int(lib().gqa_attn_prefill_keys(ctypes.byref(desc) if desc is not None else None, q, k, v, seq_lens,
+                                           positions, q_norm_w, k_norm_w, float(rope_theta), out, workspace,
+                                           int(workspace_bytes), stream))
+
+
+def gqa_attn_prefill_attend(desc, q, k, v, seq_lens, positions, q_norm_w, k_norm_w, rope_theta, out, workspace,
+                            workspace_bytes, stream) -> int:
+    return int(lib().gqa_attn_prefill_attend(ctypes.byref(desc) if desc is not None else None, q, k, v, seq_lens,
+                                             positions, q_norm_w, k_norm_w, float(rope_theta), out, workspace,
+                                             int(workspace_bytes), stream))
+
+
 def gqa_attn_prefill_chunk(desc, q, k_cache, v_cache, past_lens, chunk_lens, positions, q_norm_w, k_norm_w,
                            rope_theta, out, workspace, workspace_bytes, stream) -> int:
     return int(lib().gqa_attn_prefill_chunk(ctypes.byref(desc) if desc is not None else None, q, k_cache, v_cache,
@@ -241,7 +260,8 @@ def decode_desc(q, k_cache, v_cache, out, kv_split_tokens: int = 0, eps: float =
         write_new_k=1 if write_new_k else 0)
 
 
-def prefill_desc(q, k, v, out, causal: bool = True, eps: float = 1e-6, scale: float = 0.0) -> GqaPrefillDesc:
+def prefill_desc(q, k, v, out, causal: bool = True, eps: float = 1e-6, scale: float = 0.0,
+                 write_k_cache: bool = False) -> GqaPrefillDesc:
     """Descriptor for q [B, Hq, S, 128], k/v [B, Hkv, S, 128], out [B, Hq, S, 128]."""
     B, Hq, S, d = q.shape
     Hkv = k.shape[1]
@@ -252,11 +272,11 @@ def prefill_desc(q, k, v, out, causal: bool = True, eps: float = 1e-6, scale: fl
         k_stride_b=k.stride(0), k_stride_h=k.stride(1), k_stride_s=k.stride(2),
         v_stride_b=v.stride(0), v_stride_h=v.stride(1), v_stride_s=v.stride(2),
         out_stride_b=out.stride(0), out_stride_h=out.stride(1), out_stride_s=out.stride(2),
-        eps=float(eps), scale=float(scale))
+        eps=float(eps), scale=float(scale), write_k_cache=1 if write_k_cache else 0)
 
 
 def prefill_chunk_desc(q, k_cache, v_cache, out, causal: bool = True, eps: float = 1e-6,
-                       scale: float = 0.0) -> GqaPrefillDesc:
+                       scale: float = 0.0, write_k_cache: bool = False) -> GqaPrefillDesc:
     """Descriptor for a chunk: q / out [B, Hq, T_max, 128], caches [B, Hkv, S, 128]."""
     B, Hq, T, d = q.shape
     _, Hkv, S, _ = k_cache.shape
@@ -267,7 +287,7 @@ def prefill_chunk_desc(q, k_cache, v_cache, out, causal: bool = True, eps: float
         k_stride_b=k_cache.stride(0), k_stride_h=k_cache.stride(1), k_stride_s=k_cache.stride(2),
         v_stride_b=v_cache.stride(0), v_stride_h=v_cache.stride(1), v_stride_s=v_cache.stride(2),
         out_stride_b=out.stride(0), out_stride_h=out.stride(1), out_stride_s=out.stride(2),
-        eps=float(eps), scale=float(scale), max_chunk=T)
+        eps=float(eps), scale=float(scale), max_chunk=T, write_k_cache=1 if write_k_cache else 0)
 
 
 def _stream_ptr(stream) -> int:
@@ -318,14 +338,15 @@ def prefill_workspace(desc: GqaPrefillDesc, device) -> "object":
 
 def prefill(q, k, v, seq_lens, positions, q_norm_w=None, k_norm_w=None, rope_theta: float = 0.0, out=None,
             causal: bool = True, eps: float = 1e-6, scale: float = 0.0, out_dtype=None, workspace="auto",
-            stream=None):
+            stream=None, write_k_cache: bool = False):
     """gqa_attn_prefill on torch tensors (device memory); returns out.
     workspace: "auto" allocates one (two-phase path), None selects the
-    single-kernel path, or a uint8 device tensor."""
+    single-kernel path, or a uint8 device tensor.  With write_k_cache, k
+    receives the post-prologue keys (bf16)."""
     import torch
     if out is None:
         out = torch.empty(q.shape, dtype=out_dtype or torch.float32, device=q.device)
-    desc = prefill_desc(q, k, v, out, causal, eps, scale)
+    desc = prefill_desc(q, k, v, out, causal, eps, scale, write_k_cache)
     if isinstance(workspace, str):
         workspace = prefill_workspace(desc, q.device)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
@@ -338,13 +359,14 @@ def prefill(q, k, v, seq_lens, positions, q_norm_w=None, k_norm_w=None, rope_the
 
 def prefill_chunk(q, k_cache, v_cache, past_lens, chunk_lens, positions, q_norm_w=None, k_norm_w=None,
                   rope_theta: float = 0.0, out=None, causal: bool = True, eps: float = 1e-6, scale: float = 0.0,
-                  out_dtype=None, workspace=None, stream=None):
+                  out_dtype=None, workspace=None, stream=None, write_k_cache: bool = False):
     """gqa_attn_prefill_chunk on torch tensors (device memory); returns out.
-    workspace: a uint8 device tensor, or None to allocate one."""
+    workspace: a uint8 device tensor, or None to allocate one.  With
+    write_k_cache, the chunk's key rows receive their post-prologue values."""
     import torch
     if out is None:
         out = torch.empty(q.shape, dtype=out_dtype or torch.float32, device=q.device)
-    desc = prefill_chunk_desc(q, k_cache, v_cache, out, causal, eps, scale)
+    desc = prefill_chunk_desc(q, k_cache, v_cache, out, causal, eps, scale, write_k_cache)
     if workspace is None:
         workspace = prefill_workspace(desc, q.device)
     ws_bytes = workspace.numel() * workspace.element_size()
@@ -388,7 +410,8 @@ def decode_paged(q, k_pages, v_pages, block_table, seq_lens, positions, q_norm_w
 
 def prefill_chunk_paged(q, k_pages, v_pages, block_table, past_lens, chunk_lens, positions, q_norm_w=None,
                         k_norm_w=None, rope_theta: float = 0.0, out=None, causal: bool = True, eps: float = 1e-6,
-                        scale: float = 0.0, out_dtype=None, workspace=None, stream=None):
+                        scale: float = 0.0, out_dtype=None, workspace=None, stream=None,
+                        write_k_cache: bool = False):
     """gqa_attn_prefill_chunk_paged on torch tensors: k_pages / v_pages [num_pages, Hkv, bs, 128],
     block_table [B, max_blocks] int32 (cache capacity max_blocks * bs); returns out."""
     import torch
@@ -403,7 +426,7 @@ def prefill_chunk_paged(q, k_pages, v_pages, block_table, past_lens, chunk_lens,
         k_stride_b=k_pages.stride(0), k_stride_h=k_pages.stride(1), k_stride_s=k_pages.stride(2),
         v_stride_b=v_pages.stride(0), v_stride_h=v_pages.stride(1), v_stride_s=v_pages.stride(2),
         out_stride_b=out.stride(0), out_stride_h=out.stride(1), out_stride_s=out.stride(2),
-        eps=float(eps), scale=float(scale), max_chunk=T, block_size=bs)
+        eps=float(eps), scale=float(scale), max_chunk=T, block_size=bs, write_k_cache=1 if write_k_cache else 0)
     if workspace is None:
         workspace = prefill_workspace(desc, q.device)
     ws_bytes = workspace.numel() * workspace.element_size()

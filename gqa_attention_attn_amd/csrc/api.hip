@@ -127,6 +127,7 @@ gqa_status check_prefill_desc(const gqa_prefill_desc* d) {
   if (d->head_dim != GQA_ATTN_HEAD_DIM) return GQA_ERR_UNSUPPORTED;
   if (d->in_dtype != GQA_BF16 || !dtype_ok(d->out_dtype)) return GQA_ERR_UNSUPPORTED;
   if (d->causal != 0 && d->causal != 1) return GQA_ERR_SHAPE;
+  if (d->write_k_cache != 0 && d->write_k_cache != 1) return GQA_ERR_SHAPE;
   if (d->block_size != 0) {   // paged: a power of two >= 16 rows per page, whole pages
     if (d->block_size < 16 || (d->block_size & (d->block_size - 1)) != 0 || d->max_seq % d->block_size != 0)
       return GQA_ERR_SHAPE;
@@ -346,6 +347,7 @@ gqa_status prepare_prefill(const gqa_prefill_desc* d, const void* q, const void*
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) || !aligned16(q_norm_w) ||
       !aligned16(k_norm_w) || ((uintptr_t)lens & 3u) || ((uintptr_t)positions & 3u) || ((uintptr_t)past_lens & 3u))
     return GQA_ERR_ALIGN;
+  if (d->write_k_cache && workspace == nullptr) return GQA_ERR_WORKSPACE;   // the write-back is phase 1's
   if (workspace != nullptr) {
     if (workspace_bytes < gqa::prefill_workspace_bytes(d->batch, d->num_q_heads, d->num_kv_heads, d->max_seq,
                                                        d->max_chunk > 0 ? d->max_chunk : d->max_seq, d->causal != 0))
@@ -387,6 +389,7 @@ gqa_status prepare_prefill(const gqa_prefill_desc* d, const void* q, const void*
   p.max_seq = d->max_seq;
   p.max_chunk = past_lens != nullptr && d->max_chunk > 0 ? d->max_chunk : d->max_seq;
   p.causal = d->causal;
+  p.write_k_cache = d->write_k_cache;
   p.out_bf16 = d->out_dtype == GQA_BF16;
   prefill_blocking(p.group, &p.heads_per_wg, &p.block_q);
   p.n_qblocks = (d->max_seq + p.block_q - 1) / p.block_q;
@@ -412,6 +415,35 @@ gqa_status gqa_attn_prefill(const gqa_prefill_desc* d, const void* q, const void
   const hipError_t e = workspace != nullptr ? gqa::launch_prefill_phased(p, workspace, stream)
                                             : gqa::launch_prefill_fused(p, stream);
   return e == hipSuccess ? GQA_OK : GQA_ERR_HIP;
+}
+
+// The two phases of gqa_attn_prefill with a workspace, as separate calls.
+static gqa_status prefill_phase(const gqa_prefill_desc* d, const void* q, const void* k, const void* v,
+                                const int32_t* seq_lens, const int32_t* positions, const void* q_norm_w,
+                                const void* k_norm_w, float rope_theta, void* out, void* workspace,
+                                size_t workspace_bytes, hipStream_t stream, int phase) {
+  if (workspace == nullptr) return GQA_ERR_WORKSPACE;
+  gqa::PrefillParams p;
+  const gqa_status st = prepare_prefill(d, q, k, v, seq_lens, nullptr, positions, q_norm_w, k_norm_w, rope_theta,
+                                        out, workspace, workspace_bytes, &p);
+  if (st != GQA_OK) return st;
+  return gqa::launch_prefill_phased(p, workspace, stream, phase) == hipSuccess ? GQA_OK : GQA_ERR_HIP;
+}
+
+gqa_status gqa_attn_prefill_keys(const gqa_prefill_desc* d, const void* q, const void* k, const void* v,
+                                 const int32_t* seq_lens, const int32_t* positions, const void* q_norm_w,
+                                 const void* k_norm_w, float rope_theta, void* out, void* workspace,
+                                 size_t workspace_bytes, hipStream_t stream) {
+  return prefill_phase(d, q, k, v, seq_lens, positions, q_norm_w, k_norm_w, rope_theta, out, workspace,
+                       workspace_bytes, stream, gqa::kPhaseKeys);
+}
+
+gqa_status gqa_attn_prefill_attend(const gqa_prefill_desc* d, const void* q, const void* k, const void* v,
+                                   const int32_t* seq_lens, const int32_t* positions, const void* q_norm_w,
+                                   const void* k_norm_w, float rope_theta, void* out, void* workspace,
+                                   size_t workspace_bytes, hipStream_t stream) {
+  return prefill_phase(d, q, k, v, seq_lens, positions, q_norm_w, k_norm_w, rope_theta, out, workspace,
+                       workspace_bytes, stream, gqa::kPhaseAttend);
 }
 
 gqa_status gqa_attn_prefill_chunk(const gqa_prefill_desc* d, const void* q, const void* k_cache,

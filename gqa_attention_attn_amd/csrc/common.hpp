@@ -63,6 +63,7 @@ struct PrefillParams {
   int32_t block_log2;     // paged: log2(rows per page)
   int32_t max_blocks;     // paged: row length of block_table
   int32_t max_chunk;      // query / output rows per sequence (max_seq for a plain prefill)
+  int32_t write_k_cache;  // two-phase: store each new key's post-prologue row (bf16) over its raw row
   int32_t span_tiles;     // two-phase: at most this many 32-key tiles per attention workgroup
   int32_t n_spans;        // two-phase: key spans per query block in the grid (1: no split)
   uint32_t* counters;     // two-phase, n_spans > 1: arrivals per (b, q head, query block)
@@ -90,7 +91,12 @@ inline hipError_t launch_kernel(void (*kernel)(Args...), dim3 grid, dim3 block, 
 hipError_t launch_decode_partition(const DecodeParams& p, bool in_bf16, hipStream_t stream);
 hipError_t launch_decode_merge(const DecodeParams& p, hipStream_t stream);
 hipError_t launch_prefill_fused(const PrefillParams& p, hipStream_t stream);
-hipError_t launch_prefill_phased(const PrefillParams& p, void* workspace, hipStream_t stream);
+// Phases of the two-phase prefill: the key prologue into the workspace, then
+// attention over it.
+constexpr int kPhaseKeys = 1;
+constexpr int kPhaseAttend = 2;
+hipError_t launch_prefill_phased(const PrefillParams& p, void* workspace, hipStream_t stream,
+                                 int phases = kPhaseKeys | kPhaseAttend);
 // Bytes of the two-phase prefill workspace, for a plain prefill (max_chunk =
 // max_seq) and a chunked one (max_chunk <= max_seq) alike.
 size_t prefill_workspace_bytes(int batch, int num_q_heads, int num_kv_heads, int max_seq, int max_chunk, bool causal);
@@ -129,6 +135,22 @@ __device__ __forceinline__ uint32_t pack_f16x2(float lo, float hi) {
 }
 
 __device__ __forceinline__ f16x8 as_f16x8(u32x4 v) { return __builtin_bit_cast(f16x8, v); }
+
+// Largest finite fp16 magnitude.
+constexpr float kF16Max = 65504.0f;
+
+// x clamped to [-65504, 65504]; NaN stays NaN (IEEE maximum / minimum
+// propagate it, unlike fmaxf / fminf).
+__device__ __forceinline__ float clamp_f16_range(float x) {
+  return __builtin_elementwise_minimum(__builtin_elementwise_maximum(x, -kF16Max), kF16Max);
+}
+
+// Two f32 to packed fp16, saturating: magnitudes beyond 65504 become +-65504
+// instead of +-inf (round to nearest even inside the range).  Used for the
+// prefill operands q', k' and v, whose range is the caller's.
+__device__ __forceinline__ uint32_t pack_f16x2_sat(float lo, float hi) {
+  return pack_f16x2(clamp_f16_range(lo), clamp_f16_range(hi));
+}
 
 // Element e (0..7) of 8 packed bf16 held in 4 dwords, as float.
 __device__ __forceinline__ float bf16_elem(const u32x4& v, int e) {

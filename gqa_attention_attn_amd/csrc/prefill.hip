@@ -136,10 +136,10 @@ __device__ __forceinline__ void stage_unit(PrefillSmem& sm, const Raw& r, const 
     }
     uint32_t* krow = sm.kt[buf][lkey];
     const int sw = kswz(lkey);
-    *(u32x4*)(krow + 4 * (c ^ sw)) = u32x4{pack_f16x2(xl[0], xl[1]), pack_f16x2(xl[2], xl[3]),
-                                          pack_f16x2(xl[4], xl[5]), pack_f16x2(xl[6], xl[7])};
-    *(u32x4*)(krow + 4 * ((8 + c) ^ sw)) = u32x4{pack_f16x2(xh[0], xh[1]), pack_f16x2(xh[2], xh[3]),
-                                                pack_f16x2(xh[4], xh[5]), pack_f16x2(xh[6], xh[7])};
+    *(u32x4*)(krow + 4 * (c ^ sw)) = u32x4{pack_f16x2_sat(xl[0], xl[1]), pack_f16x2_sat(xl[2], xl[3]),
+                                          pack_f16x2_sat(xl[4], xl[5]), pack_f16x2_sat(xl[6], xl[7])};
+    *(u32x4*)(krow + 4 * ((8 + c) ^ sw)) = u32x4{pack_f16x2_sat(xh[0], xh[1]), pack_f16x2_sat(xh[2], xh[3]),
+                                                pack_f16x2_sat(xh[4], xh[5]), pack_f16x2_sat(xh[6], xh[7])};
   } else {
     const int v = u - kKUnits;
     const int kp = v & 15, dc = v >> 4;
@@ -147,8 +147,8 @@ __device__ __forceinline__ void stage_unit(PrefillSmem& sm, const Raw& r, const 
 #pragma unroll
     for (int j = 0; j < 4; ++j) {   // dims 8dc + 2j (lo halves) and 8dc + 2j + 1 (hi halves)
       const uint32_t a = r.a[j], c = r.b[j];
-      *(uint32_t*)&sm.vt[buf][8 * dc + 2 * j][pos] = pack_f16x2(bf16lo(a), bf16lo(c));
-      *(uint32_t*)&sm.vt[buf][8 * dc + 2 * j + 1][pos] = pack_f16x2(bf16hi(a), bf16hi(c));
+      *(uint32_t*)&sm.vt[buf][8 * dc + 2 * j][pos] = pack_f16x2_sat(bf16lo(a), bf16lo(c));
+      *(uint32_t*)&sm.vt[buf][8 * dc + 2 * j + 1][pos] = pack_f16x2_sat(bf16hi(a), bf16hi(c));
     }
   }
 }
@@ -276,10 +276,10 @@ __global__ __launch_bounds__(kMaxThreads) void prefill_kernel(const PrefillParam
           xh[e] = hi * c + lo * s;
         }
       }
-      qf[j] = as_f16x8(u32x4{pack_f16x2(xl[0], xl[1]), pack_f16x2(xl[2], xl[3]), pack_f16x2(xl[4], xl[5]),
-                              pack_f16x2(xl[6], xl[7])});
-      qf[4 + j] = as_f16x8(u32x4{pack_f16x2(xh[0], xh[1]), pack_f16x2(xh[2], xh[3]), pack_f16x2(xh[4], xh[5]),
-                                  pack_f16x2(xh[6], xh[7])});
+      qf[j] = as_f16x8(u32x4{pack_f16x2_sat(xl[0], xl[1]), pack_f16x2_sat(xl[2], xl[3]),
+                              pack_f16x2_sat(xl[4], xl[5]), pack_f16x2_sat(xl[6], xl[7])});
+      qf[4 + j] = as_f16x8(u32x4{pack_f16x2_sat(xh[0], xh[1]), pack_f16x2_sat(xh[2], xh[3]),
+                                  pack_f16x2_sat(xh[4], xh[5]), pack_f16x2_sat(xh[6], xh[7])});
     }
   }
   if (has0) stage_unit(sm, r0, p, rope, pos0, 0, u0, 0);

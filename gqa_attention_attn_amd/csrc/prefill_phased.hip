@@ -85,10 +85,11 @@ __device__ __forceinline__ SeqExtent seq_extent(const PrefillParams& p, int b) {
 
 // ----------------------------------------------------------------- phase 1: key prologue
 
-// Eight bf16 (packed) to eight fp16 (packed), round to nearest even.
+// Eight bf16 (packed) to eight fp16 (packed), round to nearest even,
+// saturating at +-65504.
 __device__ __forceinline__ u32x4 bf16x8_to_f16x8(const u32x4 x) {
-  return u32x4{pack_f16x2(bf16lo(x[0]), bf16hi(x[0])), pack_f16x2(bf16lo(x[1]), bf16hi(x[1])),
-               pack_f16x2(bf16lo(x[2]), bf16hi(x[2])), pack_f16x2(bf16lo(x[3]), bf16hi(x[3]))};
+  return u32x4{pack_f16x2_sat(bf16lo(x[0]), bf16hi(x[0])), pack_f16x2_sat(bf16lo(x[1]), bf16hi(x[1])),
+               pack_f16x2_sat(bf16lo(x[2]), bf16hi(x[2])), pack_f16x2_sat(bf16lo(x[3]), bf16hi(x[3]))};
 }
 
 // 16 key rows per workgroup; a row is held by 16 lanes (dims 4c..4c+3 and
@@ -99,7 +100,9 @@ __global__ __launch_bounds__(256) void key_prologue_kernel(const PrefillParams p
   __shared__ double inv_rev[kHeadDim / 2];
   const int b = blockIdx.z, h = blockIdx.y;
   const int tid = threadIdx.x, r = tid >> 4, c = tid & 15;
-  // the attention kernel's arrival counters start every call at zero
+  // the attention kernel's arrival counters are zeroed here on every call (the
+  // workspace's contents on entry are ignored); the attention kernel leaves
+  // them at zero again
   if (p.counters != nullptr && b == 0 && h == 0)
     for (int i = blockIdx.x * 256 + tid; i < p.n_counters; i += gridDim.x * 256) p.counters[i] = 0;
   const bool rope = p.rope_theta > 0.0;
@@ -162,8 +165,15 @@ __global__ __launch_bounds__(256) void key_prologue_kernel(const PrefillParams p
       x[4 + j] = bb * cs + a * sn;
     }
   }
-  *(u32x2*)(kd + 8 * c) = u32x2{pack_f16x2(x[0], x[1]), pack_f16x2(x[2], x[3])};
-  *(u32x2*)(kd + 128 + 8 * c) = u32x2{pack_f16x2(x[4], x[5]), pack_f16x2(x[6], x[7])};
+  *(u32x2*)(kd + 8 * c) = u32x2{pack_f16x2_sat(x[0], x[1]), pack_f16x2_sat(x[2], x[3])};
+  *(u32x2*)(kd + 128 + 8 * c) = u32x2{pack_f16x2_sat(x[4], x[5]), pack_f16x2_sat(x[6], x[7])};
+  // the cache keeps post-prologue keys: the row these 16 lanes (and nothing
+  // else in this call) have just read receives k' rounded to bf16
+  if (p.write_k_cache && (p.k_norm_w || rope)) {
+    uint16_t* dst = (uint16_t*)p.k + kro;
+    *(u32x2*)(dst + 4 * c) = u32x2{pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3])};
+    *(u32x2*)(dst + 64 + 4 * c) = u32x2{pack_bf16x2(x[4], x[5]), pack_bf16x2(x[6], x[7])};
+  }
 }
 
 // ----------------------------------------------------------------- phase 2: attention
@@ -639,10 +649,10 @@ __global__ __launch_bounds__(kAttnThreads, kWavesPerSimd) void attention_kernel(
             xh[e] = hi * c + lo * s;
           }
         }
-        qf[rb][j] = as_f16x8(u32x4{pack_f16x2(xl[0], xl[1]), pack_f16x2(xl[2], xl[3]),
-                                   pack_f16x2(xl[4], xl[5]), pack_f16x2(xl[6], xl[7])});
-        qf[rb][4 + j] = as_f16x8(u32x4{pack_f16x2(xh[0], xh[1]), pack_f16x2(xh[2], xh[3]),
-                                       pack_f16x2(xh[4], xh[5]), pack_f16x2(xh[6], xh[7])});
+        qf[rb][j] = as_f16x8(u32x4{pack_f16x2_sat(xl[0], xl[1]), pack_f16x2_sat(xl[2], xl[3]),
+                                   pack_f16x2_sat(xl[4], xl[5]), pack_f16x2_sat(xl[6], xl[7])});
+        qf[rb][4 + j] = as_f16x8(u32x4{pack_f16x2_sat(xh[0], xh[1]), pack_f16x2_sat(xh[2], xh[3]),
+                                       pack_f16x2_sat(xh[4], xh[5]), pack_f16x2_sat(xh[6], xh[7])});
       }
     }
   }
@@ -699,6 +709,9 @@ __global__ __launch_bounds__(kAttnThreads, kWavesPerSimd) void attention_kernel(
     if (tid == 0) {
       const uint32_t prev = __hip_atomic_fetch_add(p.counters + blk, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       last_span = prev + 1 == (uint32_t)ns;
+      // every span of the block has arrived: the counter is back to zero for
+      // the next call, so the attention phase can be replayed on its own
+      if (last_span) __hip_atomic_store(p.counters + blk, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
     __syncthreads();
     if (!last_span) return;
@@ -790,7 +803,7 @@ size_t prefill_workspace_bytes(int batch, int num_q_heads, int num_kv_heads, int
   return kv_bytes(batch, num_kv_heads, max_seq) + std::max(plain, chunk);
 }
 
-hipError_t launch_prefill_phased(const PrefillParams& p, void* workspace, hipStream_t stream) {
+hipError_t launch_prefill_phased(const PrefillParams& p, void* workspace, hipStream_t stream, int phases) {
   uint8_t* kws = (uint8_t*)workspace;
   uint8_t* vws = kws + (size_t)p.batch * p.num_kv_heads * ws_tiles(p.max_seq) * kTileBytes;
   const SplitPlan sp = split_plan(p.batch, p.num_q_heads, p.max_seq, p.max_chunk, p.causal != 0);
@@ -810,9 +823,13 @@ hipError_t launch_prefill_phased(const PrefillParams& p, void* workspace, hipStr
   }
   AttnOrder ord;
   fill_order(sp, p.max_seq, p.max_chunk, p.causal != 0, ord);
-  const hipError_t e = launch_kernel(key_prologue_kernel, dim3((unsigned)(ws_tiles(p.max_seq) * kBN / 16), p.num_kv_heads, p.batch),
-                                     dim3(256), stream, q, kws, vws);
-  if (e != hipSuccess) return e;
+  if (phases & kPhaseKeys) {
+    const hipError_t e = launch_kernel(key_prologue_kernel,
+                                       dim3((unsigned)(ws_tiles(p.max_seq) * kBN / 16), p.num_kv_heads, p.batch),
+                                       dim3(256), stream, q, kws, vws);
+    if (e != hipSuccess) return e;
+  }
+  if (!(phases & kPhaseAttend)) return hipSuccess;
   return launch_kernel(attention_kernel, dim3(q.n_qblocks * q.n_spans * p.num_q_heads * p.batch), dim3(kAttnThreads),
                        stream, q, (const uint8_t*)kws, (const uint8_t*)vws, ord);
 }

@@ -29,9 +29,10 @@
  *    loads.
  *  - The caller owns every buffer.  The library allocates nothing per call,
  *    keeps no mutable global state (calls are reentrant and thread-safe),
- *    never writes q / k / v / norm weights, writes `out` (and `workspace`),
- *    and writes a cache only where a decode descriptor asks for it
- *    (write_new_k: the new key's own row).  Calls are asynchronous on `stream`; the library
+ *    never writes q, v or the norm weights, writes `out` (and `workspace`),
+ *    and writes the key cache only where a descriptor asks for it (decode
+ *    write_new_k: the new key's own row; prefill write_k_cache: the rows of
+ *    the new tokens).  Calls are asynchronous on `stream`; the library
  *    never synchronises the host.
  *  - Every argument check except GQA_ERR_HIP happens on the host before any
  *    HIP call, so a rejected call has no device side effects.  No exception
@@ -60,7 +61,7 @@ extern "C" {
 
 #define GQA_ATTN_HEAD_DIM 128
 #define GQA_ATTN_MAX_GROUP 16      /* largest supported G = Hq / Hkv in decode */
-#define GQA_ATTN_VERSION 2
+#define GQA_ATTN_VERSION 3
 
 typedef enum gqa_status {
   GQA_OK = 0,
@@ -108,7 +109,8 @@ typedef struct gqa_prefill_desc {
   int32_t num_kv_heads;    /* Hkv, Hq % Hkv == 0                                   */
   int32_t head_dim;        /* must be 128                                          */
   int32_t max_seq;         /* S: token rows per sequence in q / k / v / out        */
-  int32_t in_dtype;        /* must be GQA_BF16 (products on fp16 MFMA)             */
+  int32_t in_dtype;        /* must be GQA_BF16 (products on fp16 MFMA, whose 11-bit
+                              operands cannot carry f32 inputs to their 1e-5 bound) */
   int32_t out_dtype;       /* GQA_F32 or GQA_BF16                                  */
   int32_t causal;          /* 1: query i sees keys j <= i; 0: all keys < S_b       */
   int64_t q_stride_b, q_stride_h, q_stride_s;
@@ -122,6 +124,8 @@ typedef struct gqa_prefill_desc {
   int32_t block_size;      /* 0: contiguous caches; > 0: rows per page of a paged
                               cache (gqa_attn_prefill_chunk_paged only), a power
                               of two >= 16 dividing max_seq                        */
+  int32_t write_k_cache;   /* 1: each new token's key row receives its
+                              post-prologue value (below); needs a workspace     */
 } gqa_prefill_desc;
 
 /* Human-readable name of a status code (static storage; never NULL). */
@@ -267,10 +271,13 @@ gqa_status gqa_attn_prefill_workspace_size(const gqa_prefill_desc* desc, size_t*
  * with f32 accumulation: q', k' and P are rounded to fp16 (round to nearest
  * even) and v converted to fp16 before the products.  The conversion of a
  * bf16 input is exact for magnitudes in [2^-14, 65504] and loses at most
- * 2^-25 absolute below; a v element, or a q' or k' element after the
- * prologue, of magnitude 65520 or more becomes infinite and the output rows
- * that read it are undefined (with the RMSNorm on, |q'|, |k'| are at most
- * sqrt(128) max|gamma|).
+ * 2^-25 absolute below.  Beyond that range the conversion saturates: an
+ * element of v or k' (after the prologue), or of q' (the two-phase path
+ * carries the softmax scale times log2(e) in q', so there the bound applies
+ * to q' * scale * log2(e)), whose magnitude exceeds 65504 enters the products
+ * as +-65504, and the result is that of the inputs so clamped (finite; NaN
+ * inputs stay NaN).  With the RMSNorm on, |q'|, |k'| are at most
+ * sqrt(128) max|gamma|.
  *
  * workspace: optional.  With a device buffer of at least
  * gqa_attn_prefill_workspace_size bytes (256-byte aligned; contents on entry
@@ -282,12 +289,49 @@ gqa_status gqa_attn_prefill_workspace_size(const gqa_prefill_desc* desc, size_t*
  * (query block, key tile) pair (no workspace, more arithmetic).  Calls that
  * share a workspace must not run concurrently (the key tiles, and the split
  * counters the call resets, are per call).
- * Errors: as gqa_attn_decode.
+ *
+ * desc->write_k_cache == 1 (two-phase path only) makes the key phase store,
+ * for every token s < n, k'_s rounded to bf16 over k[b, kv, s, :] after it has
+ * read that row ("Qwen3-14B Optimization" 2.1 Shape 4: the rope phase writes
+ * the rotated key into its KV-cache slot), so that k then holds the
+ * post-prologue keys a later chunked prefill or decode reads as its cache.
+ * Each row is read and written by the same threads and read by nothing else
+ * in the call; the attention phase reads only the workspace.  v is never
+ * written.  With the prologue off (no k_norm_w and rope_theta <= 0) nothing
+ * is written.
+ * Errors: as gqa_attn_decode; GQA_ERR_WORKSPACE for write_k_cache without a
+ * workspace; GQA_ERR_SHAPE for write_k_cache not 0 or 1.
  */
 gqa_status gqa_attn_prefill(const gqa_prefill_desc* desc, const void* q, const void* k, const void* v,
                             const int32_t* seq_lens, const int32_t* positions, const void* q_norm_w,
                             const void* k_norm_w, float rope_theta, void* out, void* workspace,
                             size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * The two phases of gqa_attn_prefill with a workspace, as separate calls with
+ * the same arguments (workspace required).  gqa_attn_prefill(..., workspace,
+ * ...) is exactly gqa_attn_prefill_keys(...) followed by
+ * gqa_attn_prefill_attend(...) on the same stream.
+ *
+ * gqa_attn_prefill_keys: the key prologue of every key row into the
+ * workspace (and, with write_k_cache, into k); writes nothing to `out`.
+ * gqa_attn_prefill_attend: attention of every query row (query prologue
+ * applied on load) over the keys the workspace holds; reads q, v (through the
+ * workspace), positions, seq_lens, q_norm_w and the workspace, writes `out`.
+ * The workspace must hold the key phase of the same descriptor, inputs and
+ * lengths; the attention phase may be repeated over it (its split counters
+ * return to zero at the end of every call).
+ * Errors: as gqa_attn_prefill; GQA_ERR_WORKSPACE for a missing workspace.
+ */
+gqa_status gqa_attn_prefill_keys(const gqa_prefill_desc* desc, const void* q, const void* k, const void* v,
+                                 const int32_t* seq_lens, const int32_t* positions, const void* q_norm_w,
+                                 const void* k_norm_w, float rope_theta, void* out, void* workspace,
+                                 size_t workspace_bytes, hipStream_t stream);
+
+gqa_status gqa_attn_prefill_attend(const gqa_prefill_desc* desc, const void* q, const void* k, const void* v,
+                                   const int32_t* seq_lens, const int32_t* positions, const void* q_norm_w,
+                                   const void* k_norm_w, float rope_theta, void* out, void* workspace,
+                                   size_t workspace_bytes, hipStream_t stream);
 
 /*
  * Chunked prefill ("ADR-0060: AHBM GQA Fused Attention Kernel (Llama3-70B)"
@@ -305,7 +349,10 @@ gqa_status gqa_attn_prefill(const gqa_prefill_desc* desc, const void* q, const v
  * is aligned at the bottom right of the T x (P + T) score matrix) or all
  * j < P + T (non-causal), of KV head floor(h / G):
  *   out[b, h, t, :] = sum_j softmax_j(scale * q'_t . K'_j) v_cache[b, kv, j, :]
- * Rows t >= T of out are not written; cache rows j >= P + T are not read; the
+ * Rows t >= T of out are not written; cache rows j >= P + T are not read.
+ * With desc->write_k_cache == 1 the chunk's key rows P <= j < P + T receive
+ * their post-prologue values (bf16), as in gqa_attn_prefill, so the cache
+ * holds post-prologue keys for the next chunk or decode step; otherwise the
  * caches are not written.  With P = 0 this is gqa_attn_prefill over the chunk.
  *
  * q, out: [B, Hq, T_max, 128] (strides q_stride_* / out_stride_*); k_cache,

@@ -29,7 +29,7 @@ Sources (the three web pages; no line numbers):
   - #602 paragraph: RoPE rotates the lo/hi halves of the head dimension; the
     QK-norm reciprocal is a per-row scalar that RoPE is linear in.
 
-Readings taken where the pages are silent (each listed in the design doc):
+Readings taken where the pages are silent:
 RMSNorm is x * (mean(x^2) + eps)^-1/2 * gamma over one head's d elements
 (gamma shared by all heads); RMSNorm comes before RoPE; RoPE is the textbook
 rotation of pairs (i, i + d/2) by angle p * theta^(-2i/d); in decode only the

@@ -266,6 +266,23 @@ def test_prefill_workspace_size_and_errors():
     assert call_prefill(d, ws=FAKE + 16, wsb=need) == G.GQA_ERR_ALIGN
 
 
+def test_prefill_phases_and_cache_write_errors():
+    d = pdesc()
+    st, need = G.gqa_attn_prefill_workspace_size(d)
+    for fn in (G.gqa_attn_prefill_keys, G.gqa_attn_prefill_attend):
+        # the phases exist only with a workspace
+        assert fn(d, FAKE, FAKE, FAKE, FAKE, FAKE, NULL, NULL, 1e6, FAKE, NULL, 0, None) == G.GQA_ERR_WORKSPACE
+        assert fn(d, FAKE, FAKE, FAKE, FAKE, FAKE, NULL, NULL, 1e6, FAKE, FAKE, need - 1, None) == G.GQA_ERR_WORKSPACE
+        assert fn(None, FAKE, FAKE, FAKE, FAKE, FAKE, NULL, NULL, 1e6, FAKE, FAKE, need, None) == G.GQA_ERR_NULL
+        assert fn(d, NULL, FAKE, FAKE, FAKE, FAKE, NULL, NULL, 1e6, FAKE, FAKE, need, None) == G.GQA_ERR_NULL
+        assert fn(pdesc(in_dtype=G.GQA_F32), FAKE, FAKE, FAKE, FAKE, FAKE, NULL, NULL, 1e6, FAKE, FAKE, need,
+                  None) == G.GQA_ERR_UNSUPPORTED
+    # the key-cache write-back is done by the key phase: no workspace, no write-back
+    assert call_prefill(pdesc(write_k_cache=1)) == G.GQA_ERR_WORKSPACE
+    assert call_prefill(pdesc(write_k_cache=2), ws=FAKE, wsb=need) == G.GQA_ERR_SHAPE
+    assert call_chunk(pdesc(max_chunk=64, write_k_cache=-1), wsb=need) == G.GQA_ERR_SHAPE
+
+
 def call_chunk(d, q=FAKE, k=FAKE, v=FAKE, past=FAKE, cl=FAKE, pos=FAKE, qw=NULL, kw=NULL, out=FAKE, ws=FAKE,
                wsb=1 << 40):
     return G.gqa_attn_prefill_chunk(d, q, k, v, past, cl, pos, qw, kw, 1e6, out, ws, wsb, None)
@@ -321,3 +338,23 @@ def test_prefill_chunk_paged_errors():
     assert call_prefill(pdesc(block_size=64)) == G.GQA_ERR_SHAPE
     for bad in (8, 24, 96):
         assert call(pdesc(max_chunk=64, block_size=bad)) == G.GQA_ERR_SHAPE
+
+
+# ---- the measurement probes (include/gqa_probe.h, libgqa_probe.so)
+
+def test_probe_library_exports_and_host_checks():
+    from gqa_attention_attn_amd import probe as P
+    if not os.path.exists(P.PROBE_LIB_PATH):
+        pytest.skip("libgqa_probe.so not built")
+    h = open(os.path.join(ROOT, "include", "gqa_probe.h")).read()
+    decl = set(re.findall(r"^\s*int32_t\s+(gqa_probe_\w+)\s*\(", h, re.M))
+    assert decl == set(P.EXPORTS)
+    out = subprocess.run(["nm", "-D", "--defined-only", P.PROBE_LIB_PATH], capture_output=True, text=True).stdout
+    assert decl <= set(re.findall(r"\bT (gqa_probe_\w+)", out))
+    # NULL, misaligned or ragged arguments are rejected on the host (status 1), before any HIP call
+    assert P.read(None, 1024, 64, None) == 1
+    assert P.read(4096 + 8, 1024, 64, None) == 1
+    assert P.read(4096, 1000, 64, None) == 1
+    assert P.read(4096, 1024, None, None) == 1
+    assert P.copy(4096, None, 1024, None) == 1
+    assert P.copy(4096, 8192 + 4, 1024, None) == 1
