@@ -138,19 +138,97 @@ def test_paths_agree():
     compare(a, b, ATOL_BF16, "two-phase vs single-kernel")
 
 
+def test_phases_equal_prefill_and_attend_replays():
+    # keys then attend is the two-phase prefill bitwise; the attention phase
+    # repeated over one key phase gives the same output every time, also for
+    # a plan that splits key ranges (8 query heads x 16 blocks = 128 items:
+    # two spans per long block, whose arrival counters return to zero)
+    torch = require_gpu()
+    for B, Hq, Hkv, S in ((1, 10, 2, 384), (1, 8, 1, 2048)):
+        inp = small(B=B, Hq=Hq, Hkv=Hkv, S=S, lens=[S])
+        g = gpu_inputs(inp)
+        log(f"case prefill phases B={B} Hq={Hq} Hkv={Hkv} S={S}")
+        whole = run(inp, g=g).cpu().numpy()
+        out = torch.full((B, Hq, S, 128), float("nan"), device="cuda")
+        desc = G.prefill_desc(g["q"], g["k"], g["v"], out, True, inp["eps"])
+        ws = G.prefill_workspace(desc, "cuda")
+        args = lambda: (desc, g["q"].data_ptr(), g["k"].data_ptr(), g["v"].data_ptr(), g["sl"].data_ptr(),
+                        g["pos"].data_ptr(), g["qw"].data_ptr(), g["kw"].data_ptr(), inp["rope_theta"],
+                        out.data_ptr(), ws.data_ptr(), ws.numel(), torch.cuda.current_stream().cuda_stream)
+        assert G.gqa_attn_prefill_keys(*args()) == G.GQA_OK
+        for rep in range(3):
+            out.fill_(float("nan"))
+            assert G.gqa_attn_prefill_attend(*args()) == G.GQA_OK
+            torch.cuda.synchronize()
+            assert np.array_equal(out.cpu().numpy(), whole), f"attend replay {rep} differs"
+        compare(whole, ref(inp), ATOL_BF16, f"phases S={S}")
+
+
 @pytest.mark.parametrize("path", PATHS)
-def test_qwen3_prefill_s4096_sampled(path):
-    # the full Qwen3-14B causal prefill (S = 4096, 40 / 8 heads), checked on
-    # sampled heads and rows that span first, diagonal, ragged-tile and last rows
-    w = synth.QWEN3_PREFILL
-    log(f"case {w.name} {path}")
-    inp = synth.make_prefill(w)
+def test_fp16_range_saturates(path):
+    # v and k' enter fp16 products; beyond +-65504 they saturate, and the call
+    # returns the oracle's result for the inputs clamped to that range.
+    # 59904 (bf16-exact) is inside the range, -70144 and 70144 are not.
+    inp = small(B=1, Hq=10, Hkv=2, S=160, lens=[160], norm=False, theta=0.0)
+    inp["v"][0, 0, 0, 3] = 59904.0      # key 0 of KV head 0
+    inp["v"][0, 1, 0, 7] = -70144.0     # key 0 of KV head 1
+    inp["v"][0, 1, 40, 9] = 70144.0
+    inp["k"][0, 1, 9, 11] = 70144.0
+    clamped = dict(inp, v=np.clip(inp["v"], -65504.0, 65504.0), k=np.clip(inp["k"], -65504.0, 65504.0))
+    log(f"case fp16 range {path}")
     out = run(inp, path=path).cpu().numpy()
-    heads = [0, 4, 5, 17, 39]
-    rows = np.array([0, 1, 63, 64, 127, 128, 129, 1000, 2047, 2048, 3071, 4094, 4095])
-    r = ref(inp, heads=heads, rows=rows)
-    compare(out[0][heads][:, rows], r[0][heads][:, rows], ATOL_BF16, "qwen3 prefill sampled")
     assert np.all(np.isfinite(out))
+    # row 0 sees key 0 alone (weight exactly 1): the stored value, saturated or not
+    assert np.all(out[0, 0:5, 0, 3] == 59904.0)
+    assert np.all(out[0, 5:10, 0, 7] == -65504.0)
+    want = ref(clamped)
+    # P is rounded to fp16 (11 significant bits) before P V, so each output
+    # element is off by at most 2^-10 sum_j w_j |v_j| (the oracle's output
+    # for |v|) beyond the usual bound
+    mass = ref(dict(clamped, v=np.abs(clamped["v"])))
+    err = np.abs(out - want)
+    bound = ATOL_BF16 + 2.0 ** -10 * mass
+    assert np.all(err <= bound), f"max excess {np.max(err - bound)}"
+
+
+# ---- the full Qwen3-14B causal prefill (S = 4096, 40 query heads over 8 KV
+# heads): every element of out against the oracle.  out starts as NaN, so a
+# block the kernels leave unwritten fails.  The GPU output is computed once
+# per path; the oracle once per KV group (5 query heads each) and shared by
+# both paths.
+
+_QWEN3 = {}
+
+
+def qwen3_inputs():
+    if "inp" not in _QWEN3:
+        _QWEN3["inp"] = synth.make_prefill(synth.QWEN3_PREFILL)
+    return _QWEN3["inp"]
+
+
+def qwen3_oracle_group(kv):
+    key = ("ref", kv)
+    if key not in _QWEN3:
+        heads = list(range(5 * kv, 5 * kv + 5))
+        _QWEN3[key] = ref(qwen3_inputs(), heads=heads)[0, heads]
+    return _QWEN3[key]
+
+
+@pytest.fixture(scope="module", params=PATHS)
+def qwen3_gpu(request):
+    torch = require_gpu()
+    inp = qwen3_inputs()
+    log(f"case {synth.QWEN3_PREFILL.name} {request.param} (out pre-filled with NaN)")
+    out = torch.full(inp["q"].shape, float("nan"), dtype=torch.float32, device="cuda")
+    run(inp, out=out, path=request.param)
+    return request.param, out.cpu().numpy()
+
+
+@pytest.mark.parametrize("kv", range(8))
+def test_qwen3_prefill_s4096_full(qwen3_gpu, kv):
+    path, out = qwen3_gpu
+    heads = list(range(5 * kv, 5 * kv + 5))
+    compare(out[0, heads], qwen3_oracle_group(kv), ATOL_BF16, f"qwen3 prefill {path} KV group {kv} (heads {heads[0]}-{heads[-1]}, all rows)")
 
 
 def test_prefill_last_row_matches_decode():
