@@ -46,8 +46,11 @@ def test_prefill_write_k_cache_stores_the_prologue_rows():
     gq, gk = bf(1 + 0.1 * rng.standard_normal(128)), bf(1 + 0.1 * rng.standard_normal(128))
     t = torch.bfloat16
     k0, k1, vd, qd = dev(k, t), dev(k, t), dev(v, t), dev(q, t)
-    a = G.prefill(qd, k0, vd, ints(lens), ints(pos0), dev(gq, t), dev(gk, t), THETA, eps=EPS)
-    b = G.prefill(qd, k1, vd, ints(lens), ints(pos0), dev(gq, t), dev(gk, t), THETA, eps=EPS, write_k_cache=True)
+    # rows past a sequence's length are not written: both outputs start equal
+    a = G.prefill(qd, k0, vd, ints(lens), ints(pos0), dev(gq, t), dev(gk, t), THETA, eps=EPS,
+                  out=torch.zeros(B, Hq, S, 128, device="cuda"))
+    b = G.prefill(qd, k1, vd, ints(lens), ints(pos0), dev(gq, t), dev(gk, t), THETA, eps=EPS, write_k_cache=True,
+                  out=torch.zeros(B, Hq, S, 128, device="cuda"))
     torch.cuda.synchronize()
     assert torch.equal(a, b), "write_k_cache changed the output"
     assert torch.equal(k0, dev(k, t)), "flag off wrote the cache"
@@ -85,10 +88,11 @@ def test_chunk_write_k_cache_stores_only_the_chunk_rows(bs):
         k[b][:, :P] = bf(O.prologue(k[b][:, :P], gk, pos0[b] + np.arange(P), THETA, EPS))
     t = torch.bfloat16
     log(f"case chunk write_k_cache bs={bs}")
+    zeros = lambda: torch.zeros(B, Hq, Tmax, 128, device="cuda")   # rows past a chunk are not written
     if bs == 0:
         k0, k1, vd = dev(k, t), dev(k, t), dev(v, t)
         call = lambda kk, w: G.prefill_chunk(dev(q, t), kk, vd, ints(past), ints(chunk), ints(pos0), dev(gq, t),
-                                             dev(gk, t), THETA, eps=EPS, write_k_cache=w)
+                                             dev(gk, t), THETA, eps=EPS, write_k_cache=w, out=zeros())
         logical = lambda kk: kk.float().cpu().numpy()
     else:
         nb = S // bs
@@ -103,7 +107,7 @@ def test_chunk_write_k_cache_stores_only_the_chunk_rows(bs):
         k0, k1, vd = dev(kp, t), dev(kp, t), dev(vp, t)
         call = lambda kk, w: G.prefill_chunk_paged(dev(q, t), kk, vd, ints(table), ints(past), ints(chunk),
                                                    ints(pos0), dev(gq, t), dev(gk, t), THETA, eps=EPS,
-                                                   write_k_cache=w)
+                                                   write_k_cache=w, out=zeros())
         logical = lambda kk: O.paged_gather(kk.float().cpu().numpy(), table, np.full(B, S), bs, S)
     a = call(k0, False)
     b2 = call(k1, True)
