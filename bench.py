@@ -720,7 +720,7 @@ def main():
             torch.cuda.empty_cache()
 
         extra["probes"] = measure_probes(ctx)
-        rd = extra["probes"]["hbm_read_1gib"]["gbs"]
+        rd = extra["probes"]["hbm_read_1024mib"]["gbs"]
         result["roofline"]["frac_of_read_probe"] = round(result["roofline"]["achieved"] / rd, 4)
         result["extra"] = extra
     print(json.dumps(result), flush=True)
