@@ -24,11 +24,13 @@ GQA_ERR_UNSUPPORTED = 3
 GQA_ERR_ALIGN = 4
 GQA_ERR_WORKSPACE = 5
 GQA_ERR_HIP = 6
+GQA_ERR_SCRATCH = 7
 GQA_F32 = 0
 GQA_BF16 = 1
 GQA_ATTN_HEAD_DIM = 128
 GQA_ATTN_MAX_GROUP = 16
 GQA_ATTN_VERSION = 3
+GQA_ATTN_STATIC_SCRATCH_BYTES = 16 << 20
 
 EXPORTS = (
     "gqa_attn_status_string",
@@ -38,6 +40,7 @@ EXPORTS = (
     "gqa_attn_decode",
     "gqa_attn_decode_partition",
     "gqa_attn_decode_merge",
+    "gqa_attn_decode_static",
     "gqa_attn_decode_paged",
     "gqa_attn_prefill_workspace_size",
     "gqa_attn_prefill",
@@ -115,6 +118,9 @@ def lib() -> ctypes.CDLL:
         L.gqa_attn_decode_partition.restype = ctypes.c_int
         L.gqa_attn_decode_merge.argtypes = [ctypes.POINTER(GqaDecodeDesc), vp, vp, vp, ctypes.c_size_t, vp]
         L.gqa_attn_decode_merge.restype = ctypes.c_int
+        L.gqa_attn_decode_static.argtypes = [ctypes.POINTER(GqaDecodeDesc), vp, vp, vp, vp, vp, vp, vp,
+                                             ctypes.c_float, vp, vp]
+        L.gqa_attn_decode_static.restype = ctypes.c_int
         L.gqa_attn_decode_paged.argtypes = [ctypes.POINTER(GqaDecodeDesc), vp, vp, vp, vp, vp, vp, vp, vp,
                                             ctypes.c_float, vp, vp, ctypes.c_size_t, vp]
         L.gqa_attn_decode_paged.restype = ctypes.c_int
@@ -178,6 +184,14 @@ def gqa_attn_decode_partition(desc, q, k_cache, v_cache, seq_lens, positions, q_
 def gqa_attn_decode_merge(desc, seq_lens, out, workspace, workspace_bytes, stream) -> int:
     return int(lib().gqa_attn_decode_merge(ctypes.byref(desc) if desc is not None else None, seq_lens, out,
                                            workspace, int(workspace_bytes), stream))
+
+
+def gqa_attn_decode_static(desc, q, k_cache, v_cache, seq_lens, positions, q_norm_w, k_norm_w, rope_theta, out,
+                           stream) -> int:
+    """gqa_attn_decode with the partials in the library's static device array (no workspace)."""
+    return int(lib().gqa_attn_decode_static(ctypes.byref(desc) if desc is not None else None, q, k_cache, v_cache,
+                                            seq_lens, positions, q_norm_w, k_norm_w, float(rope_theta), out,
+                                            stream))
 
 
 def gqa_attn_decode_paged(desc, q, k_pages, v_pages, block_table, seq_lens, positions, q_norm_w, k_norm_w,

@@ -4,6 +4,8 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "../../include/gqa_attn.h"
 #include "common.hpp"
 
@@ -164,6 +166,7 @@ const char* gqa_attn_status_string(gqa_status status) {
     case GQA_ERR_ALIGN: return "GQA_ERR_ALIGN: pointer or stride not 16-byte aligned";
     case GQA_ERR_WORKSPACE: return "GQA_ERR_WORKSPACE: workspace missing or too small";
     case GQA_ERR_HIP: return "GQA_ERR_HIP: kernel launch failed";
+    case GQA_ERR_SCRATCH: return "GQA_ERR_SCRATCH: the call needs more than the library's static decode scratch";
   }
   return "GQA_ERR_UNKNOWN: unknown status code";
 }
@@ -299,6 +302,64 @@ gqa_status gqa_attn_decode(const gqa_decode_desc* d, const void* q, const void* 
   const gqa_status st = prepare_decode(d, q, k_cache, v_cache, seq_lens, positions, q_norm_w, k_norm_w, rope_theta,
                                        out, workspace, workspace_bytes, true, &p);
   if (st != GQA_OK) return st;
+  if (gqa::launch_decode_partition(p, d->in_dtype == GQA_BF16, stream) != hipSuccess) return GQA_ERR_HIP;
+  return gqa::launch_decode_merge(p, stream) == hipSuccess ? GQA_OK : GQA_ERR_HIP;
+}
+
+}  // extern "C"
+
+namespace {
+
+// ---- decode partials without a caller workspace: a file-scope device array
+//      of GQA_ATTN_STATIC_SCRATCH_BYTES.  Each device that runs the library
+//      holds its own copy (until the process ends) at its own address, found
+//      once per device with hipGetSymbolAddress while that device is current;
+//      host code passes only that address to kernels, never the array's name.
+static __device__ __align__(256) uint8_t scratch[GQA_ATTN_STATIC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex scratch_mutex;
+void* scratch_ptr[kMaxDevices] = {};
+
+// Address of this device's scratch array (the current device's).
+gqa_status device_scratch(void** ptr) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return GQA_ERR_HIP;
+  if (dev < 0 || dev >= kMaxDevices) return GQA_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(scratch_mutex);
+  if (scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) return GQA_ERR_HIP;
+    scratch_ptr[dev] = p;
+  }
+  *ptr = scratch_ptr[dev];
+  return GQA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+gqa_status gqa_attn_decode_static(const gqa_decode_desc* d, const void* q, const void* k_cache, const void* v_cache,
+                                  const int32_t* seq_lens, const int32_t* positions, const void* q_norm_w,
+                                  const void* k_norm_w, float rope_theta, void* out, hipStream_t stream) {
+  const gqa_status st = check_decode_desc(d);
+  if (st != GQA_OK) return st;
+  int32_t T, n;
+  decode_plan(d, &T, &n);
+  if (decode_ws_bytes(d, T, n) > GQA_ATTN_STATIC_SCRATCH_BYTES) return GQA_ERR_SCRATCH;
+  // every argument check on the host first (a stand-in workspace address of
+  // the right alignment and size), then the scratch address (HIP calls)
+  gqa::DecodeParams p;
+  gqa_status v = prepare_decode(d, q, k_cache, v_cache, seq_lens, positions, q_norm_w, k_norm_w, rope_theta, out,
+                                (void*)(uintptr_t)256, GQA_ATTN_STATIC_SCRATCH_BYTES, true, &p);
+  if (v != GQA_OK) return v;
+  void* ws = nullptr;
+  v = device_scratch(&ws);
+  if (v != GQA_OK) return v;
+  v = prepare_decode(d, q, k_cache, v_cache, seq_lens, positions, q_norm_w, k_norm_w, rope_theta, out, ws,
+                     GQA_ATTN_STATIC_SCRATCH_BYTES, true, &p);
+  if (v != GQA_OK) return v;
   if (gqa::launch_decode_partition(p, d->in_dtype == GQA_BF16, stream) != hipSuccess) return GQA_ERR_HIP;
   return gqa::launch_decode_merge(p, stream) == hipSuccess ? GQA_OK : GQA_ERR_HIP;
 }

@@ -62,6 +62,8 @@ extern "C" {
 #define GQA_ATTN_HEAD_DIM 128
 #define GQA_ATTN_MAX_GROUP 16      /* largest supported G = Hq / Hkv in decode */
 #define GQA_ATTN_VERSION 3
+/* bytes of the device array that gqa_attn_decode_static keeps its partials in */
+#define GQA_ATTN_STATIC_SCRATCH_BYTES (16u << 20)
 
 typedef enum gqa_status {
   GQA_OK = 0,
@@ -71,7 +73,9 @@ typedef enum gqa_status {
                               decode cache slab of one (b, head) >= 4 GiB        */
   GQA_ERR_ALIGN = 4,       /* base pointer or stride not 16-byte aligned          */
   GQA_ERR_WORKSPACE = 5,   /* workspace NULL or smaller than required             */
-  GQA_ERR_HIP = 6          /* a kernel launch failed (its hipLaunchKernel status) */
+  GQA_ERR_HIP = 6,         /* a kernel launch failed (its hipLaunchKernel status) */
+  GQA_ERR_SCRATCH = 7      /* gqa_attn_decode_static: partials exceed the static
+                              scratch (GQA_ATTN_STATIC_SCRATCH_BYTES)             */
 } gqa_status;
 
 typedef enum gqa_dtype {
@@ -219,6 +223,30 @@ gqa_status gqa_attn_decode_partition(const gqa_decode_desc* desc, const void* q,
 
 gqa_status gqa_attn_decode_merge(const gqa_decode_desc* desc, const int32_t* seq_lens, void* out, void* workspace,
                                  size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * gqa_attn_decode without a workspace argument, for callers that cannot
+ * allocate device memory: code under HIP graph capture, serving loops and
+ * harnesses that forbid allocation.  Same computation, outputs, plan and
+ * kernels as gqa_attn_decode (bitwise the same out), with the split-KV
+ * partials kept in a file-scope device array of GQA_ATTN_STATIC_SCRATCH_BYTES
+ * (16 MiB) that every device running the library holds until the process
+ * ends.  The call allocates nothing (no hipMalloc, no allocating library
+ * routine); its first call on a device looks up that device's copy of the
+ * array (hipGetSymbolAddress, with the device current) and keeps the address.
+ * Every call on one device shares its array: calls that overlap on a device
+ * (other streams, other host threads) race and must be serialised by the
+ * caller; the array's contents between calls are unspecified (nothing in it
+ * needs to start at zero).  Plans needing at most the array's bytes are
+ * accepted (gqa_attn_decode_workspace_size reports what a descriptor needs).
+ * Errors: as gqa_attn_decode (no GQA_ERR_WORKSPACE); GQA_ERR_SCRATCH when the
+ * plan needs more than the array holds (checked on the host before any HIP
+ * call); GQA_ERR_HIP also when the array's address cannot be looked up.
+ */
+gqa_status gqa_attn_decode_static(const gqa_decode_desc* desc, const void* q, const void* k_cache,
+                                  const void* v_cache, const int32_t* seq_lens, const int32_t* positions,
+                                  const void* q_norm_w, const void* k_norm_w, float rope_theta, void* out,
+                                  hipStream_t stream);
 
 /*
  * Decode over a paged KV cache (block table; the layout a serving engine's

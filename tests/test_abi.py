@@ -225,6 +225,29 @@ def test_prefill_pointer_errors():
         assert call_prefill(d, **{name: FAKE + 4}) == G.GQA_ERR_ALIGN, name
 
 
+def test_decode_static_host_checks():
+    # the entry point without a workspace: every argument check on the host,
+    # and plans whose partials exceed the static array are refused
+    st = G.gqa_attn_decode_static
+    h = header_text()
+    assert G.GQA_ATTN_STATIC_SCRATCH_BYTES == eval(re.search(r"#define GQA_ATTN_STATIC_SCRATCH_BYTES \((\d+)u << (\d+)\)",
+                                                             h).expand(r"\1 << \2"))
+    d = ddesc(kv_split_tokens=512)
+    assert st(None, FAKE, FAKE, FAKE, FAKE, FAKE, NULL, NULL, 1e6, FAKE, None) == G.GQA_ERR_NULL
+    assert st(d, NULL, FAKE, FAKE, FAKE, FAKE, NULL, NULL, 1e6, FAKE, None) == G.GQA_ERR_NULL
+    assert st(d, FAKE, FAKE, FAKE, FAKE, FAKE, NULL, NULL, 1e6, NULL, None) == G.GQA_ERR_NULL
+    assert st(d, FAKE + 4, FAKE, FAKE, FAKE, FAKE, NULL, NULL, 1e6, FAKE, None) == G.GQA_ERR_ALIGN
+    assert st(ddesc(head_dim=64), FAKE, FAKE, FAKE, FAKE, FAKE, NULL, NULL, 1e6, FAKE, None) == G.GQA_ERR_UNSUPPORTED
+    # 64 sequences x 64 query heads x 256 partials x 520 bytes = 520 MiB > 16 MiB
+    big = ddesc(batch=64, num_q_heads=64, max_seq=1 << 17, kv_split_tokens=512, q_stride_b=64 * 128,
+                k_stride_b=8 * (1 << 17) * 128, k_stride_h=(1 << 17) * 128, v_stride_b=8 * (1 << 17) * 128,
+                v_stride_h=(1 << 17) * 128, out_stride_b=64 * 128)
+    stb, need = G.gqa_attn_decode_workspace_size(big)
+    assert stb == G.GQA_OK and need > G.GQA_ATTN_STATIC_SCRATCH_BYTES
+    assert st(big, FAKE, FAKE, FAKE, FAKE, FAKE, NULL, NULL, 1e6, FAKE, None) == G.GQA_ERR_SCRATCH
+    assert "static decode scratch" in G.gqa_attn_status_string(G.GQA_ERR_SCRATCH)
+
+
 def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(G, "LIB_PATH", str(tmp_path / "missing.so"))
     monkeypatch.setattr(G, "_lib", None)
