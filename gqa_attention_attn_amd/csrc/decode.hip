@@ -42,20 +42,28 @@ constexpr int kXcds = 8;
 constexpr int kStreamWaves = 4;
 constexpr int kPrologueWave = kStreamWaves;
 constexpr int kThreads = (kStreamWaves + 1) * 64;
+// Single-chunk grids of many workgroups run a 4-wave form instead: streaming
+// wave 0 also runs the prologue and one chunk-state buffer suffices, so two
+// workgroups share a compute unit (two waves per SIMD, no register spills) and
+// one's start (length, q rows, prologue) and short-lived empty ranges overlap
+// the other's K/V stream.
+constexpr int kThreads4 = kStreamWaves * 64;
+constexpr int kMany4 = 1024;   // grids of at least this many single-chunk workgroups
 constexpr int kStep = 32;        // keys per wave step
 constexpr int kORow = 132;       // padded LDS row (floats) of the in-workgroup merge
 constexpr int kQRow = 136;       // padded bf16 q' row (272 bytes): 16 rows x 16 bytes hit distinct banks
 
-struct __attribute__((aligned(16))) DecodeSmem {
+template <int NB>   // chunk-state buffers: 2 when a workgroup sweeps several chunks
+struct __attribute__((aligned(16))) DecodeSmemT {
   float cs[64][2];               // RoPE cos / sin at positions[b]
   float qp[16][kHeadDim];        // q' rows after the prologue (rows >= G are zero)
   uint16_t qh[16][kQRow];        // bf16(q')            (rows >= G are zero)
   uint16_t ql[16][kQRow];        // bf16(q' - bf16(q'))
   float kn[kHeadDim];            // the new key row after the prologue
   float snew[16];                // score of the new key per query head (log2 units)
-  float mo[2][kStreamWaves][16][kORow];   // per-wave unnormalised O of a chunk (double-buffered)
-  float mm[2][kStreamWaves][16];
-  float ml[2][kStreamWaves][16];
+  float mo[NB][kStreamWaves][16][kORow];   // per-wave unnormalised O of a chunk (double-buffered when NB = 2)
+  float mm[NB][kStreamWaves][16];
+  float ml[NB][kStreamWaves][16];
 };
 
 // Half-row fetch of a 128-element row for the 16 lanes that hold it:
@@ -275,7 +283,8 @@ __device__ __forceinline__ void load_step(Step& st, const SL& sl, int key0, int 
 struct QFragBF16 { bf16x8 hi[4], lo[4]; };
 struct QFragF32 { float q[32]; };
 
-__device__ __forceinline__ void load_qfrag(QFragBF16& qf, const DecodeSmem& sm, int n16, int q4) {
+template <class SM>
+__device__ __forceinline__ void load_qfrag(QFragBF16& qf, const SM& sm, int n16, int q4) {
 #pragma unroll
   for (int kb = 0; kb < 4; ++kb) {
     qf.hi[kb] = *(const bf16x8*)&sm.qh[n16][32 * q4 + 8 * kb];
@@ -283,7 +292,8 @@ __device__ __forceinline__ void load_qfrag(QFragBF16& qf, const DecodeSmem& sm, 
   }
 }
 
-__device__ __forceinline__ void load_qfrag(QFragF32& qf, const DecodeSmem& sm, int n16, int q4) {
+template <class SM>
+__device__ __forceinline__ void load_qfrag(QFragF32& qf, const SM& sm, int n16, int q4) {
 #pragma unroll
   for (int j = 0; j < 32; j += 4) {
     const f32x4 x = *(const f32x4*)&sm.qp[n16][32 * q4 + j];
@@ -445,8 +455,8 @@ __device__ __forceinline__ void prologue_issue(const DecodeParams& p, int b, int
   pr.y = fetch_half_row<BF16>(krow, c16);
 }
 
-template <bool BF16>
-__device__ __forceinline__ void prologue_finish(const DecodeParams& p, DecodeSmem& sm, double pos, int lane,
+template <bool BF16, class SM>
+__device__ __forceinline__ void prologue_finish(const DecodeParams& p, SM& sm, double pos, int lane,
                                                 bool rope, bool has_new, PrologueRegs<BF16>& pr) {
   const int r4 = lane >> 4, c16 = lane & 15;
   const int G = p.group;
@@ -533,7 +543,8 @@ __device__ __forceinline__ void write_zero_rows(const DecodeParams& p, int b, in
 // section 4, in-workgroup level) for head g, dims d8 .. d8+7: the chunk's
 // maximum M, sum l and unnormalised O.  The chunk holds at least one key, so
 // M is finite.
-__device__ __forceinline__ void chunk_state(const DecodeSmem& sm, int buf, int g, int d8, float& M, float& lt,
+template <class SM>
+__device__ __forceinline__ void chunk_state(const SM& sm, int buf, int g, int d8, float& M, float& lt,
                                             float (&acc)[8]) {
   M = sm.mm[buf][0][g];
 #pragma unroll
@@ -567,7 +578,8 @@ __device__ __forceinline__ void store_partial(const DecodeParams& p, int b, int 
 // thread t takes head t/16 (+ nthr/16, ...) and dims 8 (t%16) .. +7; the
 // result is the workgroup's partial in slot wc (or, with a single chunk in
 // the plan, the normalised output row).
-__device__ __forceinline__ void merge_chunk(const DecodeParams& p, const DecodeSmem& sm, int buf, int b, int h, int wc,
+template <class SM>
+__device__ __forceinline__ void merge_chunk(const DecodeParams& p, const SM& sm, int buf, int b, int h, int wc,
                                             int t, int nthr) {
   const int G = p.group, d8 = (t & 15) * 8;
   for (int g = t >> 4; g < G; g += nthr >> 4) {
@@ -598,7 +610,8 @@ struct RunMerge {
   float o[4][8];
 };
 
-__device__ __forceinline__ void fold_chunk(const DecodeParams& p, const DecodeSmem& sm, int buf, int lane,
+template <class SM>
+__device__ __forceinline__ void fold_chunk(const DecodeParams& p, const SM& sm, int buf, int lane,
                                            RunMerge& r) {
   const int d8 = (lane & 15) * 8;
 #pragma unroll
@@ -648,13 +661,18 @@ __device__ __forceinline__ const uint8_t* k_row(const DecodeParams& p, int b, in
   }
 }
 
-template <bool BF16, bool PAGED>
-__global__ __launch_bounds__(kThreads, BF16 ? 2 : 1) void decode_partition_kernel(const DecodeParams p) {
+// PW: a dedicated prologue wave beside the 4 streaming waves (any plan);
+// otherwise the 4-wave form for single-chunk workgroups (cpw = 1), whose
+// streaming wave 0 runs the prologue.
+template <bool BF16, bool PAGED, bool PW>
+__global__ __launch_bounds__(PW ? kThreads : kThreads4, BF16 ? 2 : 1) void decode_partition_kernel(const DecodeParams p) {
   using Step = typename std::conditional<BF16, StepBF16, StepF32>::type;
   using QFrag = typename std::conditional<BF16, QFragBF16, QFragF32>::type;
   constexpr int kElem = BF16 ? 2 : 4;
+  constexpr int kPW = PW ? kPrologueWave : 0;        // the wave that runs the prologue
+  constexpr int kNT = PW ? kThreads : kThreads4;
 
-  __shared__ DecodeSmem sm;
+  __shared__ DecodeSmemT<PW ? 2 : 1> sm;
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform branches
@@ -712,7 +730,7 @@ __global__ __launch_bounds__(kThreads, BF16 ? 2 : 1) void decode_partition_kerne
   const bool has_new = (rope || p.k_norm_w != nullptr) && c0 < L && c1 == L;   // range holds slot L-1
   const int kn = has_new ? L - 1 : -1;
   PrologueRegs<BF16> pr;
-  if (wave == kPrologueWave && c0 < L) prologue_issue<BF16>(p, b, h, lane, k_row<PAGED>(p, b, h, max(kn, 0), kElem), pr);
+  if (wave == kPW && c0 < L) prologue_issue<BF16>(p, b, h, lane, k_row<PAGED>(p, b, h, max(kn, 0), kElem), pr);
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");   // keeps the loads above on this side
   __builtin_amdgcn_s_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
@@ -731,7 +749,7 @@ __global__ __launch_bounds__(kThreads, BF16 ? 2 : 1) void decode_partition_kerne
     load_step(A, sl, c0 + s * kStep, c1, n16, q4, sl.page_of(c0 + s * kStep, c1));
     page = sl.page_of(c0 + (s + kStreamWaves) * kStep, c1);
   }
-  if (wave == kPrologueWave) prologue_finish<BF16>(p, sm, pos, lane, rope, has_new, pr);
+  if (wave == kPW) prologue_finish<BF16>(p, sm, pos, lane, rope, has_new, pr);
   __syncthreads();   // q', the new-key score and the tables are in LDS
 
   if (stream) {
@@ -751,8 +769,9 @@ __global__ __launch_bounds__(kThreads, BF16 ? 2 : 1) void decode_partition_kerne
                    n16, q4, page);
         s += kStreamWaves;
       }
-      // ---- this wave's state of chunk j into LDS buffer j % 2
-      const int buf = j & 1;
+      // ---- this wave's state of chunk j into LDS buffer j % 2 (the only one
+      //      in the 4-wave form, whose workgroups hold one chunk)
+      const int buf = PW ? (j & 1) : 0;
       rs.l = sum_xor32(sum_xor16(rs.l));
       if (q4 == 0) {
         sm.mm[buf][wave][n16] = rs.m;
@@ -766,7 +785,7 @@ __global__ __launch_bounds__(kThreads, BF16 ? 2 : 1) void decode_partition_kerne
       }
       __syncthreads();
     }
-  } else {
+  } else if constexpr (PW) {
     // the prologue wave folds chunk j while the streaming waves sweep chunk j+1,
     // then the last chunk, and stores the workgroup's partial
     RunMerge run;
@@ -790,25 +809,25 @@ __global__ __launch_bounds__(kThreads, BF16 ? 2 : 1) void decode_partition_kerne
   // ---- the new key's transformed row replaces the raw one in its cache slot:
   //      every read of that row (the prologue's and the streaming waves' step
   //      holding it) is complete, and no other workgroup reads it
-  if (p.write_new_k && has_new && wave == kPrologueWave && lane < 32) {
+  if (p.write_new_k && has_new && wave == kPW && lane < 32) {
     uint8_t* row = (uint8_t*)k_row<PAGED>(p, b, h, kn, kElem);
     const f32x4 y = *(const f32x4*)&sm.kn[4 * lane];
     if (BF16) *(u32x2*)(row + 8 * lane) = u32x2{pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3])};
     else *(f32x4*)(row + 16 * lane) = y;
   }
   // ---- a single chunk: every thread of the workgroup merges its wave states
-  if (nchunks == 1) merge_chunk(p, sm, 0, b, h, wc, tid, kThreads);
+  if (nchunks == 1) merge_chunk(p, sm, 0, b, h, wc, tid, kNT);
 }
 
 // ----------------------------------------------------------------- merge kernel
 // One workgroup per (q head, sequence): out = sum_c 2^(m_c - M) O_c / sum_c 2^(m_c - M) l_c
 // over the partials of the n = ceil(L / (cpw T)) partition workgroups that
 // hold keys (ADR-0060 section 4).  Thread
-// (group sg, dims 4*d4 .. 4*d4+3) folds chunks sg, sg + 16, ... with a running
-// maximum, kMergeUnroll chunks per batch of loads; the 16 group states are then
+// (group sg, dims 4*d4 .. 4*d4+3) folds chunks sg, sg + 4, ... with a running
+// maximum, kMergeUnroll chunks per batch of loads; the 4 group states are then
 // merged through LDS.
 
-constexpr int kMergeThreads = 512;
+constexpr int kMergeThreads = 128;
 constexpr int kMergeGroups = kMergeThreads / 32;
 constexpr int kMergeUnroll = 8;
 
@@ -905,8 +924,16 @@ template <bool BF16>
 hipError_t launch_partition(const DecodeParams& p, hipStream_t stream) {
   const int wpg = (p.n_split + p.cpw - 1) / p.cpw;
   const dim3 grid(wpg * p.num_kv_heads * p.batch);
-  if (p.block_table != nullptr) return launch_kernel(decode_partition_kernel<BF16, true>, grid, dim3(kThreads), stream, p);
-  return launch_kernel(decode_partition_kernel<BF16, false>, grid, dim3(kThreads), stream, p);
+  if constexpr (BF16) {
+    if (p.cpw == 1 && grid.x >= kMany4) {   // many single-chunk workgroups: two per compute unit
+      if (p.block_table != nullptr)
+        return launch_kernel(decode_partition_kernel<BF16, true, false>, grid, dim3(kThreads4), stream, p);
+      return launch_kernel(decode_partition_kernel<BF16, false, false>, grid, dim3(kThreads4), stream, p);
+    }
+  }
+  if (p.block_table != nullptr)
+    return launch_kernel(decode_partition_kernel<BF16, true, true>, grid, dim3(kThreads), stream, p);
+  return launch_kernel(decode_partition_kernel<BF16, false, true>, grid, dim3(kThreads), stream, p);
 }
 
 }  // namespace
