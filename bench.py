@@ -141,9 +141,13 @@ def summarize_counters(args):
         out["algorithmic_bytes_per_launch"] = args.algorithmic_bytes
         out["traffic_over_algorithmic"] = round(out["traffic_bytes_per_launch"] / args.algorithmic_bytes, 4)
     out["commands"] = [
-        f"cd /tmp && timeout -s KILL 90 rocprofv3 --pmc {c} --output-format csv -d $REPO/gpurun_out/ctr/{tag} -o p "
+        f"cd /tmp && timeout -s KILL 120 rocprofv3 --pmc {c} --output-format csv -d $REPO/{d} -o p "
         f"-- python3 $REPO/bench.py --only {args.workload_arg or args.workload} --eager-calls 3 --copy-probe-mib {mib}"
-        for c, tag in (("FETCH_SIZE", "F"), ("WRITE_SIZE", "W"))]
+        for c, d in (("FETCH_SIZE", os.path.relpath(fetch_dir, ROOT)), ("WRITE_SIZE", os.path.relpath(write_dir, ROOT)))]
+    out["summary_command"] = (f"python3 bench.py --summarize-counters {os.path.relpath(fetch_dir, ROOT)} "
+                              f"{os.path.relpath(write_dir, ROOT)} --workload {args.workload} --kernel {args.kernel} "
+                              f"--workload-arg {args.workload_arg or args.workload} --copy-probe-mib {mib}"
+                              + (f" --algorithmic-bytes {args.algorithmic_bytes}" if args.algorithmic_bytes else ""))
     out["source_files"] = list(sources)
     out["source_sha256"] = source_digest(sources)
     path = counter_file(args.kernel, args.workload)
