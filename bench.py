@@ -126,7 +126,7 @@ def summarize_counters(args):
     out = {"kernel_key": f"{args.kernel}:{args.workload}", "workload": args.workload, "kernel_name_fragment": frag}
     for name, d, counter in (("fetch", fetch_dir, "FETCH_SIZE"), ("write", write_dir, "WRITE_SIZE")):
         rows = read_counter_csv(d, counter)
-        cal = [v for k, g, v in rows if "copy_kernel" in k]
+        cal = [v for k, g, v in rows if k.startswith("(anonymous namespace)::copy_kernel(")]   # the probe copy
         vals = [v for k, g, v in rows if frag in k]
         if not cal or not vals:
             raise SystemExit(f"{d}: no {counter} rows for the probe copy or for {frag}")
