@@ -15,8 +15,9 @@
 //
 // gfx950 mapping (not the pages' design, which targets an NPU / simulator):
 //  * one workgroup = (chunk c, KV head h, sequence b) on a 1-D grid whose
-//    chunks of one (b, h) share an XCD when the group count allows; 4
-//    streaming waves + 1 prologue wave.  Streaming wave w handles 32-key
+//    chunks of one (b, h) share an XCD when the group count allows, the
+//    chunks that hold keys ahead of those past their sequence's end (the
+//    lengths are read on the device); 4 streaming waves + 1 prologue wave.  Streaming wave w handles 32-key
 //    steps w, w+4, ... of the chunk with its own online-softmax state; the 4
 //    states are merged through LDS at the end.
 //  * The prologue wave has its own in-order memory queue: it loads q, the
@@ -32,7 +33,7 @@
 //  * Memory requests of one compute unit are served in issue order, so the
 //    prologue wave issues its small loads (q, norm weights, the new key row)
 //    before the streaming waves start the K/V stream, behind a workgroup
-//    barrier; the sequence length and positions come through scalar loads.
+//    barrier.
 #include "common.hpp"
 
 namespace gqa {
@@ -45,8 +46,7 @@ constexpr int kThreads = (kStreamWaves + 1) * 64;
 // Single-chunk grids of many workgroups run a 4-wave form instead: streaming
 // wave 0 also runs the prologue and one chunk-state buffer suffices, so two
 // workgroups share a compute unit (two waves per SIMD, no register spills) and
-// one's start (length, q rows, prologue) and short-lived empty ranges overlap
-// the other's K/V stream.
+// one's start (lengths, q rows, prologue) overlaps the other's K/V stream.
 constexpr int kThreads4 = kStreamWaves * 64;
 constexpr int kMany4 = 1024;   // grids of at least this many single-chunk workgroups
 constexpr int kStep = 32;        // keys per wave step
@@ -661,6 +661,78 @@ __device__ __forceinline__ const uint8_t* k_row(const DecodeParams& p, int b, in
   }
 }
 
+// Inclusive prefix sum over the 64 lanes of a wave: shifts by 1, 2, 4 and 8
+// lanes inside each 16-lane row (DPP row_shr, zeros shifted in), then the
+// last lane of rows 0 and 2 added to rows 1 and 3 (row_bcast:15), then lane
+// 31 to rows 2 and 3 (row_bcast:31).
+template <int CTRL, int ROWS>
+__device__ __forceinline__ int dpp_int(int v) {
+  return __builtin_amdgcn_update_dpp(0, v, CTRL, ROWS, 0xF, false);
+}
+__device__ __forceinline__ int wave_prefix_sum(int v) {
+  v += dpp_int<0x111, 0xF>(v);
+  v += dpp_int<0x112, 0xF>(v);
+  v += dpp_int<0x114, 0xF>(v);
+  v += dpp_int<0x118, 0xF>(v);
+  v += dpp_int<0x142, 0xA>(v);
+  v += dpp_int<0x143, 0xC>(v);
+  return v;
+}
+
+// Workgroup -> (group, its workgroup wc, the group's clamped length), with
+// every workgroup whose key range holds keys ahead of those past their
+// sequence's end.  The lengths are device data, so the grid still covers
+// every range (ceil(n_split / cpw) per group); a workgroup reads the lengths
+// of the groups it may serve and finds its range by a prefix sum over their
+// live-workgroup counts ceil(L / (split cpw)), one for L = 0 (it writes that
+// group's zero rows when the plan is unsplit).  When the group count is a
+// multiple of 8, XCD x serves groups x, x + 8, ... in that order (workgroup
+// x + 8 s is the s-th of XCD x), so a group's partials stay in one L2 for the
+// merge; otherwise groups are served in order.  Every wave of a workgroup
+// reads the same lengths and reaches the same answer; false for the
+// workgroups past the live ones, which return without touching memory.
+__device__ __forceinline__ bool live_slot(const DecodeParams& p, int lane, int& grp, int& wc, int& len) {
+  const int groups = p.batch * p.num_kv_heads;
+  const int keys = p.split * p.cpw;   // keys per workgroup
+  const bool by_xcd = groups % kXcds == 0;
+  const int first = by_xcd ? (int)(blockIdx.x % kXcds) : 0, stride = by_xcd ? kXcds : 1;
+  const int n = by_xcd ? groups / kXcds : groups;
+  int s = by_xcd ? (int)(blockIdx.x / kXcds) : (int)blockIdx.x;
+  if (p.batch == 1) {   // one length for every group: no prefix sum
+    int L1 = p.seq_lens[0];
+    L1 = L1 < 0 ? 0 : (L1 > p.max_seq ? p.max_seq : L1);
+    const int cnt = L1 == 0 ? 1 : (L1 + keys - 1) / keys;
+    if (s >= n * cnt) return false;
+    grp = first + stride * (s / cnt);
+    wc = s % cnt;
+    len = L1;
+    return true;
+  }
+  for (int base = 0; base < n; base += 64) {
+    const int j = base + lane;
+    int Lj = 0, cnt = 0;
+    if (j < n) {
+      Lj = p.seq_lens[(first + stride * j) / p.num_kv_heads];
+      Lj = Lj < 0 ? 0 : (Lj > p.max_seq ? p.max_seq : Lj);
+      cnt = Lj == 0 ? 1 : (Lj + keys - 1) / keys;
+    }
+    const int incl = wave_prefix_sum(cnt);
+    const unsigned long long hit = __ballot(j < n && s < incl);
+    if (hit != 0) {
+      const int l = (int)__builtin_ctzll(hit);   // the first lane whose prefix passes s
+      const int excl = __builtin_amdgcn_readlane(incl - cnt, l);
+      const int w = s - excl;
+      if (base + l >= n || w < 0 || w >= __builtin_amdgcn_readlane(cnt, l)) return false;   // never taken
+      grp = first + stride * (base + l);
+      wc = w;
+      len = __builtin_amdgcn_readlane(Lj, l);
+      return true;
+    }
+    s -= __builtin_amdgcn_readlane(incl, 63);
+  }
+  return false;
+}
+
 // PW: a dedicated prologue wave beside the 4 streaming waves (any plan);
 // otherwise the 4-wave form for single-chunk workgroups (cpw = 1), whose
 // streaming wave 0 runs the prologue.
@@ -679,19 +751,9 @@ __global__ __launch_bounds__(PW ? kThreads : kThreads4, BF16 ? 2 : 1) void decod
   const int n16 = lane & 15, q4 = lane >> 4;
   const bool direct = p.n_split == 1;
 
-  // ---- workgroup -> (group = (b, h), chunks cf .. cf + cpw - 1)
-  const int groups = p.batch * p.num_kv_heads;
-  const int wpg = (p.n_split + p.cpw - 1) / p.cpw;   // workgroups per group
-  const int bid = blockIdx.x;
-  int grp, wc;
-  if (groups % kXcds == 0) {   // the workgroups of one group on one XCD
-    const int slot = bid / kXcds;
-    grp = bid % kXcds + kXcds * (slot / wpg);
-    wc = slot % wpg;
-  } else {
-    grp = bid / wpg;
-    wc = bid % wpg;
-  }
+  // ---- workgroup -> (group = (b, h), chunks cf .. cf + cpw - 1), live ranges first
+  int grp, wc, L;
+  if (!live_slot(p, lane, grp, wc, L)) return;   // past every live range: nothing to do
   const int b = grp / p.num_kv_heads, h = grp % p.num_kv_heads;
   const int cf = wc * p.cpw;
   const int c0 = cf * p.split;
@@ -723,8 +785,6 @@ __global__ __launch_bounds__(PW ? kThreads : kThreads4, BF16 ? 2 : 1) void decod
   //      their first K/V steps behind them (one memory queue per compute unit)
   const bool stream = wave < kStreamWaves;
   const bool rope = p.rope_theta > 0.0;
-  int L = p.seq_lens[b];   // scalar loads, ahead of any fence
-  L = L < 0 ? 0 : (L > p.max_seq ? p.max_seq : L);
   const double pos = rope ? (double)p.positions[b] : 0.0;
   const int c1 = min(cap, L);
   const bool has_new = (rope || p.k_norm_w != nullptr) && c0 < L && c1 == L;   // range holds slot L-1

@@ -142,6 +142,29 @@ def test_empty_and_clamped_lengths():
         compare(out, ref(inp), ATOL_BF16, f"empty/clamped split {split}")
 
 
+@pytest.mark.parametrize("B,Hq,Hkv,S,split,dtype", [
+    (72, 8, 8, 256, 64, "bf16"),    # 576 groups: 72 per XCD, the 4-wave form
+    (72, 8, 8, 256, 64, "f32"),
+    (67, 5, 1, 128, 32, "bf16"),    # 67 groups, not a multiple of 8: groups served in order
+    (9, 40, 8, 2048, 128, "bf16"),  # several chunks per workgroup
+])
+def test_live_ranges_first_grid(B, Hq, Hkv, S, split, dtype):
+    """The partition grid serves the key ranges that hold keys first, found on
+    the device by a prefix sum over the groups' lengths (in passes of 64
+    groups): empty sequences, lengths on and off chunk boundaries, more than
+    64 groups per pass."""
+    rng = np.random.default_rng(B * 1000 + S)
+    lens = rng.integers(0, S + 1, size=B)
+    lens[::7] = 0
+    lens[1::5] = split * rng.integers(1, S // split + 1, size=len(lens[1::5]))   # whole chunks
+    lens[2::11] = S
+    inp = small(B=B, Hq=Hq, Hkv=Hkv, S=S, dtype=dtype, lens=lens.tolist(), seed=B)
+    log(f"case live-first grid B={B} Hkv={Hkv} S={S} split={split} {dtype}")
+    out = run(inp, dtype, split=split).cpu().numpy()
+    assert np.all(out[lens == 0] == 0.0)
+    compare(out, ref(inp), ATOL_F32 if dtype == "f32" else ATOL_BF16, f"live-first B={B} split={split}")
+
+
 @pytest.mark.parametrize("norm,theta", [(False, 0.0), (True, 0.0), (False, 5e5)])
 def test_prologue_switches(norm, theta):
     for dtype in ("f32", "bf16"):
