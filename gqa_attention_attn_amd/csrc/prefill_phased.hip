@@ -501,6 +501,7 @@ __global__ __launch_bounds__(kAttnThreads, kWavesPerSimd) void attention_kernel(
   __shared__ __attribute__((aligned(16))) uint8_t kt0[kTileBytes], kt1[kTileBytes];
   __shared__ __attribute__((aligned(16))) uint8_t vt0[kTileBytes], vt1[kTileBytes];
   __shared__ double inv_rev[kHeadDim / 2];   // query RoPE: theta^(-2i/128) / (2 pi)
+  __shared__ __attribute__((aligned(16))) uint16_t gam[kHeadDim];   // query norm weights (bf16)
   __shared__ int last_span;                   // this workgroup merges its query block's spans
   LDS_AS uint8_t* const K0 = (LDS_AS uint8_t*)kt0;
   LDS_AS uint8_t* const K1 = (LDS_AS uint8_t*)kt1;
@@ -570,11 +571,13 @@ __global__ __launch_bounds__(kAttnThreads, kWavesPerSimd) void attention_kernel(
   const uint8_t* vslab = vws + slab;
   const uint32_t lane_off = 16u * lane;
 
-  // ---- first tiles requested before the query prologue
-  dma_tile<kTileBytes / 1024>(k0a, kslab + ta * kTileBytes, lane_off, wave);
-  dma_tile<kTileBytes / 1024>(v0a, vslab + ta * kTileBytes, lane_off, wave);
-  if (tb - ta > 1) dma_tile<kTileBytes / 1024>(k1a, kslab + (ta + 1) * kTileBytes, lane_off, wave);
+  // ---- the q rows and the norm weights are requested first; the first tiles'
+  //      copies go out once they have landed, and land during the query
+  //      prologue (loads return in issue order: copies issued first would hold
+  //      the q rows back)
   if (tid < 64 && rope) inv_rev[tid] = rope_inv_freq(tid, p.rope_log2_theta) * 0.15915494309189535;
+  u32x4 gv = {0u, 0u, 0u, 0u};
+  if (tid < 16 && p.q_norm_w) gv = *(const u32x4*)((const uint16_t*)p.q_norm_w + 8 * tid);
 
   // ---- query prologue: lane (n32, hf) owns rows wq0 + n32 and wq0 + 32 + n32
   //      of head hq, dims [32hf, 32hf+32) and [64+32hf, 64+32hf+32)
@@ -596,8 +599,18 @@ __global__ __launch_bounds__(kAttnThreads, kWavesPerSimd) void attention_kernel(
         for (int j = 0; j < 4; ++j) qlo[rb][j] = qhi[rb][j] = u32x4{0, 0, 0, 0};
       }
     }
-    __builtin_amdgcn_s_waitcnt(0);   // this thread's tile copies (and q rows) have landed
-    __syncthreads();                 // tables, K'_0, K'_1, V_0
+    __builtin_amdgcn_s_waitcnt(0);   // this thread's q rows and table entries have landed
+    if (tid < 16 && p.q_norm_w) *(u32x4*)&gam[8 * tid] = gv;
+    dma_tile<kTileBytes / 1024>(k0a, kslab + ta * kTileBytes, lane_off, wave);
+    dma_tile<kTileBytes / 1024>(v0a, vslab + ta * kTileBytes, lane_off, wave);
+    if (tb - ta > 1) dma_tile<kTileBytes / 1024>(k1a, kslab + (ta + 1) * kTileBytes, lane_off, wave);
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // this wave's table and norm-weight writes are done
+    // the tables are visible to every wave; no wait for the tile copies here
+    // (the wavefront-scope fences keep LDS accesses on their side of the
+    // barrier without waiting for outstanding loads)
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     const uint16_t* g = (const uint16_t*)p.q_norm_w;
 #pragma unroll
     for (int rb = 0; rb < kRB; ++rb) {
@@ -625,8 +638,8 @@ __global__ __launch_bounds__(kAttnThreads, kWavesPerSimd) void attention_kernel(
           xh[e] = bf16_elem(qhi[rb][j], e);
         }
         if (g) {
-          const u32x4 glo = *(const u32x4*)(g + 32 * hf + 8 * j);
-          const u32x4 ghi = *(const u32x4*)(g + 64 + 32 * hf + 8 * j);
+          const u32x4 glo = *(const u32x4*)&gam[32 * hf + 8 * j];
+          const u32x4 ghi = *(const u32x4*)&gam[64 + 32 * hf + 8 * j];
 #pragma unroll
           for (int e = 0; e < 8; ++e) {
             xl[e] *= r * bf16_elem(glo, e);
@@ -668,6 +681,8 @@ __global__ __launch_bounds__(kAttnThreads, kWavesPerSimd) void attention_kernel(
   }
 
   f32x16 sa[kRB], sb[kRB];
+  __builtin_amdgcn_s_waitcnt(0);   // this thread's tile copies have landed
+  __syncthreads();                 // K'_0, K'_1, V_0
   if (wc.wtiles > ta) {   // scores and row maxima of tile ta (every row sees the span's first key: m is finite)
     const float zero[kRB] = {};
     qk_tile(sa, K0, qf, n32, hf, zero);
