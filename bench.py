@@ -701,15 +701,15 @@ def main():
         del t, call
         torch.cuda.empty_cache()
 
-        for bs in (0, 64):
-            t, call, cflops = prefill_chunk_case(ctx, bs=bs)
+        for key, past, chunk, bs in (("prefill_chunk", 3072, 1024, 0), ("prefill_chunk_paged", 3072, 1024, 64),
+                                     ("prefill_chunk_short", 4000, 96, 0)):
+            t, call, cflops = prefill_chunk_case(ctx, past, chunk, bs=bs)
             us_c = 1000.0 * graph_time_ms(torch, call, pk, max(2, W // 5)) / pk
-            key = "prefill_chunk" + ("_paged" if bs else "")
             tf_c = cflops / (us_c * 1e-6) / 1e12
-            extra[key] = {"workload": "qwen3_14b_prefill_chunk_3072_cached_1024_new", "block_size": bs,
+            extra[key] = {"workload": f"qwen3_14b_prefill_chunk_{past}_cached_{chunk}_new", "block_size": bs,
                           "us_per_call": round(us_c, 2), "tflops": round(tf_c, 2),
                           "frac_of_bf16_peak": round(tf_c / BF16_PEAK_TFLOPS, 4), "algorithmic_flops": cflops}
-            log(f"[bench] {key} (3072 cached + 1024 new) {us_c:.1f} us -> {tf_c:.1f} TFLOP/s")
+            log(f"[bench] {key} ({past} cached + {chunk} new) {us_c:.1f} us -> {tf_c:.1f} TFLOP/s")
             del t, call
             torch.cuda.empty_cache()
 

@@ -749,10 +749,12 @@ __global__ __launch_bounds__(kAttnThreads, kWavesPerSimd) void attention_kernel(
 // are used only when the grid has fewer than 384 workgroups (1.5 per compute
 // unit), where it cannot fill the GPU: a chunk after a long cached prefix,
 // or one sequence with few heads.  Spans are then sized for about 640 items
-// (2.5 workgroups per compute unit), at least 32 tiles and at most 16 per
+// (2.5 workgroups per compute unit), at least 16 tiles and at most 16 per
 // block.  Measured on Qwen3-14B shapes: a 1024-token chunk after 3072
 // cached tokens takes 134 us unsplit, 119 us in 2 spans, 134 us in 3; a
-// 96-token chunk after 4000, 104 us unsplit, 66 in 2 spans, 45 in 4; the
+// 96-token chunk after 4000, 104 us unsplit, 66 in 2 spans, 45 in 4, 41 in
+// 8 (16 tiles per span; 8 tiles per span, 16 spans: 44 us, the last span's
+// merge of 16 partials costing more than the shorter spans save); the
 // 4096-token prefill (1280 workgroups) is not split, splitting its longest
 // blocks made it 8 % slower.
 struct SplitPlan {
@@ -772,7 +774,7 @@ SplitPlan split_plan(int batch, int num_q_heads, int max_seq, int max_chunk, boo
   int longest = 0;
   for (int qb = 0; qb < sp.n_qblocks; ++qb) longest = std::max(longest, est_block_tiles(max_seq, max_chunk, causal, qb));
   const int64_t items = (int64_t)batch * num_q_heads * sp.n_qblocks;
-  sp.span_tiles = (int)std::max<int64_t>({32, ((int64_t)longest * items + 639) / 640, (tiles + 15) / 16});
+  sp.span_tiles = (int)std::max<int64_t>({16, ((int64_t)longest * items + 639) / 640, (tiles + 15) / 16});
   if (items < 384 && longest > sp.span_tiles) sp.n_spans = (tiles + sp.span_tiles - 1) / sp.span_tiles;
   return sp;
 }

@@ -121,6 +121,19 @@ def test_qwen3_chunk_3072_plus_1024_full():
     compare(out, ref(c), ATOL, "qwen3 chunk 3072+1024, all heads and rows")
 
 
+@pytest.mark.parametrize("past,chunk", [(4000, 96), (3968, 128)])
+def test_qwen3_short_chunk_after_long_prefix_full(past, chunk):
+    # a short chunk after a long cached prefix: few query blocks, so each
+    # block's key range is split over several workgroups whose partials the
+    # last one merges; every element, out pre-filled with NaN
+    torch = require_gpu()
+    c = make(B=1, Hq=40, Hkv=8, S=past + chunk, Tmax=chunk, past=[past], chunk=[chunk], seed=67)
+    log(f"case chunked prefill qwen3 {past}+{chunk} (out pre-filled with NaN)")
+    out_t = torch.full((1, 40, chunk, 128), float("nan"), dtype=torch.float32, device="cuda")
+    out = run(c, out=out_t)
+    compare(out, ref(c), ATOL, f"qwen3 chunk {past}+{chunk}, all heads and rows")
+
+
 @pytest.mark.parametrize("bs", [16, 64, 256])
 def test_paged_chunk_equals_contiguous_bitwise(bs):
     torch = require_gpu()

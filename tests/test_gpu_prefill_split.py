@@ -4,7 +4,7 @@ Attention Kernel (Llama3-70B)" section 4: partials of disjoint key ranges
 combine by the log-sum-exp merge; the last workgroup of a block merges).
 
 The split is taken when the grid has fewer than 384 workgroups (a single
-sequence or few heads here), with key spans of at least 32 tiles of 32 keys;
+sequence or few heads here), with key spans of at least 16 tiles of 32 keys;
 blocks that see more keys than one span are split.  Checked against the fp64 oracle on every
 output element (bf16 inputs, fp16 products, f32 accumulation: max |err| <=
 1e-2), against the single-kernel path (which never splits), bitwise between
