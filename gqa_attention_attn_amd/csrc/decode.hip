@@ -15,9 +15,11 @@
 //
 // gfx950 mapping (not the pages' design, which targets an NPU / simulator):
 //  * one workgroup = (chunk c, KV head h, sequence b) on a 1-D grid whose
-//    chunks of one (b, h) share an XCD when the group count allows, the
-//    chunks that hold keys ahead of those past their sequence's end (the
-//    lengths are read on the device); 4 streaming waves + 1 prologue wave.  Streaming wave w handles 32-key
+//    chunks of one (b, h) share an XCD when the group count allows; in a
+//    batch the chunks that hold keys come ahead of those past their
+//    sequence's end (the lengths are read on the device), a single
+//    sequence's map is static so that its q rows are requested while its
+//    length is read; 4 streaming waves + 1 prologue wave.  Streaming wave w handles 32-key
 //    steps w, w+4, ... of the chunk with its own online-softmax state; the 4
 //    states are merged through LDS at the end.
 //  * The prologue wave has its own in-order memory queue: it loads q, the
@@ -438,9 +440,10 @@ struct PrologueRegs {
 };
 
 // Branch-free: every lane fetches valid rows, so no fetch is waited on here.
+// The q rows and norm weights (prologue_issue_q) need only the group; the new
+// key row (prologue_issue_k) needs the length.
 template <bool BF16>
-__device__ __forceinline__ void prologue_issue(const DecodeParams& p, int b, int h, int lane,
-                                               const uint8_t* krow, PrologueRegs<BF16>& pr) {
+__device__ __forceinline__ void prologue_issue_q(const DecodeParams& p, int b, int h, int lane, PrologueRegs<BF16>& pr) {
   constexpr int kElem = BF16 ? 2 : 4;
   const int r4 = lane >> 4, c16 = lane & 15;
   const int G = p.group;
@@ -452,7 +455,10 @@ __device__ __forceinline__ void prologue_issue(const DecodeParams& p, int b, int
   }
   pr.gq = fetch_half_row<BF16>(p.q_norm_w != nullptr ? p.q_norm_w : p.q, c16);
   pr.gk = fetch_half_row<BF16>(p.k_norm_w != nullptr ? p.k_norm_w : p.q, c16);
-  pr.y = fetch_half_row<BF16>(krow, c16);
+}
+template <bool BF16>
+__device__ __forceinline__ void prologue_issue_k(const uint8_t* krow, int lane, PrologueRegs<BF16>& pr) {
+  pr.y = fetch_half_row<BF16>(krow, lane & 15);
 }
 
 template <bool BF16, class SM>
@@ -679,18 +685,20 @@ __device__ __forceinline__ int wave_prefix_sum(int v) {
   return v;
 }
 
-// Workgroup -> (group, its workgroup wc, the group's clamped length), with
-// every workgroup whose key range holds keys ahead of those past their
-// sequence's end.  The lengths are device data, so the grid still covers
-// every range (ceil(n_split / cpw) per group); a workgroup reads the lengths
-// of the groups it may serve and finds its range by a prefix sum over their
-// live-workgroup counts ceil(L / (split cpw)), one for L = 0 (it writes that
-// group's zero rows when the plan is unsplit).  When the group count is a
-// multiple of 8, XCD x serves groups x, x + 8, ... in that order (workgroup
-// x + 8 s is the s-th of XCD x), so a group's partials stay in one L2 for the
-// merge; otherwise groups are served in order.  Every wave of a workgroup
-// reads the same lengths and reaches the same answer; false for the
-// workgroups past the live ones, which return without touching memory.
+// Workgroup -> (group, its workgroup wc, the group's clamped length) for a
+// batch of several sequences, with every workgroup whose key range holds keys
+// ahead of those past their sequence's end.  The lengths are device data, so
+// the grid still covers every range (ceil(n_split / cpw) per group); a
+// workgroup reads the lengths of the groups it may serve and finds its range
+// by a prefix sum over their live-workgroup counts ceil(L / (split cpw)), one
+// for L = 0 (it writes that group's zero rows when the plan is unsplit).  When
+// the group count is a multiple of 8, XCD x serves groups x, x + 8, ... in
+// that order (workgroup x + 8 s is the s-th of XCD x), so a group's partials
+// stay in one L2 for the merge; otherwise groups are served in order.  Every
+// wave of a workgroup reads the same lengths and reaches the same answer;
+// false for the workgroups past the live ones, which return without touching
+// memory.  (A batch of one maps its workgroups statically, without the
+// lengths.)
 __device__ __forceinline__ bool live_slot(const DecodeParams& p, int lane, int& grp, int& wc, int& len) {
   const int groups = p.batch * p.num_kv_heads;
   const int keys = p.split * p.cpw;   // keys per workgroup
@@ -698,16 +706,6 @@ __device__ __forceinline__ bool live_slot(const DecodeParams& p, int lane, int& 
   const int first = by_xcd ? (int)(blockIdx.x % kXcds) : 0, stride = by_xcd ? kXcds : 1;
   const int n = by_xcd ? groups / kXcds : groups;
   int s = by_xcd ? (int)(blockIdx.x / kXcds) : (int)blockIdx.x;
-  if (p.batch == 1) {   // one length for every group: no prefix sum
-    int L1 = p.seq_lens[0];
-    L1 = L1 < 0 ? 0 : (L1 > p.max_seq ? p.max_seq : L1);
-    const int cnt = L1 == 0 ? 1 : (L1 + keys - 1) / keys;
-    if (s >= n * cnt) return false;
-    grp = first + stride * (s / cnt);
-    wc = s % cnt;
-    len = L1;
-    return true;
-  }
   for (int base = 0; base < n; base += 64) {
     const int j = base + lane;
     int Lj = 0, cnt = 0;
@@ -751,9 +749,25 @@ __global__ __launch_bounds__(PW ? kThreads : kThreads4, BF16 ? 2 : 1) void decod
   const int n16 = lane & 15, q4 = lane >> 4;
   const bool direct = p.n_split == 1;
 
-  // ---- workgroup -> (group = (b, h), chunks cf .. cf + cpw - 1), live ranges first
+  // ---- workgroup -> (group = (b, h), chunks cf .. cf + cpw - 1)
   int grp, wc, L;
-  if (!live_slot(p, lane, grp, wc, L)) return;   // past every live range: nothing to do
+  PrologueRegs<BF16> pr;
+  if (p.batch == 1) {
+    // one length for every group: a static map (the workgroups of a group
+    // consecutive, on one XCD when the group count allows), so the prologue
+    // wave requests the q rows and norm weights while the length is read
+    const int groups = p.num_kv_heads;
+    const bool by_xcd = groups % kXcds == 0;
+    const int s = by_xcd ? (int)(blockIdx.x / kXcds) : (int)blockIdx.x;
+    grp = (by_xcd ? (int)(blockIdx.x % kXcds) : 0) + (by_xcd ? kXcds : 1) * (s / p.wpg);
+    wc = s % p.wpg;
+    if (wave == kPW) prologue_issue_q<BF16>(p, 0, grp, lane, pr);
+    L = p.seq_lens[0];
+    L = L < 0 ? 0 : (L > p.max_seq ? p.max_seq : L);
+    if (wc > 0 && wc * p.split * p.cpw >= L) return;   // past the sequence (wc = 0 writes an empty one's zero rows)
+  } else {
+    if (!live_slot(p, lane, grp, wc, L)) return;   // past every live range: nothing to do
+  }
   const int b = grp / p.num_kv_heads, h = grp % p.num_kv_heads;
   const int cf = wc * p.cpw;
   const int c0 = cf * p.split;
@@ -789,8 +803,10 @@ __global__ __launch_bounds__(PW ? kThreads : kThreads4, BF16 ? 2 : 1) void decod
   const int c1 = min(cap, L);
   const bool has_new = (rope || p.k_norm_w != nullptr) && c0 < L && c1 == L;   // range holds slot L-1
   const int kn = has_new ? L - 1 : -1;
-  PrologueRegs<BF16> pr;
-  if (wave == kPW && c0 < L) prologue_issue<BF16>(p, b, h, lane, k_row<PAGED>(p, b, h, max(kn, 0), kElem), pr);
+  if (wave == kPW && c0 < L) {
+    if (p.batch != 1) prologue_issue_q<BF16>(p, b, h, lane, pr);
+    prologue_issue_k<BF16>(k_row<PAGED>(p, b, h, max(kn, 0), kElem), lane, pr);
+  }
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");   // keeps the loads above on this side
   __builtin_amdgcn_s_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
