@@ -165,6 +165,23 @@ def test_live_ranges_first_grid(B, Hq, Hkv, S, split, dtype):
     compare(out, ref(inp), ATOL_F32 if dtype == "f32" else ATOL_BF16, f"live-first B={B} split={split}")
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("L", [0, 1, 31, 128, 129, 1000, 2047, 2048])
+def test_single_sequence_lengths(dtype, L):
+    """A batch of one maps its partition workgroups statically (KV head, chunk
+    range) and returns those past the length: empty, one-key, partial-step,
+    chunk-boundary and full lengths, unsplit, single-chunk and multi-chunk
+    workgroups (split 32 over 2048 keys: several chunks per workgroup)."""
+    inp = small(B=1, Hq=40, Hkv=8, S=2048, dtype=dtype, lens=[L], seed=L + 5)
+    r = ref(inp)
+    for split in (0, 32, 128, 2048):
+        log(f"case single sequence L={L} split={split} {dtype}")
+        out = run(inp, dtype, split=split).cpu().numpy()
+        if L == 0:
+            assert np.all(out == 0.0)
+        compare(out, r, ATOL_F32 if dtype == "f32" else ATOL_BF16, f"B=1 L={L} split={split}")
+
+
 @pytest.mark.parametrize("norm,theta", [(False, 0.0), (True, 0.0), (False, 5e5)])
 def test_prologue_switches(norm, theta):
     for dtype in ("f32", "bf16"):

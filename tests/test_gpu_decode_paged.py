@@ -95,6 +95,19 @@ def test_paged_many_chunks_per_workgroup():
         compare(run_paged(c, "bf16", split), ref(c), ATOL["bf16"], f"paged multi-chunk split={split}")
 
 
+@pytest.mark.parametrize("L", [0, 1, 65, 3000, 4096])
+def test_paged_single_sequence_lengths(L):
+    # a batch of one: workgroups past the length return before any page is
+    # looked up (table entries past the last block are -1)
+    c = paged(B=1, Hq=40, Hkv=8, S=4096, bs=64, dtype="bf16", lens=[L], seed=75 + L)
+    for split in (0, 128, 512):
+        log(f"case paged single sequence L={L} split={split}")
+        out = run_paged(c, "bf16", split)
+        if L == 0:
+            assert np.all(out == 0.0)
+        compare(out, ref(c), ATOL["bf16"], f"paged B=1 L={L} split={split}")
+
+
 def test_paged_write_new_k_lands_in_its_page():
     torch = require_gpu()
     c = paged(B=3, Hq=10, Hkv=2, S=512, bs=64, dtype="bf16", lens=[512, 65, 64], seed=73)
