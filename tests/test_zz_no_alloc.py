@@ -4,7 +4,8 @@ nothing (its split-KV partials live in the library's static device array).
 Through the C ABI: two calls in a row, the second with a smaller input, each
 equal bitwise to gqa_attn_decode on the same inputs (same plan, same kernels)
 and within the bf16 bound (1e-2) of the fp64 oracle; a plan whose partials
-exceed the array is refused on the host.
+exceed the array is refused on the host; a call captured in a HIP graph and
+replayed, each replay bitwise equal to the eager decode.
 """
 
 import numpy as np
@@ -66,3 +67,46 @@ def test_decode_static_refuses_oversized_plans():
     fake = 1 << 20
     assert G.gqa_attn_decode_static(d, fake, fake, fake, fake, fake, None, None, 5e5, fake,
                                     None) == G.GQA_ERR_SCRATCH
+
+
+def test_decode_static_under_graph_capture():
+    """The callers this entry point is for may capture it: a HIP graph of one
+    call, replayed with new q rows written eagerly between replays (and a
+    synchronisation after each), every replay bitwise equal to an eager
+    gqa_attn_decode on the same inputs."""
+    torch = require_gpu()
+    w = synth.QWEN3_DECODE
+    inp = synth.make_decode(w)
+    bf = torch.bfloat16
+    q, k, v = dev(inp["q"], bf), dev(inp["k"], bf), dev(inp["v"], bf)
+    qw, kw = dev(inp["q_norm_w"], bf), dev(inp["k_norm_w"], bf)
+    sl, pos = ints(inp["seq_lens"]), ints(inp["positions"])
+    out_g = torch.full(tuple(q.shape), float("nan"), device="cuda")
+    desc = G.decode_desc(q, k, v, out_g, w.split_tokens, w.eps)
+    st, need = G.gqa_attn_decode_workspace_size(desc)
+    assert st == G.GQA_OK
+    ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+    p = lambda t: None if t is None else t.data_ptr()
+    call = lambda o, stream: G.gqa_attn_decode_static(desc, p(q), p(k), p(v), p(sl), p(pos), p(qw), p(kw),
+                                                      w.rope_theta, p(o), stream)
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):   # one eager call first
+        assert call(out_g, s.cuda_stream) == G.GQA_OK
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=s):
+        assert call(out_g, s.cuda_stream) == G.GQA_OK
+    rng = np.random.default_rng(91)
+    for r in range(4):
+        log(f"case decode_static graph replay {r}")
+        q.copy_(dev(synth.bf16_round(rng.standard_normal(tuple(q.shape)).astype(np.float32)), bf))
+        torch.cuda.synchronize()
+        out_g.fill_(float("nan"))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        out_e = torch.full(tuple(q.shape), float("nan"), device="cuda")
+        assert G.gqa_attn_decode(desc, p(q), p(k), p(v), p(sl), p(pos), p(qw), p(kw), w.rope_theta, p(out_e),
+                                 p(ws), need, torch.cuda.current_stream().cuda_stream) == G.GQA_OK
+        torch.cuda.synchronize()
+        assert torch.equal(out_g, out_e), f"graph replay {r} differs from the eager decode"
