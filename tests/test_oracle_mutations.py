@@ -116,6 +116,7 @@ def test_unmutated_oracle_passes_every_pin():
     assert first_failure(O) is None
 
 
+@pytest.mark.filterwarnings("ignore::RuntimeWarning")   # a mutant may compute inf - inf
 @pytest.mark.parametrize("name,edits", MUTATIONS, ids=[m[0] for m in MUTATIONS])
 def test_planted_mistake_fails_a_pin(name, edits):
     caught = first_failure(mutant(edits))
