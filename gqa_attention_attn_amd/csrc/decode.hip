@@ -685,8 +685,8 @@ __device__ __forceinline__ int wave_prefix_sum(int v) {
   return v;
 }
 
-// Workgroup -> (group, its workgroup wc, the group's clamped length) for a
-// batch of several sequences, with every workgroup whose key range holds keys
+// Workgroup -> (group, its workgroup wc, the group's clamped length and its
+// sequence's position) for a batch of several sequences, with every workgroup whose key range holds keys
 // ahead of those past their sequence's end.  The lengths are device data, so
 // the grid still covers every range (ceil(n_split / cpw) per group); a
 // workgroup reads the lengths of the groups it may serve and finds its range
@@ -697,9 +697,10 @@ __device__ __forceinline__ int wave_prefix_sum(int v) {
 // stay in one L2 for the merge; otherwise groups are served in order.  Every
 // wave of a workgroup reads the same lengths and reaches the same answer;
 // false for the workgroups past the live ones, which return without touching
-// memory.  (A batch of one maps its workgroups statically, without the
-// lengths.)
-__device__ __forceinline__ bool live_slot(const DecodeParams& p, int lane, int& grp, int& wc, int& len) {
+// memory.  The positions come with the lengths (vector loads: a scalar load
+// issued behind a compute unit's K/V stream returns late).  (A batch of one
+// maps its workgroups statically, without the lengths.)
+__device__ __forceinline__ bool live_slot(const DecodeParams& p, int lane, int& grp, int& wc, int& len, int& posv) {
   const int groups = p.batch * p.num_kv_heads;
   const int keys = p.split * p.cpw;   // keys per workgroup
   const bool by_xcd = groups % kXcds == 0;
@@ -708,9 +709,10 @@ __device__ __forceinline__ bool live_slot(const DecodeParams& p, int lane, int& 
   int s = by_xcd ? (int)(blockIdx.x / kXcds) : (int)blockIdx.x;
   for (int base = 0; base < n; base += 64) {
     const int j = base + lane;
-    int Lj = 0, cnt = 0;
+    int Lj = 0, cnt = 0, Pj = 0;
     if (j < n) {
       Lj = p.seq_lens[(first + stride * j) / p.num_kv_heads];
+      Pj = p.positions[(first + stride * j) / p.num_kv_heads];
       Lj = Lj < 0 ? 0 : (Lj > p.max_seq ? p.max_seq : Lj);
       cnt = Lj == 0 ? 1 : (Lj + keys - 1) / keys;
     }
@@ -724,6 +726,7 @@ __device__ __forceinline__ bool live_slot(const DecodeParams& p, int lane, int& 
       grp = first + stride * (base + l);
       wc = w;
       len = __builtin_amdgcn_readlane(Lj, l);
+      posv = __builtin_amdgcn_readlane(Pj, l);
       return true;
     }
     s -= __builtin_amdgcn_readlane(incl, 63);
@@ -750,7 +753,7 @@ __global__ __launch_bounds__(PW ? kThreads : kThreads4, BF16 ? 2 : 1) void decod
   const bool direct = p.n_split == 1;
 
   // ---- workgroup -> (group = (b, h), chunks cf .. cf + cpw - 1)
-  int grp, wc, L;
+  int grp, wc, L, posv = 0;
   PrologueRegs<BF16> pr;
   if (p.batch == 1) {
     // one length for every group: a static map (the workgroups of a group
@@ -766,7 +769,7 @@ __global__ __launch_bounds__(PW ? kThreads : kThreads4, BF16 ? 2 : 1) void decod
     L = L < 0 ? 0 : (L > p.max_seq ? p.max_seq : L);
     if (wc > 0 && wc * p.split * p.cpw >= L) return;   // past the sequence (wc = 0 writes an empty one's zero rows)
   } else {
-    if (!live_slot(p, lane, grp, wc, L)) return;   // past every live range: nothing to do
+    if (!live_slot(p, lane, grp, wc, L, posv)) return;   // past every live range: nothing to do
   }
   const int b = grp / p.num_kv_heads, h = grp % p.num_kv_heads;
   const int cf = wc * p.cpw;
@@ -799,7 +802,7 @@ __global__ __launch_bounds__(PW ? kThreads : kThreads4, BF16 ? 2 : 1) void decod
   //      their first K/V steps behind them (one memory queue per compute unit)
   const bool stream = wave < kStreamWaves;
   const bool rope = p.rope_theta > 0.0;
-  const double pos = rope ? (double)p.positions[b] : 0.0;
+  const double pos = rope ? (double)(p.batch == 1 ? p.positions[0] : posv) : 0.0;
   const int c1 = min(cap, L);
   const bool has_new = (rope || p.k_norm_w != nullptr) && c0 < L && c1 == L;   // range holds slot L-1
   const int kn = has_new ? L - 1 : -1;
