@@ -441,7 +441,9 @@ struct PrologueRegs {
 
 // Branch-free: every lane fetches valid rows, so no fetch is waited on here.
 // The q rows and norm weights (prologue_issue_q) need only the group; the new
-// key row (prologue_issue_k) needs the length.
+// key row (prologue_issue_k) needs the length and is fetched only by the
+// workgroup whose range holds it, so that the others' q' waits on the q rows
+// alone.
 template <bool BF16>
 __device__ __forceinline__ void prologue_issue_q(const DecodeParams& p, int b, int h, int lane, PrologueRegs<BF16>& pr) {
   constexpr int kElem = BF16 ? 2 : 4;
@@ -766,6 +768,7 @@ __global__ __launch_bounds__(PW ? kThreads : kThreads4, BF16 ? 2 : 1) void decod
     wc = s % p.wpg;
     if (wave == kPW) prologue_issue_q<BF16>(p, 0, grp, lane, pr);
     L = p.seq_lens[0];
+    posv = p.positions[0];   // with the length: issued after it, it would queue behind the K/V stream
     L = L < 0 ? 0 : (L > p.max_seq ? p.max_seq : L);
     if (wc > 0 && wc * p.split * p.cpw >= L) return;   // past the sequence (wc = 0 writes an empty one's zero rows)
   } else {
@@ -802,13 +805,13 @@ __global__ __launch_bounds__(PW ? kThreads : kThreads4, BF16 ? 2 : 1) void decod
   //      their first K/V steps behind them (one memory queue per compute unit)
   const bool stream = wave < kStreamWaves;
   const bool rope = p.rope_theta > 0.0;
-  const double pos = rope ? (double)(p.batch == 1 ? p.positions[0] : posv) : 0.0;
+  const double pos = rope ? (double)posv : 0.0;
   const int c1 = min(cap, L);
   const bool has_new = (rope || p.k_norm_w != nullptr) && c0 < L && c1 == L;   // range holds slot L-1
   const int kn = has_new ? L - 1 : -1;
   if (wave == kPW && c0 < L) {
     if (p.batch != 1) prologue_issue_q<BF16>(p, b, h, lane, pr);
-    prologue_issue_k<BF16>(k_row<PAGED>(p, b, h, max(kn, 0), kElem), lane, pr);
+    if (has_new) prologue_issue_k<BF16>(k_row<PAGED>(p, b, h, kn, kElem), lane, pr);
   }
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");   // keeps the loads above on this side
   __builtin_amdgcn_s_barrier();
