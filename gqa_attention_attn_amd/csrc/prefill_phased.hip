@@ -422,7 +422,9 @@ struct WaveCtx {
 
 // Tile t of the wave (t < wtiles): the scores of tile t+1 (K'_{t+1} in
 // kt_next) go to s_next beside the exponentials of s_cur (tile t), then P V of
-// tile t (V_t in vt) beside the row maxima of tile t+1.  On the wave's last
+// tile t (V_t in vt) beside the row maxima of tile t+1 (taken before the
+// diagonal tiles' masking branch, so that they share the products' basic
+// block, and taken again after it on those tiles).  On the wave's last
 // tile the scores and maxima are computed from whatever kt_next holds and
 // discarded, which keeps the loop body one basic block apart from the masking
 // of the diagonal tiles and the (rare) rescale.  The scores of tile t+1 are
@@ -440,15 +442,16 @@ __device__ __forceinline__ void wave_tile(int t, f32x16 (&s_cur)[kRB], f32x16 (&
   for (int rb = 0; rb < kRB; ++rb) neg_m[rb] = -ws.m[rb];
   qk_tile(s_next, kt_next, qf, n32, hf, neg_m);
   softmax_exp(s_cur, ws.l, pf);
+  float mx[kRB];   // row maxima of tile t+1 less m, in the block of the products
+  row_max(s_next, mx);
   pv_tile(ws.o, vt, pf, lane);
   const int ks = (t + 1) * kBN;
-  if (w.needs_mask(ks)) {
+  if (w.needs_mask(ks)) {   // a diagonal tile: its maxima again, after the mask
     int lim[kRB];
     w.limits(ks, hf, lim);
     apply_mask(s_next, lim);
+    row_max(s_next, mx);
   }
-  float mx[kRB];   // row maxima of tile t+1 less m
-  row_max(s_next, mx);
   bool grow = false;
 #pragma unroll
   for (int rb = 0; rb < kRB; ++rb) grow = grow || mx[rb] > kLazyRescale;
