@@ -187,8 +187,10 @@ struct Slab {
 
 // Loads of one step.  FULL: every row of the step is below kend, no
 // predication.  !FULL (the last step of a chunk): rows at or past kend are
-// replaced by row kend-1 (always valid) and the loaded values are zeroed, so
-// rows past the sequence are never read and the code stays branch-free.
+// replaced by row kend-1 (always valid), so rows past the sequence are never
+// read.  Their values stay as loaded: the scores of keys at or past kend are
+// masked to -inf, which makes their P exactly 0, so nothing waits on these
+// loads here and both forms leave the same loads in flight.
 template <bool FULL, class SL>
 __device__ __forceinline__ void load_k(StepBF16& st, const SL& sl, int key0, int kend, int n16, int q4, int page) {
   int rel;
@@ -201,10 +203,7 @@ __device__ __forceinline__ void load_k(StepBF16& st, const SL& sl, int key0, int
                               : (uint32_t)((ok ? key : kend - 1) - key0 + rel) * sl.kss + 64u * q4;
     const u32x4* src = (const u32x4*)(kb + off);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const u32x4 x = src[j];
-      st.k[gi][j] = ok ? x : u32x4{0, 0, 0, 0};
-    }
+    for (int j = 0; j < 4; ++j) st.k[gi][j] = src[j];
   }
 }
 
@@ -218,8 +217,7 @@ __device__ __forceinline__ void load_v(StepBF16& st, const SL& sl, int key0, int
     const bool ok = FULL || key < kend;
     const uint32_t off = FULL ? (uint32_t)(rel + vkey_t(t)) * sl.vss + sl.vlane
                               : (uint32_t)((ok ? key : kend - 1) - key0 + rel) * sl.vss + 16u * n16;
-    const u32x4 x = *(const u32x4*)(vb + off);
-    st.v[t] = ok ? x : u32x4{0, 0, 0, 0};
+    st.v[t] = *(const u32x4*)(vb + off);
   }
 }
 
@@ -235,10 +233,7 @@ __device__ __forceinline__ void load_k(StepF32& st, const SL& sl, int key0, int 
                               : (uint32_t)((ok ? key : kend - 1) - key0 + rel) * sl.kss + 128u * q4;
     const f32x4* src = (const f32x4*)(kb + off);
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const f32x4 x = src[j];
-      st.k[gi][j] = ok ? x : f32x4{0.f, 0.f, 0.f, 0.f};
-    }
+    for (int j = 0; j < 8; ++j) st.k[gi][j] = src[j];
   }
 }
 
@@ -253,9 +248,8 @@ __device__ __forceinline__ void load_v(StepF32& st, const SL& sl, int key0, int 
     const uint32_t off = FULL ? (uint32_t)(rel + 16 * (e >> 2) + (e & 3)) * sl.vss + sl.vlane
                               : (uint32_t)((ok ? key : kend - 1) - key0 + rel) * sl.vss + 32u * n16;
     const f32x4* src = (const f32x4*)(vb + off);
-    const f32x4 x0 = src[0], x1 = src[1];
-    st.v[e][0] = ok ? x0 : f32x4{0.f, 0.f, 0.f, 0.f};
-    st.v[e][1] = ok ? x1 : f32x4{0.f, 0.f, 0.f, 0.f};
+    st.v[e][0] = src[0];
+    st.v[e][1] = src[1];
   }
 }
 
@@ -375,19 +369,25 @@ __device__ __forceinline__ void accumulate_pv(const StepF32& st, const float (&p
 }
 
 // One 32-key step from buffer st; afterwards st is refilled with the step at
-// next_key0 (if next_key0 < kend): its K half right after the QK^T MFMAs
-// have consumed st.k, its V half right after P V has consumed st.v.
+// Refill (kRefill, or kRefillIfMore when next_key0 < kend): the step at
+// next_key0 is requested into st, its K half right after the QK^T MFMAs have
+// consumed st.k, its V half right after P V has consumed st.v.  (The bf16
+// sweep gives a wave's last step no refill and leaves the step loop with it,
+// so on the loop's back edge K and V are always in flight in that order and
+// the compiler's wait counts let the QK^T products wait for K only.)
 // kn >= 0: the score of key kn (the new key) is replaced by snew[lane % 16].
 // page: the page of next_key0 (paged caches), requested a step earlier; on
 // return it holds the page of the step after next_key0.
-template <class Step, class QFrag, class SL>
+enum RefillMode { kNoRefill, kRefill, kRefillIfMore };
+
+template <RefillMode REFILL, class Step, class QFrag, class SL>
 __device__ __forceinline__ void sweep_step(Step& st, const QFrag& qf, const float* snew, int kn, RunState& rs,
                                            float scale_log2, int key0, int kend, int next_key0, const SL& sl,
                                            int n16, int q4, int& page) {
   const bool full = key0 + kStep <= kend;
   float s[8];
   scores(st, qf, scale_log2, s);
-  const bool more = next_key0 < kend;
+  const bool more = REFILL == kRefill || (REFILL == kRefillIfMore && next_key0 < kend);
   if (more) load_k_any(st, sl, next_key0, kend, n16, q4, page);
   if (kn >= key0 && kn < key0 + kStep) {   // wave-uniform: this step holds the new key
     const float sn = snew[n16];
@@ -847,8 +847,17 @@ __global__ __launch_bounds__(PW ? kThreads : kThreads4, BF16 ? 2 : 1) void decod
       // flight during this step's softmax and P V, its V during the next QK^T
       const int s_end = min(nsteps, (j + 1) * spc);
       while (s < s_end) {
-        sweep_step(A, qf, sm.snew, kn, rs, p.scale_log2, c0 + s * kStep, c1, c0 + (s + kStreamWaves) * kStep, sl,
-                   n16, q4, page);
+        const int next = c0 + (s + kStreamWaves) * kStep;
+        if constexpr (BF16) {
+          if (next >= c1) {   // this wave's last step of the range: no refill
+            sweep_step<kNoRefill>(A, qf, sm.snew, kn, rs, p.scale_log2, c0 + s * kStep, c1, next, sl, n16, q4, page);
+            s += kStreamWaves;
+            break;
+          }
+          sweep_step<kRefill>(A, qf, sm.snew, kn, rs, p.scale_log2, c0 + s * kStep, c1, next, sl, n16, q4, page);
+        } else {
+          sweep_step<kRefillIfMore>(A, qf, sm.snew, kn, rs, p.scale_log2, c0 + s * kStep, c1, next, sl, n16, q4, page);
+        }
         s += kStreamWaves;
       }
       // ---- this wave's state of chunk j into LDS buffer j % 2 (the only one
