@@ -185,7 +185,12 @@ struct Slab {
   }
 };
 
-// Loads of one step.  FULL: every row of the step is below kend, no
+// Loads of one step.  Cache policy (bf16): a V load instruction reads 4 whole
+// rows, every cache line it touches in full, so V is read non-temporally (not
+// kept in the caches); a K load instruction reads 16-byte pieces of 16 rows at
+// a 64-byte stride, so each line is touched by all 4 instructions of a row
+// group and K keeps the default policy (the L2 serves the other pieces).
+// FULL: every row of the step is below kend, no
 // predication.  !FULL (the last step of a chunk): rows at or past kend are
 // replaced by row kend-1 (always valid), so rows past the sequence are never
 // read.  Their values stay as loaded: the scores of keys at or past kend are
@@ -217,7 +222,7 @@ __device__ __forceinline__ void load_v(StepBF16& st, const SL& sl, int key0, int
     const bool ok = FULL || key < kend;
     const uint32_t off = FULL ? (uint32_t)(rel + vkey_t(t)) * sl.vss + sl.vlane
                               : (uint32_t)((ok ? key : kend - 1) - key0 + rel) * sl.vss + 16u * n16;
-    st.v[t] = *(const u32x4*)(vb + off);
+    st.v[t] = __builtin_nontemporal_load((const u32x4*)(vb + off));
   }
 }
 
