@@ -487,7 +487,9 @@ def prefill_chunk_case(ctx, past=3072, chunk=1024, bs=0):
 
 def paged_decode_case(ctx, w, bs):
     """A decode workload over a paged cache of bs-row pages (shuffled pool with
-    exactly the pages the lengths need; seeded synthetic rows)."""
+    exactly the pages the lengths need; seeded synthetic rows).  Calls rotate
+    over enough pools (>= LLC_BYTES of K/V) that the Infinity Cache cannot
+    serve one call's rows to the next, as for the contiguous workloads."""
     torch, G, synth, np = ctx["torch"], ctx["G"], ctx["synth"], ctx["np"]
     rng = np.random.Generator(np.random.PCG64(w.seed + 200))
     lens = synth.lengths_of(w)
@@ -495,15 +497,18 @@ def paged_decode_case(ctx, w, bs):
     used = [-(-int(L) // bs) for L in lens]
     npages = sum(used)
     bf = torch.bfloat16
-    kp = torch.randn(npages, w.num_kv_heads, bs, 128, device="cuda", dtype=bf)
-    vp = torch.randn(npages, w.num_kv_heads, bs, 128, device="cuda", dtype=bf)
+    pool_bytes = 2 * npages * w.num_kv_heads * bs * 128 * 2
+    sets = max(1, math.ceil(LLC_BYTES / pool_bytes))
+    kps = [torch.randn(npages, w.num_kv_heads, bs, 128, device="cuda", dtype=bf) for _ in range(sets)]
+    vps = [torch.randn(npages, w.num_kv_heads, bs, 128, device="cuda", dtype=bf) for _ in range(sets)]
+    kp, vp = kps[0], vps[0]
     perm = rng.permutation(npages)
     table = np.full((w.batch, nb), -1, dtype=np.int32)
     k = 0
     for b, u in enumerate(used):
         table[b, :u] = perm[k:k + u]
         k += u
-    t = dict(q=torch.randn(w.batch, w.num_q_heads, 128, device="cuda", dtype=bf), kp=kp, vp=vp,
+    t = dict(q=torch.randn(w.batch, w.num_q_heads, 128, device="cuda", dtype=bf), kp=kps, vp=vps,
              table=torch.from_numpy(table).cuda(), sl=torch.from_numpy(lens).cuda(),
              pos=torch.from_numpy(np.maximum(lens, 1) - 1).cuda(),
              qw=(1 + 0.1 * torch.randn(128, device="cuda")).to(bf) if w.qk_norm else None,
@@ -523,7 +528,8 @@ def paged_decode_case(ctx, w, bs):
     ptr = lambda x: None if x is None else x.data_ptr()
 
     def call(i, stream):
-        st = G.gqa_attn_decode_paged(desc, q.data_ptr(), kp.data_ptr(), vp.data_ptr(), t["table"].data_ptr(),
+        j = i % sets
+        st = G.gqa_attn_decode_paged(desc, q.data_ptr(), kps[j].data_ptr(), vps[j].data_ptr(), t["table"].data_ptr(),
                                      t["sl"].data_ptr(), t["pos"].data_ptr(), ptr(t["qw"]), ptr(t["kw"]),
                                      w.rope_theta, out.data_ptr(), t["ws"].data_ptr(), t["ws"].numel(), stream)
         assert st == G.GQA_OK

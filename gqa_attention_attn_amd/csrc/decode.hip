@@ -127,7 +127,7 @@ __device__ __forceinline__ void prologue_row(float (&x)[8], int c16, bool norm, 
 // ----------------------------------------------------------------- K/V step buffers
 
 struct StepBF16 {
-  u32x4 k[2][4];   // K rows key0 + 16*gi + (lane%16), dims 32*(lane/16) + 8*kb .. +8
+  u32x4 k[2][4];   // K rows key0 + 16*gi + (lane%16), dims 32*kb + 8*(lane/16) .. +8
   u32x4 v[8];      // V rows key0 + vkey(t), dims 8*(lane%16) .. +8
 };
 
@@ -149,6 +149,7 @@ __device__ __forceinline__ constexpr int vkey_t(int t) { return t < 4 ? t : 12 +
 // rows, so the 32 rows of a step always share one page.
 template <bool PAGED>
 struct Slab {
+  static constexpr bool kPaged = PAGED;
   const uint8_t* kb;
   const uint8_t* vb;
   uint32_t kss, vss;     // row strides in bytes
@@ -185,11 +186,14 @@ struct Slab {
   }
 };
 
-// Loads of one step.  Cache policy (bf16): a V load instruction reads 4 whole
-// rows, every cache line it touches in full, so V is read non-temporally (not
-// kept in the caches); a K load instruction reads 16-byte pieces of 16 rows at
-// a 64-byte stride, so each line is touched by all 4 instructions of a row
-// group and K keeps the default policy (the L2 serves the other pieces).
+// Loads of one step (bf16).  V is read non-temporally (streamed once, not
+// kept in the caches): a V load instruction reads 4 whole rows.  K load
+// instruction kb reads bytes 64 kb .. 64 kb + 63 of 16 rows (lane (n16, q4):
+// row n16, dims 32 kb + 8 q4 .. +7; the q fragment holds the same dims), so
+// the two instructions that share a cache line are issued back to back; K is
+// read non-temporally over a contiguous cache and with the default policy over
+// a paged one, where that measured faster.  (The arithmetic is the same on
+// both, so paged and contiguous results are bitwise equal.)
 // FULL: every row of the step is below kend, no
 // predication.  !FULL (the last step of a chunk): rows at or past kend are
 // replaced by row kend-1 (always valid), so rows past the sequence are never
@@ -198,6 +202,7 @@ struct Slab {
 // loads here and both forms leave the same loads in flight.
 template <bool FULL, class SL>
 __device__ __forceinline__ void load_k(StepBF16& st, const SL& sl, int key0, int kend, int n16, int q4, int page) {
+  constexpr bool kNT = !SL::kPaged;
   int rel;
   const uint8_t* kb = sl.kbase(key0, page, rel);
 #pragma unroll
@@ -205,10 +210,10 @@ __device__ __forceinline__ void load_k(StepBF16& st, const SL& sl, int key0, int
     const int key = key0 + 16 * gi + n16;
     const bool ok = FULL || key < kend;
     const uint32_t off = FULL ? (uint32_t)(rel + 16 * gi) * sl.kss + sl.klane
-                              : (uint32_t)((ok ? key : kend - 1) - key0 + rel) * sl.kss + 64u * q4;
+                              : (uint32_t)((ok ? key : kend - 1) - key0 + rel) * sl.kss + 16u * q4;
     const u32x4* src = (const u32x4*)(kb + off);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) st.k[gi][j] = src[j];
+    for (int j = 0; j < 4; ++j) st.k[gi][j] = kNT ? __builtin_nontemporal_load(&src[4 * j]) : src[4 * j];
   }
 }
 
@@ -287,9 +292,9 @@ struct QFragF32 { float q[32]; };
 template <class SM>
 __device__ __forceinline__ void load_qfrag(QFragBF16& qf, const SM& sm, int n16, int q4) {
 #pragma unroll
-  for (int kb = 0; kb < 4; ++kb) {
-    qf.hi[kb] = *(const bf16x8*)&sm.qh[n16][32 * q4 + 8 * kb];
-    qf.lo[kb] = *(const bf16x8*)&sm.ql[n16][32 * q4 + 8 * kb];
+  for (int kb = 0; kb < 4; ++kb) {   // the dims lane (n16, q4) holds of K for product kb
+    qf.hi[kb] = *(const bf16x8*)&sm.qh[n16][32 * kb + 8 * q4];
+    qf.lo[kb] = *(const bf16x8*)&sm.ql[n16][32 * kb + 8 * q4];
   }
 }
 
@@ -799,7 +804,7 @@ __global__ __launch_bounds__(PW ? kThreads : kThreads4, BF16 ? 2 : 1) void decod
   sl.kss = (uint32_t)(p.k_ss * kElem);
   sl.vss = (uint32_t)(p.v_ss * kElem);
   if constexpr (BF16) {
-    sl.klane = (uint32_t)n16 * sl.kss + 64u * q4;          // K row n16, dims 32*q4 ..
+    sl.klane = (uint32_t)n16 * sl.kss + 16u * q4;          // K row n16, dims 32*kb + 8*q4 ..
     sl.vlane = (uint32_t)(4 * q4) * sl.vss + 16u * n16;    // V rows 4*q4 + .., dims 8*n16 ..
   } else {
     sl.klane = (uint32_t)n16 * sl.kss + 128u * q4;
