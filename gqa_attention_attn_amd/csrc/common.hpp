@@ -153,6 +153,15 @@ __device__ __forceinline__ uint32_t pack_f16x2_sat(float lo, float hi) {
   return pack_f16x2(clamp_f16_range(lo), clamp_f16_range(hi));
 }
 
+// The fp16 saturation of pack_f16x2_sat applied after an unsaturated
+// conversion: a half that became +-inf (|x| >= 65520 rounds there) is set to
+// +-65504, which is what converting the clamped value gives; finite halves
+// and NaN are unchanged.
+__device__ __forceinline__ uint32_t saturate_inf_f16x2(uint32_t w) {
+  const uint32_t lo = w & 0xffffu, hi = w >> 16;
+  return (((lo & 0x7fffu) == 0x7c00u) ? lo - 1u : lo) | ((((hi & 0x7fffu) == 0x7c00u) ? hi - 1u : hi) << 16);
+}
+
 // Element e (0..7) of 8 packed bf16 held in 4 dwords, as float.
 __device__ __forceinline__ float bf16_elem(const u32x4& v, int e) {
   uint32_t w = v[e >> 1];
@@ -219,12 +228,10 @@ __device__ __forceinline__ void rope_cos_sin_f64(double pos, double inv, float& 
 }
 
 // cos / sin of the angle pos * inv where inv_rev = inv / (2 pi): the product
-// and its reduction to [0, 1) revolutions are done in double, the final
-// sin / cos by the hardware instructions (which take revolutions).
+// and its reduction to [0, 1) revolutions (v_fract_f64) are done in double,
+// the final sin / cos by the hardware instructions (which take revolutions).
 __device__ __forceinline__ void rope_cos_sin_rev(double pos, double inv_rev, float& c, float& s) {
-  double r = pos * inv_rev;
-  r -= floor(r);
-  const float rf = (float)r;
+  const float rf = (float)__builtin_amdgcn_fract(pos * inv_rev);
   s = __builtin_amdgcn_sinf(rf);
   c = __builtin_amdgcn_cosf(rf);
 }

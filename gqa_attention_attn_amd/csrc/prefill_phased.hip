@@ -529,7 +529,7 @@ __global__ __launch_bounds__(kAttnThreads, kWavesPerSimd) void attention_kernel(
   __shared__ __attribute__((aligned(16))) uint8_t kt0[kTileBytes], kt1[kTileBytes];
   __shared__ __attribute__((aligned(16))) uint8_t vt0[kTileBytes], vt1[kTileBytes];
   __shared__ double inv_rev[kHeadDim / 2];   // query RoPE: theta^(-2i/128) / (2 pi)
-  __shared__ __attribute__((aligned(16))) uint16_t gam[kHeadDim];   // query norm weights (bf16)
+  __shared__ __attribute__((aligned(16))) float gam[kHeadDim];   // query norm weights
   __shared__ int last_span;                   // this workgroup merges its query block's spans
   LDS_AS uint8_t* const K0 = (LDS_AS uint8_t*)kt0;
   LDS_AS uint8_t* const K1 = (LDS_AS uint8_t*)kt1;
@@ -628,7 +628,10 @@ __global__ __launch_bounds__(kAttnThreads, kWavesPerSimd) void attention_kernel(
       }
     }
     __builtin_amdgcn_s_waitcnt(0);   // this thread's q rows and table entries have landed
-    if (tid < 16 && p.q_norm_w) *(u32x4*)&gam[8 * tid] = gv;
+    if (tid < 16 && p.q_norm_w) {
+      *(f32x4*)&gam[8 * tid] = f32x4{bf16lo(gv[0]), bf16hi(gv[0]), bf16lo(gv[1]), bf16hi(gv[1])};
+      *(f32x4*)&gam[8 * tid + 4] = f32x4{bf16lo(gv[2]), bf16hi(gv[2]), bf16lo(gv[3]), bf16hi(gv[3])};
+    }
     dma_tile<kTileBytes / 1024>(k0a, kslab + ta * kTileBytes, lane_off, wave);
     dma_tile<kTileBytes / 1024>(v0a, vslab + ta * kTileBytes, lane_off, wave);
     if (tb - ta > 1) dma_tile<kTileBytes / 1024>(k1a, kslab + (ta + 1) * kTileBytes, lane_off, wave);
@@ -657,6 +660,7 @@ __global__ __launch_bounds__(kAttnThreads, kWavesPerSimd) void attention_kernel(
       }
       r *= p.scale_log2;   // q' carries the softmax scale times log2(e) (RoPE is linear)
       const double qpos = pos0 + (double)(ext.past + wc.qrow[rb]);
+      float amax = 0.f;   // the largest |q'| of the lane (NaN if any is NaN)
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         float xl[8], xh[8];
@@ -666,12 +670,12 @@ __global__ __launch_bounds__(kAttnThreads, kWavesPerSimd) void attention_kernel(
           xh[e] = bf16_elem(qhi[rb][j], e);
         }
         if (g) {
-          const u32x4 glo = *(const u32x4*)&gam[32 * hf + 8 * j];
-          const u32x4 ghi = *(const u32x4*)&gam[64 + 32 * hf + 8 * j];
+          const f32x4 gl0 = *(const f32x4*)&gam[32 * hf + 8 * j], gl1 = *(const f32x4*)&gam[32 * hf + 8 * j + 4];
+          const f32x4 gh0 = *(const f32x4*)&gam[64 + 32 * hf + 8 * j], gh1 = *(const f32x4*)&gam[64 + 32 * hf + 8 * j + 4];
 #pragma unroll
           for (int e = 0; e < 8; ++e) {
-            xl[e] *= r * bf16_elem(glo, e);
-            xh[e] *= r * bf16_elem(ghi, e);
+            xl[e] *= r * (e < 4 ? gl0[e] : gl1[e - 4]);
+            xh[e] *= r * (e < 4 ? gh0[e] : gh1[e - 4]);
           }
         } else {
 #pragma unroll
@@ -690,10 +694,24 @@ __global__ __launch_bounds__(kAttnThreads, kWavesPerSimd) void attention_kernel(
             xh[e] = hi * c + lo * s;
           }
         }
-        qf[rb][j] = as_f16x8(u32x4{pack_f16x2_sat(xl[0], xl[1]), pack_f16x2_sat(xl[2], xl[3]),
-                                   pack_f16x2_sat(xl[4], xl[5]), pack_f16x2_sat(xl[6], xl[7])});
-        qf[rb][4 + j] = as_f16x8(u32x4{pack_f16x2_sat(xh[0], xh[1]), pack_f16x2_sat(xh[2], xh[3]),
-                                       pack_f16x2_sat(xh[4], xh[5]), pack_f16x2_sat(xh[6], xh[7])});
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          amax = __builtin_elementwise_maximum(__builtin_elementwise_maximum(amax, fabsf(xl[e])), fabsf(xh[e]));
+        qf[rb][j] = as_f16x8(u32x4{pack_f16x2(xl[0], xl[1]), pack_f16x2(xl[2], xl[3]), pack_f16x2(xl[4], xl[5]),
+                                   pack_f16x2(xl[6], xl[7])});
+        qf[rb][4 + j] = as_f16x8(u32x4{pack_f16x2(xh[0], xh[1]), pack_f16x2(xh[2], xh[3]), pack_f16x2(xh[4], xh[5]),
+                                       pack_f16x2(xh[6], xh[7])});
+      }
+      // fp16 saturation after the conversion, on the rare waves with an
+      // element beyond 65504 (or a NaN, which the fix leaves as it is)
+      if (__any(!(amax <= kF16Max))) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          u32x4 w = __builtin_bit_cast(u32x4, qf[rb][j]);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) w[i] = saturate_inf_f16x2(w[i]);
+          qf[rb][j] = as_f16x8(w);
+        }
       }
     }
   }
