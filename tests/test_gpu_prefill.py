@@ -4,6 +4,8 @@ bf16 inputs, fp16 MFMA operands (q', k', P rounded to fp16, v converted
 exactly), f32 accumulation, f32 output: max |err| <= 1e-2.
 """
 
+import math
+
 import numpy as np
 import pytest
 
@@ -207,6 +209,29 @@ def test_fp16_range_saturates_k(path):
     assert np.allclose(out[0, 5:8, 9:], np.broadcast_to(inp["v"][0, 1, 9], (3, 151, 128)), rtol=2.0 ** -10,
                        atol=1e-6)
     compare(out, want, ATOL_BF16, f"saturated k {path}")
+
+
+@pytest.mark.parametrize("path", PATHS)
+def test_fp16_range_saturates_q(path):
+    # q' = q * scale * log2(e) (no norm) enters QK^T in fp16: q[11] = +-2^20
+    # gives q'[11] = +-133712, which saturates to +-65504, so the call returns
+    # the oracle's result for q[11] = +-65504 / (scale log2 e).  In KV head 1
+    # only key 9 has a nonzero dim 11 (1.0): it takes all the weight of the
+    # rows with q[11] = +2^20 that see it and none of those with -2^20.  An
+    # unsaturated q' would be +-inf, and inf * 0 makes those rows NaN.
+    inp = small(B=1, Hq=10, Hkv=2, S=160, lens=[160], norm=False, theta=0.0)
+    inp["k"][0, 1, :, 11] = 0.0
+    inp["k"][0, 1, 9, 11] = 1.0
+    inp["q"][0, 5:8, :, 11] = 2.0 ** 20
+    inp["q"][0, 8:10, :, 11] = -(2.0 ** 20)
+    lim = 65504.0 / ((1.0 / math.sqrt(128.0)) * math.log2(math.e))
+    clamped = dict(inp, q=np.clip(inp["q"], -lim, lim))
+    log(f"case fp16 range of q, {path}")
+    out = run(inp, path=path).cpu().numpy()
+    assert np.all(np.isfinite(out))
+    assert np.allclose(out[0, 5:8, 9:], np.broadcast_to(inp["v"][0, 1, 9], (3, 151, 128)), rtol=2.0 ** -10,
+                       atol=1e-6)
+    compare(out, ref(clamped), ATOL_BF16, f"saturated q {path}")
 
 
 # ---- the full Qwen3-14B causal prefill (S = 4096, 40 query heads over 8 KV
