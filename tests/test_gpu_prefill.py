@@ -78,6 +78,18 @@ def test_small_ragged_multi_tile(causal, path):
 
 
 @pytest.mark.parametrize("path", PATHS)
+@pytest.mark.parametrize("theta", [1e6, 5e5])
+def test_large_positions(theta, path):
+    # RoPE angles of queries and keys up to ~130159 rad: the product and its
+    # reduction to revolutions in double on both sides
+    inp = small(B=2, Hq=10, Hkv=2, S=160, lens=[160, 100], theta=theta)
+    inp["positions"] = np.array([130000, 65537], dtype=np.int32)
+    log(f"case prefill large positions theta={theta} {path}")
+    out = run(inp, path=path).cpu().numpy()
+    compare(valid_rows(out, inp), ref(inp), ATOL_BF16, f"large positions theta={theta} {path}")
+
+
+@pytest.mark.parametrize("path", PATHS)
 @pytest.mark.parametrize("Hq,Hkv", [(8, 8), (16, 2), (8, 1), (12, 4), (14, 2)])
 def test_group_sizes(Hq, Hkv, path):
     inp = small(B=1, Hq=Hq, Hkv=Hkv, S=200, lens=[200])
