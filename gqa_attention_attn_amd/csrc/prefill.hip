@@ -322,10 +322,18 @@ __global__ __launch_bounds__(kMaxThreads) void prefill_kernel(const PrefillParam
 #pragma unroll
         for (int i = 0; i < 16; ++i) sacc[i] = (8 * (i >> 2) + (i & 3) < lim) ? sacc[i] : -INFINITY;
       }
-      float mx = fmaxf(sacc[0], sacc[1]);
+      // IEEE maximum trees (no quieting of the MFMA results), then one maximum
+      // across the two lane halves that hold the row's two key halves
+      float mx = sacc[0];
 #pragma unroll
-      for (int i = 2; i < 16; i += 2) mx = fmaxf(mx, fmaxf(sacc[i], sacc[i + 1]));
-      mx = max_xor32(mx) * p.scale_log2;       // row max in log2 units
+      for (int i = 1; i < 15; i += 2)
+        mx = __builtin_elementwise_maximum(__builtin_elementwise_maximum(mx, sacc[i]), sacc[i + 1]);
+      mx = __builtin_elementwise_maximum(mx, sacc[15]);
+      {
+        float a, b;
+        pair_xor32(mx, a, b);
+        mx = __builtin_elementwise_maximum(a, b) * p.scale_log2;   // row max in log2 units
+      }
       // lazy rescale: keep the running max until some row's max grows by more
       // than kLazyRescale; exponents stay <= 2^kLazyRescale meanwhile
       if (__any(mx > m_run + kLazyRescale)) {
@@ -336,20 +344,20 @@ __global__ __launch_bounds__(kMaxThreads) void prefill_kernel(const PrefillParam
         for (int T = 0; T < 4; ++T) o[T] *= corr;
         m_run = m_new;
       }
-      float ps = 0.f;
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const float e = fast_exp2(fmaf(sacc[i], p.scale_log2, -m_run));
-        sacc[i] = e;
-        ps += e;
-      }
-      l_run += ps;
+      for (int i = 0; i < 16; ++i) sacc[i] = fast_exp2(fmaf(sacc[i], p.scale_log2, -m_run));
       // O^T += V^T P^T: MFMA e takes keys ks + 16e + {4hf + t, 8 + 4hf + t}, t < 4,
-      // stored contiguously at V^T positions 16e + 8hf .. 16e + 8hf + 7
+      // stored contiguously at V^T positions 16e + 8hf .. 16e + 8hf + 7.  The
+      // row sum is taken over the fp16 P the products use (v_dot2 of each
+      // pair with (1, 1)), so numerator and denominator see the same weights.
+      const f16x2 one = {(_Float16)1.0f, (_Float16)1.0f};
 #pragma unroll
       for (int e = 0; e < 2; ++e) {
         const u32x4 pf = {pack_f16x2(sacc[8 * e + 0], sacc[8 * e + 1]), pack_f16x2(sacc[8 * e + 2], sacc[8 * e + 3]),
                           pack_f16x2(sacc[8 * e + 4], sacc[8 * e + 5]), pack_f16x2(sacc[8 * e + 6], sacc[8 * e + 7])};
+#pragma unroll
+        for (int w = 0; w < 4; ++w)   // the (uint32_t) copy matters: hipcc bit-casts element 0 of a vector lvalue
+          l_run = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, (uint32_t)pf[w]), one, l_run, false);
 #pragma unroll
         for (int T = 0; T < 4; ++T) {
           const u32x4 a = *(const u32x4*)&sm.vt[buf][32 * T + n32][16 * e + 8 * hf];

@@ -216,8 +216,8 @@ def test_fp16_range_saturates_k(path):
     log(f"case fp16 range of k, {path}")
     out = run(inp, path=path).cpu().numpy()
     want = ref(clamped)
-    # rows that see key 9 with q[11] = +1 are v[9]; the single-kernel path
-    # divides the fp16-rounded P V by the sum of the unrounded P, 2^-11 apart
+    # rows that see key 9 with q[11] = +1 are v[9] (both paths divide the P V
+    # products by the sum of the same fp16 P)
     assert np.allclose(out[0, 5:8, 9:], np.broadcast_to(inp["v"][0, 1, 9], (3, 151, 128)), rtol=2.0 ** -10,
                        atol=1e-6)
     compare(out, want, ATOL_BF16, f"saturated k {path}")
