@@ -142,6 +142,16 @@ def lib() -> ctypes.CDLL:
     return _lib
 
 
+def use_library(path: str) -> None:
+    """Take the entry points from another build of the same sources (the
+    timeline build, libgqa_attn_timeline.so) instead of libgqa_attn.so; call
+    it before the first call into the library."""
+    global LIB_PATH, _lib
+    if _lib is not None and os.path.abspath(path) != os.path.abspath(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is already loaded")
+    LIB_PATH = os.path.abspath(path)
+
+
 # ----------------------------------------------------------------- raw C ABI mirrors
 
 def gqa_attn_status_string(status: int) -> str:

@@ -37,6 +37,9 @@
 //    before the streaming waves start the K/V stream, behind a workgroup
 //    barrier.
 #include "common.hpp"
+#ifdef GQA_TIMELINE
+#include "gqa_timeline.h"
+#endif
 
 namespace gqa {
 namespace {
@@ -54,6 +57,24 @@ constexpr int kMany4 = 1024;   // grids of at least this many single-chunk workg
 constexpr int kStep = 32;        // keys per wave step
 constexpr int kORow = 132;       // padded LDS row (floats) of the in-workgroup merge
 constexpr int kQRow = 136;       // padded bf16 q' row (272 bytes): 16 rows x 16 bytes hit distinct banks
+
+// Per-workgroup timeline of the partition kernel, compiled in only with
+// -DGQA_TIMELINE (a separate measurement build of the library): one lane
+// takes s_memrealtime stamps into LDS at fixed points (include/gqa_timeline.h
+// lists them) and the workgroup writes them out once at its end, so the timed
+// path gets no global memory instruction.  Without the flag the stamps
+// expand to nothing (not even their conditions).
+#ifdef GQA_TIMELINE
+constexpr int kTimelineSlots = GQA_TIMELINE_SLOTS;
+constexpr int kTimelineBlocks = GQA_TIMELINE_BLOCKS;
+__device__ uint64_t g_timeline[kTimelineBlocks * kTimelineSlots];
+#define GQA_STAMP(cond, i) \
+  do {                        \
+    if (cond) tl[(i)] = __builtin_amdgcn_s_memrealtime(); \
+  } while (0)
+#else
+#define GQA_STAMP(cond, i)
+#endif
 
 template <int NB>   // chunk-state buffers: 2 when a workgroup sweeps several chunks
 struct __attribute__((aligned(16))) DecodeSmemT {
@@ -758,11 +779,15 @@ __global__ __launch_bounds__(PW ? kThreads : kThreads4, BF16 ? 2 : 1) void decod
   constexpr int kNT = PW ? kThreads : kThreads4;
 
   __shared__ DecodeSmemT<PW ? 2 : 1> sm;
+#ifdef GQA_TIMELINE
+  __shared__ uint64_t tl[kTimelineSlots];
+#endif
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform branches
   const int n16 = lane & 15, q4 = lane >> 4;
   const bool direct = p.n_split == 1;
+  GQA_STAMP(wave == kPW && lane == 0, 0);   // entry
 
   // ---- workgroup -> (group = (b, h), chunks cf .. cf + cpw - 1)
   int grp, wc, L, posv = 0;
@@ -784,6 +809,7 @@ __global__ __launch_bounds__(PW ? kThreads : kThreads4, BF16 ? 2 : 1) void decod
   } else {
     if (!live_slot(p, lane, grp, wc, L, posv)) return;   // past every live range: nothing to do
   }
+  GQA_STAMP(wave == kPW && lane == 0, 1);   // length known
   const int b = grp / p.num_kv_heads, h = grp % p.num_kv_heads;
   const int cf = wc * p.cpw;
   const int c0 = cf * p.split;
@@ -841,8 +867,11 @@ __global__ __launch_bounds__(PW ? kThreads : kThreads4, BF16 ? 2 : 1) void decod
     load_step(A, sl, c0 + s * kStep, c1, n16, q4, sl.page_of(c0 + s * kStep, c1));
     page = sl.page_of(c0 + (s + kStreamWaves) * kStep, c1);
   }
+  GQA_STAMP(wave == 0 && lane == 0, 2);   // first K/V step requested
   if (wave == kPW) prologue_finish<BF16>(p, sm, pos, lane, rope, has_new, pr);
+  GQA_STAMP(wave == kPW && lane == 0, 3);   // prologue done
   __syncthreads();   // q', the new-key score and the tables are in LDS
+  GQA_STAMP(wave == 0 && lane == 0, 4);   // sweep starts
 
   if (stream) {
     QFrag qf;
@@ -886,6 +915,7 @@ __global__ __launch_bounds__(PW ? kThreads : kThreads4, BF16 ? 2 : 1) void decod
       }
       __syncthreads();
     }
+    GQA_STAMP(wave == 0 && lane == 0, 5);   // sweep done
   } else if constexpr (PW) {
     // the prologue wave folds chunk j while the streaming waves sweep chunk j+1,
     // then the last chunk, and stores the workgroup's partial
@@ -918,6 +948,11 @@ __global__ __launch_bounds__(PW ? kThreads : kThreads4, BF16 ? 2 : 1) void decod
   }
   // ---- a single chunk: every thread of the workgroup merges its wave states
   if (nchunks == 1) merge_chunk(p, sm, 0, b, h, wc, tid, kNT);
+#ifdef GQA_TIMELINE
+  GQA_STAMP(tid == 0, 6);   // partial (or output rows) stored
+  __syncthreads();
+  if (tid < kTimelineSlots && blockIdx.x < kTimelineBlocks) g_timeline[blockIdx.x * kTimelineSlots + tid] = tl[tid];
+#endif
 }
 
 // ----------------------------------------------------------------- merge kernel
@@ -1049,3 +1084,24 @@ hipError_t launch_decode_merge(const DecodeParams& p, hipStream_t stream) {
 }
 
 }  // namespace gqa
+
+#ifdef GQA_TIMELINE
+// include/gqa_timeline.h: exported by the measurement build only.
+extern "C" int32_t gqa_timeline_clear(void) {
+  static uint64_t zeros[gqa::kTimelineBlocks * gqa::kTimelineSlots];   // zero-initialised
+  return (int32_t)hipMemcpyToSymbol(HIP_SYMBOL(gqa::g_timeline), zeros, sizeof(zeros));
+}
+
+extern "C" int32_t gqa_timeline_read(uint64_t* host, size_t words) {
+  if (host == nullptr || words > (size_t)gqa::kTimelineBlocks * gqa::kTimelineSlots) return 1;
+  return (int32_t)hipMemcpyFromSymbol(host, HIP_SYMBOL(gqa::g_timeline), words * sizeof(uint64_t));
+}
+
+extern "C" int32_t gqa_timeline_clock_khz(int32_t* khz) {
+  if (khz == nullptr) return 1;
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e == hipSuccess) e = hipDeviceGetAttribute(khz, hipDeviceAttributeWallClockRate, dev);
+  return (int32_t)e;
+}
+#endif

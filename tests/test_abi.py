@@ -381,3 +381,31 @@ def test_probe_library_exports_and_host_checks():
     assert P.read(4096, 1024, None, None) == 1
     assert P.copy(4096, None, 1024, None) == 1
     assert P.copy(4096, 8192 + 4, 1024, None) == 1
+
+
+# ---- the timeline build (include/gqa_timeline.h, libgqa_attn_timeline.so)
+
+def test_timeline_build_exports_and_constants():
+    from gqa_attention_attn_amd import build as B, timeline as T
+    if not os.path.exists(B.TIMELINE_LIB):
+        pytest.skip("libgqa_attn_timeline.so not built")
+    h = open(os.path.join(ROOT, "include", "gqa_timeline.h")).read()
+    decl = set(re.findall(r"^\s*int32_t\s+(gqa_timeline_\w+)\s*\(", h, re.M))
+    assert decl == {"gqa_timeline_clear", "gqa_timeline_read", "gqa_timeline_clock_khz"}
+    out = subprocess.run(["nm", "-D", "--defined-only", B.TIMELINE_LIB], capture_output=True, text=True).stdout
+    exported = set(re.findall(r"\bT (gqa_\w+)", out))
+    # the same attention entry points as libgqa_attn.so, plus the timeline's
+    assert decl | set(G.EXPORTS) <= exported
+    consts = dict((k, int(v)) for k, v in re.findall(r"#define (GQA_TIMELINE_\w+) (\d+)", h))
+    assert consts == {"GQA_TIMELINE_SLOTS": T.SLOTS, "GQA_TIMELINE_BLOCKS": T.BLOCKS}
+    assert len(T.NAMES) < T.SLOTS
+    # a NULL host buffer or a read beyond the array is rejected before any HIP call
+    L = ctypes.CDLL(B.TIMELINE_LIB)
+    L.gqa_timeline_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t]
+    L.gqa_timeline_read.restype = ctypes.c_int32
+    assert L.gqa_timeline_read(None, 8) == 1
+    buf = (ctypes.c_uint64 * 8)()
+    assert L.gqa_timeline_read(ctypes.addressof(buf), T.SLOTS * T.BLOCKS + 1) == 1
+    L.gqa_timeline_clock_khz.argtypes = [ctypes.c_void_p]
+    L.gqa_timeline_clock_khz.restype = ctypes.c_int32
+    assert L.gqa_timeline_clock_khz(None) == 1
