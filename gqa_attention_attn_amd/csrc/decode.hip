@@ -1087,14 +1087,24 @@ hipError_t launch_decode_merge(const DecodeParams& p, hipStream_t stream) {
 
 #ifdef GQA_TIMELINE
 // include/gqa_timeline.h: exported by the measurement build only.
+namespace gqa {
+hipError_t timeline_attn_clear(const uint64_t* zeros, size_t bytes);   // prefill_phased.hip
+hipError_t timeline_attn_read(uint64_t* host, size_t bytes);
+}  // namespace gqa
+
 extern "C" int32_t gqa_timeline_clear(void) {
-  static uint64_t zeros[gqa::kTimelineBlocks * gqa::kTimelineSlots];   // zero-initialised
-  return (int32_t)hipMemcpyToSymbol(HIP_SYMBOL(gqa::g_timeline), zeros, sizeof(zeros));
+  static uint64_t zeros[GQA_TIMELINE_BLOCKS * GQA_TIMELINE_SLOTS];   // zero-initialised
+  hipError_t e = hipMemcpyToSymbol(HIP_SYMBOL(gqa::g_timeline), zeros, sizeof(zeros));
+  if (e == hipSuccess) e = gqa::timeline_attn_clear(zeros, sizeof(zeros));
+  return (int32_t)e;
 }
 
-extern "C" int32_t gqa_timeline_read(uint64_t* host, size_t words) {
-  if (host == nullptr || words > (size_t)gqa::kTimelineBlocks * gqa::kTimelineSlots) return 1;
-  return (int32_t)hipMemcpyFromSymbol(host, HIP_SYMBOL(gqa::g_timeline), words * sizeof(uint64_t));
+extern "C" int32_t gqa_timeline_read(int32_t kernel, uint64_t* host, size_t words) {
+  if (host == nullptr || words > (size_t)GQA_TIMELINE_BLOCKS * GQA_TIMELINE_SLOTS) return 1;
+  if (kernel == GQA_TIMELINE_DECODE)
+    return (int32_t)hipMemcpyFromSymbol(host, HIP_SYMBOL(gqa::g_timeline), words * sizeof(uint64_t));
+  if (kernel == GQA_TIMELINE_PREFILL) return (int32_t)gqa::timeline_attn_read(host, words * sizeof(uint64_t));
+  return 1;
 }
 
 extern "C" int32_t gqa_timeline_clock_khz(int32_t* khz) {

@@ -35,6 +35,9 @@
 #include <vector>
 
 #include "common.hpp"
+#ifdef GQA_TIMELINE
+#include "gqa_timeline.h"
+#endif
 
 namespace gqa {
 namespace {
@@ -48,6 +51,26 @@ constexpr int kBM = 128;                 // query rows per workgroup
 // faster.
 constexpr int kRB = 1;
 constexpr int kWaves = kBM / (32 * kRB);  // waves per workgroup
+// Per-workgroup timeline of the attention kernel, compiled in only with
+// -DGQA_TIMELINE (the measurement build; include/gqa_timeline.h lists the
+// stamps): thread 0 takes s_memrealtime stamps into LDS, the workgroup writes
+// them out after its tile loop, and thread 0 stores its end stamp at its exit.
+// Without the flag the stamp sites expand to nothing.
+#ifdef GQA_TIMELINE
+__device__ uint64_t g_timeline_attn[GQA_TIMELINE_BLOCKS * GQA_TIMELINE_SLOTS];
+#define GQA_STAMP(i)                                            \
+  do {                                                          \
+    if (tid == 0) tla[(i)] = __builtin_amdgcn_s_memrealtime();  \
+  } while (0)
+#define GQA_STAMP_END()                                                                                   \
+  do {                                                                                                    \
+    if (tid == 0 && blockIdx.x < GQA_TIMELINE_BLOCKS)                                                     \
+      g_timeline_attn[blockIdx.x * GQA_TIMELINE_SLOTS + 5] = __builtin_amdgcn_s_memrealtime();            \
+  } while (0)
+#else
+#define GQA_STAMP(i)
+#define GQA_STAMP_END()
+#endif
 constexpr int kWavesPerSimd = 3;   // 168 VGPRs; the tile loop holds no spill (the span merge does)
 constexpr int kAttnThreads = 64 * kWaves;
 constexpr int kBN = 32;                  // keys per tile
@@ -531,6 +554,9 @@ __global__ __launch_bounds__(kAttnThreads, kWavesPerSimd) void attention_kernel(
   __shared__ double inv_rev[kHeadDim / 2];   // query RoPE: theta^(-2i/128) / (2 pi)
   __shared__ __attribute__((aligned(16))) float gam[kHeadDim];   // query norm weights
   __shared__ int last_span;                   // this workgroup merges its query block's spans
+#ifdef GQA_TIMELINE
+  __shared__ uint64_t tla[GQA_TIMELINE_SLOTS];
+#endif
   LDS_AS uint8_t* const K0 = (LDS_AS uint8_t*)kt0;
   LDS_AS uint8_t* const K1 = (LDS_AS uint8_t*)kt1;
   LDS_AS uint8_t* const V0 = (LDS_AS uint8_t*)vt0;
@@ -542,6 +568,7 @@ __global__ __launch_bounds__(kAttnThreads, kWavesPerSimd) void attention_kernel(
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int n32 = lane & 31, hf = lane >> 5;
   const int G = p.group;
+  GQA_STAMP(0);   // entry
 
   // ---- workgroup -> (sequence, KV head group, query head, 128-query block, key span)
   const int nqb = p.n_qblocks;
@@ -628,6 +655,7 @@ __global__ __launch_bounds__(kAttnThreads, kWavesPerSimd) void attention_kernel(
       }
     }
     __builtin_amdgcn_s_waitcnt(0);   // this thread's q rows and table entries have landed
+    GQA_STAMP(1);                    // q rows landed
     if (tid < 16 && p.q_norm_w) {
       *(f32x4*)&gam[8 * tid] = f32x4{bf16lo(gv[0]), bf16hi(gv[0]), bf16lo(gv[1]), bf16hi(gv[1])};
       *(f32x4*)&gam[8 * tid + 4] = f32x4{bf16lo(gv[2]), bf16hi(gv[2]), bf16lo(gv[3]), bf16hi(gv[3])};
@@ -716,6 +744,7 @@ __global__ __launch_bounds__(kAttnThreads, kWavesPerSimd) void attention_kernel(
     }
   }
 
+  GQA_STAMP(2);   // query prologue done
   WaveState ws;
 #pragma unroll
   for (int rb = 0; rb < kRB; ++rb) {
@@ -729,6 +758,7 @@ __global__ __launch_bounds__(kAttnThreads, kWavesPerSimd) void attention_kernel(
   f32x16 sa[kRB], sb[kRB];
   __builtin_amdgcn_s_waitcnt(0);   // this thread's tile copies have landed
   __syncthreads();                 // K'_0, K'_1, V_0
+  GQA_STAMP(3);                    // first tiles landed
   if (wc.wtiles > ta) {   // scores and row maxima of tile ta (every row sees the span's first key: m is finite)
     const float zero[kRB] = {};
     qk_tile<true>(sa, K0, qf, n32, hf, zero);
@@ -760,6 +790,13 @@ __global__ __launch_bounds__(kAttnThreads, kWavesPerSimd) void attention_kernel(
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
   }
+#ifdef GQA_TIMELINE
+  GQA_STAMP(4);   // tile loop done
+  if (tid == 0) tla[6] = (uint64_t)(tb - ta);   // tiles of this workgroup
+  __syncthreads();
+  if (tid < GQA_TIMELINE_SLOTS && tid != 5 && blockIdx.x < GQA_TIMELINE_BLOCKS)
+    g_timeline_attn[blockIdx.x * GQA_TIMELINE_SLOTS + tid] = tid == 7 ? 0 : tla[tid];
+#endif
   // ---- a split block: store this span's state, arrive; the last span merges
   if (ns > 1) {
     const int64_t blk = ((int64_t)b * p.num_q_heads + hq) * nqb + qb;
@@ -775,18 +812,23 @@ __global__ __launch_bounds__(kAttnThreads, kWavesPerSimd) void attention_kernel(
       if (last_span) __hip_atomic_store(p.counters + blk, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
     __syncthreads();
-    if (!last_span) return;
+    if (!last_span) {
+      GQA_STAMP_END();
+      return;
+    }
     if (!wave_live) return;
     // every span's state (this one's too) from memory: the tile loop's registers are dead here
     WaveState mg;
     load_partial(mg, part, wave, lane);
     for (int k = 1; k < ns; ++k) merge_partial(mg, part + k * kPartFloats, wave, lane);
     write_rows(p, mg, wc, b, hq, T, hf);
+    GQA_STAMP_END();
     return;
   }
   // ---- epilogue: O / l for this lane's query rows
   if (!wave_live) return;
   write_rows(p, ws, wc, b, hq, T, hf);
+  GQA_STAMP_END();   // wave 0 is live in every workgroup that gets here
 }
 
 // Split plan of the attention grid (host).  The work of a query block is
@@ -896,5 +938,14 @@ hipError_t launch_prefill_phased(const PrefillParams& p, void* workspace, hipStr
   return launch_kernel(attention_kernel, dim3(q.n_qblocks * q.n_spans * p.num_q_heads * p.batch), dim3(kAttnThreads),
                        stream, q, (const uint8_t*)kws, (const uint8_t*)vws, ord);
 }
+
+#ifdef GQA_TIMELINE
+hipError_t timeline_attn_clear(const uint64_t* zeros, size_t bytes) {
+  return hipMemcpyToSymbol(HIP_SYMBOL(g_timeline_attn), zeros, bytes);
+}
+hipError_t timeline_attn_read(uint64_t* host, size_t bytes) {
+  return hipMemcpyFromSymbol(host, HIP_SYMBOL(g_timeline_attn), bytes);
+}
+#endif
 
 }  // namespace gqa

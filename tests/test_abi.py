@@ -397,15 +397,18 @@ def test_timeline_build_exports_and_constants():
     # the same attention entry points as libgqa_attn.so, plus the timeline's
     assert decl | set(G.EXPORTS) <= exported
     consts = dict((k, int(v)) for k, v in re.findall(r"#define (GQA_TIMELINE_\w+) (\d+)", h))
-    assert consts == {"GQA_TIMELINE_SLOTS": T.SLOTS, "GQA_TIMELINE_BLOCKS": T.BLOCKS}
-    assert len(T.NAMES) < T.SLOTS
-    # a NULL host buffer or a read beyond the array is rejected before any HIP call
+    assert consts == {"GQA_TIMELINE_SLOTS": T.SLOTS, "GQA_TIMELINE_BLOCKS": T.BLOCKS,
+                      "GQA_TIMELINE_DECODE": T.KERNELS["decode"], "GQA_TIMELINE_PREFILL": T.KERNELS["prefill"]}
+    assert all(len(names) < T.SLOTS for names in T.NAMES.values()) and T.TILES_SLOT >= len(T.NAMES["prefill"])
+    # a NULL host buffer, an unknown kernel or a read beyond the array is
+    # rejected before any HIP call
     L = ctypes.CDLL(B.TIMELINE_LIB)
-    L.gqa_timeline_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t]
+    L.gqa_timeline_read.argtypes = [ctypes.c_int32, ctypes.c_void_p, ctypes.c_size_t]
     L.gqa_timeline_read.restype = ctypes.c_int32
-    assert L.gqa_timeline_read(None, 8) == 1
     buf = (ctypes.c_uint64 * 8)()
-    assert L.gqa_timeline_read(ctypes.addressof(buf), T.SLOTS * T.BLOCKS + 1) == 1
+    assert L.gqa_timeline_read(0, None, 8) == 1
+    assert L.gqa_timeline_read(2, ctypes.addressof(buf), 8) == 1
+    assert L.gqa_timeline_read(1, ctypes.addressof(buf), T.SLOTS * T.BLOCKS + 1) == 1
     L.gqa_timeline_clock_khz.argtypes = [ctypes.c_void_p]
     L.gqa_timeline_clock_khz.restype = ctypes.c_int32
     assert L.gqa_timeline_clock_khz(None) == 1
