@@ -193,7 +193,7 @@ def report(kernel, us, tiles, khz, call_us, n, command) -> str:
             "(partition + merge) of B = 1, 40 query heads over 8 KV heads, 4096 cached keys, bf16,",
             "QK-norm and RoPE; K/V rotated over 64 sets (1 GiB), clock settled by graph replays.",
             "",
-            "Command (repository root on the GPU box): `" + command + "`",
+            "Command (from the repository root): `" + command + "`",
             "",
             f"Counter clock {khz} kHz; {len(us)} partition workgroups stamped; step (partition + merge,",
             f"graph of {n} calls) {call_us:.2f} µs per call.  Times in µs after the first workgroup's entry:",
@@ -212,7 +212,7 @@ def report(kernel, us, tiles, khz, call_us, n, command) -> str:
         "B = 1, 4096 tokens, 40 query heads over 8 KV heads, bf16, QK-norm and RoPE, with a workspace",
         "(key phase, then attention); clock settled by graph replays.",
         "",
-        "Command (repository root on the GPU box): `" + command + "`",
+        "Command (from the repository root): `" + command + "`",
         "",
         f"Counter clock {khz} kHz; {len(us)} attention workgroups stamped; call (key phase + attention,",
         f"graph of {n} calls) {call_us:.2f} µs.  First entry to last exit {span:.1f} µs.  Times in µs",
